@@ -1,0 +1,299 @@
+"""Pins for the CPU oracle: the pages' worked examples, closed forms, an
+independent decoder, brute-force set semantics and hand-derived payloads.
+
+Each check is chosen so that a plausible slip in the oracle (ties to the wrong
+side, a dropped field, an off-by-one in the W15 rule, a wrong bit order, a
+wrong ordinal formula term) fails at least one of them.
+"""
+import itertools
+import json
+import os
+import random
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from fcdecode import decode, eg0_length, replace_merge, trailing_zero
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _int_side(vals):
+    """Integers as 4-byte big-endian keys: bytewise order is numeric order."""
+    return gen.side_from_records([(int(v).to_bytes(4, "big"), b"") for v in vals])
+
+
+def _merged_values(A, B, refs):
+    nA = A.n
+    return [int.from_bytes(A.key(r) if r < nA else B.key(r - nA), "big") for r in refs]
+
+
+# ---- merge and co-rank: the pages' worked examples ----
+
+def test_merge_path_worked_example():
+    g = _load("merge_path_worked_example.json")
+    A, B = _int_side(g["a"]), _int_side(g["b"])
+    refs = oracle.merge(A, B)
+    assert _merged_values(A, B, refs) == g["merged"]
+    path = " ".join("down" if r < A.n else "right" for r in refs)
+    assert path == g["path"]
+    assert oracle.corank(refs, A.n, 3) == g["diagonal_3_crosses_at_i"]
+    sp = oracle.splits(refs, A.n, 2)
+    assert oracle.diagonals(len(refs), 2) == g["slice_boundaries_k"]
+    # each slice between consecutive crossings holds exactly its A and B spans
+    for p in range(len(sp) - 1):
+        d0, d1 = g["slice_boundaries_k"][p], g["slice_boundaries_k"][p + 1]
+        got = sorted(_merged_values(A, B, refs[d0:d1]))
+        want = sorted(g["a"][sp[p]:sp[p + 1]] + g["b"][d0 - sp[p]:d1 - sp[p + 1]])
+        assert got == want
+
+
+def test_dsa_corank_table():
+    g = _load("dsa_corank_table.json")
+    A, B = _int_side(g["A"]), _int_side(g["B"])
+    refs = oracle.merge(A, B)
+    assert _merged_values(A, B, refs) == g["merged"]
+    for k, (i, j) in enumerate(g["corank_ij"]):
+        assert oracle.corank(refs, A.n, k) == i and k - i == j
+
+
+def test_corank_ties_go_to_older_side():
+    g = _load("merge_path_ties_and_termination.json")["tie_case"]
+    A, B = _int_side(g["a"]), _int_side(g["b"])
+    refs = oracle.merge(A, B)
+    assert _merged_values(A, B, refs) == g["values"]
+    i = oracle.corank(refs, A.n, g["k"])
+    assert i == g["corank"]
+    assert (i, g["k"] - i) == (g["second_slice_starts_at"]["a"], g["second_slice_starts_at"]["b"])
+    # provenance, not values: the first equal pair takes a before b
+    assert [r < A.n for r in refs] == [True, True, False, False, False, True]
+
+
+def test_corank_termination_case():
+    g = _load("merge_path_ties_and_termination.json")["termination_case"]
+    A, B = _int_side(g["a"]), _int_side(g["b"])
+    refs = oracle.merge(A, B)
+    assert oracle.corank(refs, A.n, g["k"]) == g["corank"]
+
+
+# ---- closed forms ----
+
+def test_eg0_closed_form_matches_textbook_code():
+    # E(x) from the record grammar equals the length of the textbook order-0
+    # Exp-Golomb code written out independently here.
+    for x in list(range(0, 1 << 16)) + [2**20 - 1, 2**20, 2**30, 2**31 - 1]:
+        y = bin(x + 1)[2:]
+        code = "0" * (len(y) - 1) + y
+        assert len(code) == eg0_length(x)
+
+
+def _closed_form_lengths(records, W=15):
+    """E(c)+E(k-l)+(k-l)+v per survivor, from the record grammar paragraph."""
+    out = []
+    prev = None
+    for i, (k, _, v) in enumerate(records):
+        kb = 8 * len(k)
+        if i == 0:
+            l = 0
+        else:
+            pb = "".join(f"{b:08b}" for b in prev)
+            xb = "".join(f"{b:08b}" for b in k)
+            l = 0
+            while l < min(len(pb), len(xb)) and pb[l] == xb[l]:
+                l += 1
+        c = 1 + l if i % W == 0 else 8 * len(prev) - l
+        vbits = 1 if v is None else 1 + eg0_length(len(v)) + 8 * len(v)
+        out.append(eg0_length(c) + eg0_length(kb - l) + (kb - l) + vbits)
+        prev = k
+    return out
+
+
+# ---- hand-derived payloads (readings of the record grammar, field by field) ----
+
+def test_one_record_payload_bits():
+    # key "a" (0x61), present empty value, first record:
+    #   c0 = 1 + 0 = 1      EG0(1)  = 010
+    #   k - l = 8           EG0(8)  = 0001001
+    #   key bits 0..7       0x61    = 01100001
+    #   present value       1, EG0(0) = 1
+    bits = "010" + "0001001" + "01100001" + "1" + "1"
+    A = gen.side_from_records([(b"a", b"")])
+    B = gen.side_from_records([])
+    r = oracle.run(A, B)
+    assert r["T"] == len(bits) == 20
+    padded = bits + "0" * (32 - len(bits))
+    want = bytes(int(padded[i:i + 8], 2) for i in range(0, 32, 8))
+    assert r["payload"].tobytes() == want == bytes.fromhex("42587000")
+
+
+def test_merge_example_payload_bits():
+    # A = {ab: "1", b: ""}, B = {ab: tombstone, abc: "Z"}; B's ab replaces A's.
+    A = gen.side_from_records([(b"ab", b"1"), (b"b", b"")])
+    B = gen.side_from_records([(b"ab", None), (b"abc", b"Z")])
+    r = oracle.run(A, B)
+    assert list(r["final"]) == [2, 3, 1]              # B0, B1, A1
+    assert list(r["ord_A"]) == [oracle.NONE, 2] and list(r["ord_B"]) == [0, 1]
+    rec0 = "010" + "000010001" + "0110000101100010" + "0"          # ab, l=0, c=1, tombstone
+    rec1 = "1" + "0001001" + "01100011" + "1" + "010" + "01011010"  # abc, l=16, c=16-16=0, "Z"
+    rec2 = "000010011" + "011" + "10" + "1" + "1"                  # b, l=6, c=24-6=18, ""
+    assert [len(rec0), len(rec1), len(rec2)] == list(r["len_bits"]) == [29, 28, 16]
+    assert list(r["lcp_bits"]) == [0, 16, 6]
+    assert list(r["off"]) == [0, 29, 57, 73] and r["T"] == 73
+    bits = rec0 + rec1 + rec2
+    bits += "0" * (-len(bits) % 32)
+    want = bytes(int(bits[i:i + 8], 2) for i in range(0, len(bits), 8))
+    assert r["payload"].tobytes() == want
+    assert want.hex() == "411616244b1d2d04dd800000"
+
+
+def test_w15_phase_resets_control_to_absolute_length():
+    # 17 records sharing long prefixes: records 0 and 15 carry c = 1 + l.
+    keys = [b"prefix/" + bytes([0x41 + i]) + b"tail" for i in range(17)]
+    A = gen.side_from_records([(k, b"v") for k in keys[::2]])
+    B = gen.side_from_records([(k, None) for k in keys[1::2]])
+    r = oracle.run(A, B)
+    recs, info = decode(r["payload"].tobytes(), r["T"], r["S"])
+    assert [k for k, _ in recs] == keys
+    for i, d in enumerate(info):
+        if i % 15 == 0:
+            assert d["c"] == 1 + d["l"]
+        else:
+            assert d["c"] == info[i - 1]["k"] - d["l"]
+    assert info[15]["l"] == 8 * len(b"prefix/") + 3  # 'O' 01001111 vs 'P' 01010000: bit 3
+    assert info[15]["c"] == 1 + info[15]["l"]
+
+
+# ---- brute force over tiny key universes ----
+
+def _universe(alphabet, maxlen):
+    keys = [b""]
+    for L in range(1, maxlen + 1):
+        keys += [bytes(t) for t in itertools.product(alphabet, repeat=L)]
+    return sorted(keys)
+
+
+def _check_case(a_recs, b_recs, items=3):
+    A = gen.side_from_records(a_recs)
+    B = gen.side_from_records(b_recs)
+    r = oracle.run(A, B, items_per_part=items)
+    # merge: stable, ties to A  (sort (key, side) pairs: A=0 before B=1)
+    tagged = sorted([(k, 0, i) for i, (k, _) in enumerate(a_recs)]
+                    + [(k, 1, j) for j, (k, _) in enumerate(b_recs)])
+    want_refs = [i if s == 0 else A.n + i for _, s, i in tagged]
+    assert list(r["refs"]) == want_refs
+    for d, i in zip(oracle.diagonals(len(want_refs), items), r["splits"]):
+        assert i == sum(1 for x in want_refs[:d] if x < A.n)
+    # keep-newer: set semantics
+    want = replace_merge(a_recs, b_recs)
+    got = []
+    for ref in r["final"]:
+        if ref < A.n:
+            got.append((A.key(ref), "A", A.value(ref)))
+        else:
+            got.append((B.key(ref - A.n), "B", B.value(ref - A.n)))
+    assert got == want
+    both = len({k for k, _ in a_recs} & {k for k, _ in b_recs})
+    assert r["S"] == A.n + B.n - both
+    # every B record survives; ordinals are positions in the final order
+    assert all(o != oracle.NONE for o in r["ord_B"])
+    for s, ref in enumerate(r["final"]):
+        o = r["ord_A"][ref] if ref < A.n else r["ord_B"][ref - A.n]
+        assert o == s
+    assert sum(o == oracle.NONE for o in r["ord_A"]) == both
+    # collision-bit formulas give the same ordinals and final order
+    c = oracle.collision(A, B)
+    assert np.array_equal(c["ord_A"], r["ord_A"]) and np.array_equal(c["ord_B"], r["ord_B"])
+    assert np.array_equal(c["final"], r["final"]) and c["S"] == r["S"]
+    assert int(c["R"][-1]) == both
+    # decode the payload independently; lengths match the closed form
+    recs, info = decode(r["payload"].tobytes(), r["T"], r["S"])
+    assert recs == [(k, v) for k, _, v in want]
+    assert list(r["len_bits"]) == _closed_form_lengths(want) == [d["length"] for d in info]
+    assert list(r["off"][:-1]) == [d["start"] for d in info]
+    assert r["T"] == sum(int(x) for x in r["len_bits"]) == int(r["off"][-1])
+    assert len(r["payload"]) == 4 * ((r["T"] + 31) // 32)
+    assert trailing_zero(r["payload"].tobytes(), r["T"])
+    return r
+
+
+def _rand_value(rng):
+    if rng.random() < 0.2:
+        return None
+    return bytes(rng.randrange(256) for _ in range(rng.randrange(4)))
+
+
+def test_brute_force_all_pairs_small_universe():
+    # keys: "", 00, 61, FF: all 16 x 16 pairs of subsets
+    U = _universe([0x00, 0x61, 0xFF], 1)
+    rng = random.Random(7)
+    for ma in range(1 << len(U)):
+        for mb in range(1 << len(U)):
+            a = [(k, _rand_value(rng)) for t, k in enumerate(U) if ma >> t & 1]
+            b = [(k, _rand_value(rng)) for t, k in enumerate(U) if mb >> t & 1]
+            _check_case(a, b)
+
+
+def test_brute_force_random_subsets_larger_universe():
+    # all strings of length <= 2 over {00, 61, FF}: 13 keys, proper prefixes, NUL bytes
+    U = _universe([0x00, 0x61, 0xFF], 2)
+    assert len(U) == 13
+    rng = random.Random(11)
+    for _ in range(600):
+        a = [(k, _rand_value(rng)) for k in U if rng.random() < 0.5]
+        b = [(k, _rand_value(rng)) for k in U if rng.random() < 0.5]
+        _check_case(a, b, items=rng.choice([1, 2, 3, 5, 64]))
+
+
+def test_edge_cases_empty_inputs():
+    r = _check_case([], [])
+    assert r["S"] == 0 and r["T"] == 0 and len(r["payload"]) == 0
+    _check_case([(b"k", b"v")], [])
+    _check_case([], [(b"k", None)])
+    _check_case([(b"", b"")], [(b"", None)])   # the empty key, replaced by a tombstone
+
+
+def test_random_workload_roundtrip():
+    A, B = gen.make(gen.WORKLOADS[1].scaled(0.15))
+    r = _check_case(A.records(), B.records(), items=37)
+    assert r["S"] > 2000
+
+
+def test_long_records_span_many_words():
+    rng = random.Random(3)
+    a = sorted({bytes(rng.randrange(256) for _ in range(rng.randrange(40, 300))) for _ in range(40)})
+    recs = [(k, bytes(rng.randrange(256) for _ in range(rng.randrange(0, 600)))) for k in a]
+    _check_case(recs[::2], [(k, None if i % 3 == 0 else v) for i, (k, v) in enumerate(recs[1::2])])
+
+
+# ---- rank ----
+
+def test_rank_scalar_prefix_counts():
+    rng = np.random.default_rng(5)
+    for nbits in (0, 1, 31, 32, 33, 63, 64, 65, 511, 512, 513, 2047, 2048, 2049):
+        for fill in ("zero", "one", "sparse", "random"):
+            bits = {"zero": np.zeros(nbits, np.uint8), "one": np.ones(nbits, np.uint8),
+                    "sparse": (rng.random(nbits) < 0.01).astype(np.uint8),
+                    "random": (rng.random(nbits) < 0.5).astype(np.uint8)}[fill]
+            words = np.zeros((nbits + 31) // 32 + 1, np.uint32)
+            for q in np.nonzero(bits)[0]:
+                words[q >> 5] |= np.uint32(1 << (int(q) & 31))
+            pos = list(range(nbits + 1))
+            want = np.concatenate([[0], np.cumsum(bits)]).astype(np.uint32)
+            assert np.array_equal(oracle.rank(words, pos), want)
+
+
+def test_key_order_proper_prefix_and_unsigned_bytes():
+    A = gen.side_from_records([(b"ab", b""), (b"a\x80", b""), (b"\xff", b"")])
+    B = gen.side_from_records([(b"a", b""), (b"ab\x00", b""), (b"b", b"")])
+    assert oracle.key_cmp(A, 0, B, 0) > 0      # "ab" > "a": proper prefix first
+    assert oracle.key_cmp(A, 0, B, 1) < 0      # "ab" < "ab\0"
+    assert oracle.key_cmp(A, 1, B, 2) < 0      # 0x61 < 0x62 regardless of later bytes
+    assert oracle.key_cmp(A, 2, B, 2) > 0      # 0xff is large: unsigned bytes
+    assert oracle.key_cmp(A, 0, A, 0) == 0
