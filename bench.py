@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the whole merge -> keep -> lengths -> scan -> emit path on one
+MI355X, on the 8M+8M base64-key workload (or another named workload).
+
+One step is one pass of the hot path over inputs already resident in HBM:
+em_partition, em_merge_keep (or em_collision_rank), the host read of S,
+em_fc_lengths, em_scan, the host read of T, em_emit.  W untimed warm-up steps,
+then exactly K timed steps between two device synchronisations.  Prints one
+JSON line.
+
+  value      merged records/s = (|A| + |B|) * K / elapsed
+  GB/s       B_io / step time, B_io = both sides' key and value arenas, u32
+             offsets and tombstone bytes, plus the payload bytes
+  roofline   the dominant kernel's algorithmic bytes per launch over its
+             average launch time (HIP events on the launch stream)
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "merged records/s and pipeline GB/s (% of HBM peak) at 8M+8M string keys, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
+    ap.add_argument("--path", choices=("merge", "collision"), default="merge")
+    ap.add_argument("--items", type=int, default=2048, help="outputs per merge partition")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-scale", type=float, default=0.125,
+                    help="fraction of the workload the CPU oracle is timed on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def side_bytes(h) -> int:
+    return int(h.keys.size + h.vals.size + h.key_off.nbytes + h.val_off.nbytes + h.tomb.size)
+
+
+def algorithmic_bytes(Ah, Bh, pl, path):
+    """Per-launch algorithmic bytes of each call (what it must read and write once)."""
+    import numpy as np
+    S, T, N = pl.S, pl.T, Ah.n + Bh.n
+    keys = int(Ah.keys.size + Bh.keys.size)
+    offs = 4 * (Ah.n + 1 + Bh.n + 1)
+    final = pl.host("final", S)
+    lcp = pl.host("lcp", S)
+    nA = Ah.n
+    isA = final < nA
+    ia = final[isA].astype(np.int64)
+    ib = final[~isA].astype(np.int64) - nA
+    klen = np.empty(S, np.int64)
+    klen[isA] = (Ah.key_off[ia + 1].astype(np.int64) - Ah.key_off[ia])
+    klen[~isA] = (Bh.key_off[ib + 1].astype(np.int64) - Bh.key_off[ib])
+    vlen = np.empty(S, np.int64)
+    vlen[isA] = (Ah.val_off[ia + 1].astype(np.int64) - Ah.val_off[ia])
+    vlen[~isA] = (Bh.val_off[ib + 1].astype(np.int64) - Bh.val_off[ib])
+    suffix_bytes = int(np.sum(klen - (lcp.astype(np.int64) >> 3)))
+    survivor_key_bytes = int(np.sum(klen))
+    value_bytes = int(np.sum(vlen))
+    payload = 4 * ((T + 31) // 32)
+    per_rec_meta = 4 + 8 + 4 + 8 + 8 + 1  # final, off, lcp, key_off pair, val_off pair, tomb
+    out = {
+        # merge: every key byte, both offset arrays; writes refs and both ordinal arrays
+        "em_merge_keep": keys + offs + 4 * S + 4 * N,
+        # lengths: survivor refs, their keys (own + predecessor's), offsets, tombs; writes len + lcp
+        "em_fc_lengths": 4 * S + survivor_key_bytes + S * (8 + 8 + 1) + 8 * S,
+        "em_scan": 4 * S + 8 * (S + 1),
+        "em_emit": S * per_rec_meta + suffix_bytes + value_bytes + payload,
+        "em_partition": 0,
+        "em_collision_rank": keys + offs + 4 * S + 4 * N,
+    }
+    return out
+
+
+def cpu_baseline(w, scale):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import gen
+    import oracle
+    ws = w.scaled(scale)
+    A, B = gen.make(ws)
+    t0 = time.perf_counter()
+    refs = oracle.merge(A, B)
+    final, _, _, S = oracle.keep(A, B, refs)
+    _, _, _, T, payload = oracle.encode(A, B, final)
+    dt = time.perf_counter() - t0
+    n = A.n + B.n
+    return {"value": n / dt, "unit": "records/s", "cores": 1, "kind": "oracle",
+            "sample": f"{ws.name}: {A.n}+{B.n} records drawn by the same recipe "
+                      f"(scale {scale:g}), merge + keep + bitwise encode, {dt:.2f} s single-threaded",
+            "seconds": dt, "GBps": (side_bytes(A) + side_bytes(B) + len(payload)) / dt / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the path is single-device "
+                                   "(see the sharding note in the design document)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import gen
+    import merge_front_coded_amd as em
+
+    w = gen.WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    Ah, Bh = gen.make(w)
+    t_gen = time.perf_counter() - t_gen
+    print(f"# generated {w.name}: {Ah.n}+{Bh.n} records in {t_gen:.1f}s", file=sys.stderr, flush=True)
+    A = em.DeviceSide.from_host(Ah)
+    B = em.DeviceSide.from_host(Bh)
+    pl = em.Pipeline(A, B, items_per_part=args.items, path=args.path)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        pl.run()
+    torch.cuda.synchronize()
+    print(f"# warm-up done: S={pl.S} T={pl.T}", file=sys.stderr, flush=True)
+
+    # per-call HIP events on the launch stream (torch's current stream, which
+    # the binding passes to the library)
+    stream = torch.cuda.current_stream()
+    calls = ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"] \
+        if args.path == "merge" else ["em_collision_rank", "em_fc_lengths", "em_scan", "em_emit"]
+    ev = {c: [] for c in calls}
+    orig = {c: getattr(em.pipeline.em, c) for c in calls}
+
+    def timed(name):
+        f = orig[name]
+
+        def g(*a, **k):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            f(*a, **k)
+            e.record(stream)
+            ev[name].append((s, e))
+        return g
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    for c in calls:
+        setattr(em.pipeline.em, c, timed(c))
+    try:
+        start.record(stream)
+        for _ in range(args.steps):
+            pl.run()
+        end.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        for c in calls:
+            setattr(em.pipeline.em, c, orig[c])
+    wall = time.perf_counter() - t0
+    dev_ms = start.elapsed_time(end)
+    ms_per_step = dev_ms / args.steps
+    per_call_ms = {c: sum(s.elapsed_time(e) for s, e in ev[c]) / len(ev[c]) for c in calls}
+
+    N = Ah.n + Bh.n
+    payload_bytes = 4 * ((pl.T + 31) // 32)
+    b_io = side_bytes(Ah) + side_bytes(Bh) + payload_bytes
+    gbps = b_io / (ms_per_step * 1e-3) / 1e9
+    alg = algorithmic_bytes(Ah, Bh, pl, args.path)
+    dominant = max((c for c in calls if c != "em_partition"), key=lambda c: per_call_ms[c])
+    ach = alg[dominant] / (per_call_ms[dominant] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "records/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "nA": Ah.n, "nB": Bh.n, "items_per_part": args.items,
+                   "path": args.path, "parallelism": "single-gpu"},
+        "survivors": pl.S,
+        "payload_bits": pl.T,
+        "B_io_bytes": b_io,
+        "pipeline_GBps": gbps,
+        "pipeline_hbm_frac": gbps / HBM_PEAK_GBPS,
+        "survivors_per_s": pl.S / (ms_per_step * 1e-3),
+        "wall_s_timed": wall,
+        "per_call_ms": per_call_ms,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg[dominant],
+                     "avg_launch_ms": per_call_ms[dominant]},
+    }
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e.record()
+        torch.cuda.synchronize()
+        result["copy_GBps"] = 2 * n * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
+    if not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_scale)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -251,11 +251,6 @@ void shuffle(Rng& g, std::vector<T>& v) {
   for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[g.below64(i)]);
 }
 
-struct Side {
-  std::vector<uint8_t> keys, vals, tomb;
-  std::vector<uint32_t> key_off, val_off;
-};
-
 uint32_t draw_vlen(const gen_params& p, Rng& g) {
   switch (p.val_kind) {
     case VAL_FIXED: return p.vmin;
@@ -268,29 +263,18 @@ uint32_t draw_vlen(const gen_params& p, Rng& g) {
   }
 }
 
-void push_record(Side& s, const Pool& pool, uint32_t idx, bool tomb, uint32_t vlen, Rng& g) {
-  s.keys.insert(s.keys.end(), pool.key(idx), pool.key(idx) + pool.len(idx));
-  s.key_off.push_back((uint32_t)s.keys.size());
-  s.tomb.push_back(tomb ? 1 : 0);
-  if (!tomb) {
-    size_t at = s.vals.size();
-    s.vals.resize(at + vlen);
-    uint8_t* d = s.vals.data() + at;
-    uint32_t t = 0;
-    for (; t + 8 <= vlen; t += 8) {
-      uint64_t r = g.next();
-      std::memcpy(d + t, &r, 8);
-    }
-    if (t < vlen) {
-      uint64_t r = g.next();
-      std::memcpy(d + t, &r, vlen - t);
-    }
-  }
-  s.val_off.push_back((uint32_t)s.vals.size());
-}
+// One output record: which pool key, tombstone flag and value length.
+struct Rec {
+  uint32_t key;
+  uint32_t vlen;  // 0 for a tombstone
+  uint8_t tomb;
+};
 
 struct Result {
-  Side side[2];
+  Pool pool;
+  std::vector<Rec> side[2];
+  uint64_t key_bytes[2] = {0, 0}, val_bytes[2] = {0, 0};
+  uint64_t val_seed[2] = {0, 0};
   int err = 0;
 };
 
@@ -298,8 +282,10 @@ struct Result {
 
 extern "C" {
 
-// Returns a handle (never NULL); gen_error() reports a non-zero code when the
-// parameters are inconsistent or the key space cannot supply enough keys.
+// Plans both sides: draws and sorts the key pool, picks the keys of each side
+// and every record's tombstone flag and value length.  Returns a handle
+// (never NULL); gen_error() reports a non-zero code when the parameters are
+// inconsistent or the key space cannot supply enough distinct keys.
 void* gen_run(const gen_params* pp) {
   const gen_params& p = *pp;
   Result* res = new Result();
@@ -309,13 +295,12 @@ void* gen_run(const gen_params* pp) {
   }
   Rng g(p.seed);
   const uint64_t U = p.nA + p.nB - p.nX;  // distinct keys needed
-  Pool pool;
   std::vector<uint32_t> uniq;
   double factor = 1.02;
   for (int attempt = 0;; ++attempt) {
     uint64_t want = (uint64_t)std::ceil((double)U * factor) + 64;
-    draw_keys(p, g, want, pool);
-    uniq = sorted_unique(pool);
+    draw_keys(p, g, want, res->pool);
+    uniq = sorted_unique(res->pool);
     if (uniq.size() >= U) break;
     if (attempt == 12) {
       res->err = 2;
@@ -323,8 +308,8 @@ void* gen_run(const gen_params* pp) {
     }
     factor *= 1.3;
   }
-  // Choose U of the distinct keys uniformly (order kept) by dropping the surplus
-  // at random, then assign roles.
+  // Keep U of the distinct keys, chosen uniformly (order kept), by dropping
+  // the surplus at random; then assign roles A only / B only / both.
   std::vector<uint8_t> keep(uniq.size(), 1);
   for (uint64_t dropped = 0, surplus = uniq.size() - U; dropped < surplus;) {
     uint64_t i = g.below64(uniq.size());
@@ -339,52 +324,68 @@ void* gen_run(const gen_params* pp) {
   role.insert(role.end(), p.nB - p.nX, 1);
   role.insert(role.end(), p.nX, 2);
   shuffle(g, role);
-  Side& A = res->side[0];
-  Side& B = res->side[1];
-  for (Side* s : {&A, &B}) {
-    uint64_t n = s == &A ? p.nA : p.nB;
-    s->key_off.reserve(n + 1);
-    s->val_off.reserve(n + 1);
-    s->tomb.reserve(n);
-    s->keys.reserve((size_t)((double)pool.bytes.size() / (double)pool.n() * (double)n) + 64);
-    s->key_off.assign(1, 0);
-    s->val_off.assign(1, 0);
-  }
+  res->side[0].reserve(p.nA);
+  res->side[1].reserve(p.nB);
   size_t r = 0;
   for (size_t i = 0; i < uniq.size(); ++i) {
-    if (i + 16 < uniq.size()) __builtin_prefetch(&pool.off[uniq[i + 16]]);
-    if (i + 8 < uniq.size()) __builtin_prefetch(pool.bytes.data() + pool.off[uniq[i + 8]]);
     if (!keep[i]) continue;
-    uint8_t ro = role[r++];
-    if (ro != 1) {
-      bool t = g.uniform() < p.tombA;
-      push_record(A, pool, uniq[i], t, draw_vlen(p, g), g);
-    }
-    if (ro != 0) {
-      bool t = g.uniform() < p.tombB;
-      push_record(B, pool, uniq[i], t, draw_vlen(p, g), g);
+    const uint8_t ro = role[r++];
+    const uint32_t k = uniq[i];
+    for (int sd = 0; sd < 2; ++sd) {
+      if (ro == (sd == 0 ? 1 : 0)) continue;  // this key is not on side sd
+      const bool t = g.uniform() < (sd == 0 ? p.tombA : p.tombB);
+      const uint32_t vl = draw_vlen(p, g);
+      res->side[sd].push_back(Rec{k, t ? 0u : vl, (uint8_t)(t ? 1 : 0)});
+      res->key_bytes[sd] += res->pool.len(k);
+      res->val_bytes[sd] += t ? 0u : vl;
     }
   }
+  res->val_seed[0] = g.next();
+  res->val_seed[1] = g.next();
   return res;
 }
 
 int gen_error(void* h) { return ((Result*)h)->err; }
 
 void gen_sizes(void* h, int side, uint64_t* n, uint64_t* key_bytes, uint64_t* val_bytes) {
-  const Side& s = ((Result*)h)->side[side];
-  *n = s.tomb.size();
-  *key_bytes = s.keys.size();
-  *val_bytes = s.vals.size();
+  const Result* res = (const Result*)h;
+  *n = res->side[side].size();
+  *key_bytes = res->key_bytes[side];
+  *val_bytes = res->val_bytes[side];
 }
 
+// Writes one side straight into the caller's buffers (sizes from gen_sizes):
+// keys gathered from the sorted pool, value bytes drawn from the side's own
+// stream, n+1 offsets each, one tombstone byte per record.
 void gen_copy(void* h, int side, uint8_t* keys, uint32_t* key_off, uint8_t* vals, uint32_t* val_off,
               uint8_t* tomb) {
-  const Side& s = ((Result*)h)->side[side];
-  if (!s.keys.empty()) std::memcpy(keys, s.keys.data(), s.keys.size());
-  std::memcpy(key_off, s.key_off.data(), s.key_off.size() * 4);
-  if (!s.vals.empty()) std::memcpy(vals, s.vals.data(), s.vals.size());
-  std::memcpy(val_off, s.val_off.data(), s.val_off.size() * 4);
-  if (!s.tomb.empty()) std::memcpy(tomb, s.tomb.data(), s.tomb.size());
+  const Result* res = (const Result*)h;
+  const Pool& pool = res->pool;
+  const std::vector<Rec>& recs = res->side[side];
+  Rng g(res->val_seed[side]);
+  uint64_t kp = 0, vp = 0;
+  key_off[0] = 0;
+  val_off[0] = 0;
+  for (size_t i = 0; i < recs.size(); ++i) {
+    if (i + 8 < recs.size()) __builtin_prefetch(pool.bytes.data() + pool.off[recs[i + 8].key]);
+    const Rec& rc = recs[i];
+    const uint32_t L = pool.len(rc.key);
+    std::memcpy(keys + kp, pool.key(rc.key), L);
+    kp += L;
+    key_off[i + 1] = (uint32_t)kp;
+    tomb[i] = rc.tomb;
+    uint32_t t = 0;
+    for (; t + 8 <= rc.vlen; t += 8) {
+      const uint64_t x = g.next();
+      std::memcpy(vals + vp + t, &x, 8);
+    }
+    if (t < rc.vlen) {
+      const uint64_t x = g.next();
+      std::memcpy(vals + vp + t, &x, rc.vlen - t);
+    }
+    vp += rc.vlen;
+    val_off[i + 1] = (uint32_t)vp;
+  }
 }
 
 void gen_free(void* h) { delete (Result*)h; }

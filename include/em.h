@@ -1,0 +1,205 @@
+/*
+ * em.h -- C ABI of the MI355X (gfx950) replacement merge into a front-coded
+ * bit payload.
+ *
+ * Two strictly sorted, unique-key string record sets are merged: an older
+ * side A and a newer side B.  On an equal key the newer record wins and a
+ * newer tombstone stays a record.  The survivors are front coded into one
+ * canonical MSB-first bit payload.  The calls, in order:
+ *
+ *   em_partition -> em_merge_keep (or em_collision_rank) -> em_fc_lengths
+ *                -> em_scan -> em_emit
+ *
+ * Between them the host reads the survivor count S (after the merge) and the
+ * payload length T in bits (after the scan), as the pages' host does.
+ *
+ * Conventions for every call:
+ *  - All buffer pointers are DEVICE pointers unless a parameter says "host".
+ *    The caller owns all memory; the library never allocates, frees or
+ *    synchronises.  Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream) and completes asynchronously: inputs must stay alive and
+ *    unchanged, and outputs must not be read, until the stream has reached the
+ *    call's work.
+ *  - `ws` is caller-owned device scratch of `ws_bytes` bytes, 256-byte
+ *    aligned, at least em_workspace_bytes() for the same sizes.  Its contents
+ *    on entry do not matter and are undefined on return.
+ *  - Every call returns EM_OK or a negative EM_E* code.  On error nothing
+ *    defined has been written and the outputs must not be used or published
+ *    (Everett, "GPU construction experiment": a failed construction is not
+ *    permission to publish).  Argument errors are detected before any work is
+ *    enqueued.
+ *  - Inputs are trusted, not admitted (Everett, "Byte-profile GPU merge",
+ *    "Pipeline"): each side must be strictly increasing in unsigned bytewise
+ *    order with a proper prefix first.  Unsorted input gives unspecified
+ *    output but never out-of-bounds access or a hang.
+ *  - Caps (Everett, "GPU construction experiment", the host bound check, and
+ *    "Byte-profile GPU merge", "Pipeline"): |A| + |B| < 2^24 records; each
+ *    arena < 2^32 bytes (u32 offsets); key and value lengths < 2^27 bytes.
+ *    Bit offsets and payload lengths are 64-bit, which lifts the pages'
+ *    2 Gibit prototype cap.
+ */
+#ifndef EM_H
+#define EM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EM_OK 0
+#define EM_EINVAL (-1)  /* null, misaligned or inconsistent argument */
+#define EM_ERANGE (-2)  /* a cap is exceeded */
+#define EM_ENOSPC (-3)  /* workspace or output capacity too small */
+#define EM_EDEVICE (-4) /* a HIP call failed; em_last_hip_error() has its code */
+
+#define EM_NONE 0xFFFFFFFFu          /* ordinal of a replaced (dropped) A record */
+#define EM_MAX_RECORDS (1u << 24)    /* |A| + |B| must be below this */
+#define EM_MAX_FIELD_BYTES (1u << 27) /* key and value lengths must be below this */
+#define EM_ARENA_PAD 32u             /* readable bytes required past each arena's end */
+#define EM_MAX_ITEMS_PER_PART 4096u  /* largest merge tile (outputs per partition) */
+
+/*
+ * One input side.  Record r has key bytes keys[key_off[r] .. key_off[r+1])
+ * and value bytes vals[val_off[r] .. val_off[r+1]).  tomb[r] != 0 marks a
+ * tombstone (its value bytes are ignored); tomb may be NULL (no tombstones).
+ * key_off and val_off have n+1 non-decreasing entries starting at 0.
+ * keys and vals must be 16-byte aligned and readable for key_bytes +
+ * EM_ARENA_PAD (resp. val_bytes + EM_ARENA_PAD) bytes; the pad's contents are
+ * never used.  key_bytes and val_bytes are host copies of key_off[n] and
+ * val_off[n].
+ */
+typedef struct {
+  const uint8_t *keys;
+  const uint32_t *key_off;
+  const uint8_t *vals;
+  const uint32_t *val_off;
+  const uint8_t *tomb;
+  uint32_t n;
+  uint64_t key_bytes;
+  uint64_t val_bytes;
+} em_side_t;
+
+/* Device scratch in bytes needed by every call below for these sizes
+ * (host only, enqueues nothing).  items_per_part as for em_partition. */
+size_t em_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t items_per_part);
+
+/*
+ * Host only.  A conservative upper bound on T, the payload length in bits:
+ * 8 * (all key and value arena bytes) + (|A| + |B|) * 184, since each record
+ * spends at most 61 bits on each of EG0(c), EG0(k-l) and EG0(value length)
+ * plus one presence bit under the caps (Everett, "GPU construction
+ * experiment": the host checks a conservative 64-bit bound before the scan).
+ * Writes *bound (host pointer).  EM_EINVAL on NULL arguments, EM_ERANGE when a
+ * cap is exceeded.
+ */
+int em_payload_bound_bits(const em_side_t *A, const em_side_t *B, uint64_t *bound);
+
+/*
+ * Merge-path partition ("CUDA merge path: merging sorted arrays in
+ * parallel", "The merge matrix, and the diagonal that cuts it"; Everett,
+ * "GPU construction experiment", the merge paragraph).  For p = 0..P with
+ * P = ceil(N / items_per_part), N = |A| + |B|, writes splits[p] = the co-rank
+ * of diagonal d_p = min(p * items_per_part, N): the number of A records among
+ * the first d_p outputs of the stable merge in which equal keys put A first.
+ * splits: P+1 u32.  1 <= items_per_part <= EM_MAX_ITEMS_PER_PART.
+ */
+int em_partition(const em_side_t *A, const em_side_t *B, uint32_t items_per_part, uint32_t *splits,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Stable merge and keep-newer scan (Everett, "GPU construction experiment",
+ * the merge paragraph and the paragraph on the compacted order).  Merges each
+ * partition of em_partition's splits (same items_per_part), drops every A
+ * record whose key equals the next merged record's key, and compacts the
+ * survivors in merged order.  A reference names a record: A_i -> i,
+ * B_j -> |A| + j.  Writes:
+ *   final_refs[0..S)  survivors' references in output order (capacity N);
+ *   ord_A[|A|]        output ordinal of A_i, or EM_NONE if replaced (nullable);
+ *   ord_B[|B|]        output ordinal of B_j (nullable);
+ *   d_S[0]            S, the survivor count (device u32).
+ */
+int em_merge_keep(const em_side_t *A, const em_side_t *B, const uint32_t *splits,
+                  uint32_t items_per_part, uint32_t *final_refs, uint32_t *ord_A, uint32_t *ord_B,
+                  uint32_t *d_S, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Collision-bitmap variant of the keep step (Everett, "Collision bitmap and
+ * rank experiment", "Corrected record ordinals", "Temporary rank layouts" and
+ * "The three experimental paths").  Clears a bitmap over A, marks bit C_i by
+ * atomic OR when lower_bound(A, B_j) = i holds an equal key, builds the
+ * temporary rank512 directory (count, scan, finish), and places B_j at
+ * j + lb_j - R(lb_j) and each surviving A_i at i + lb(B, A_i) - R(i), where
+ * R is the exclusive collision rank; A is handled in tiles of 32 consecutive
+ * records with one search and a monotone cursor.  Same outputs and meaning as
+ * em_merge_keep (ord_A / ord_B nullable); needs no partition.
+ */
+int em_collision_rank(const em_side_t *A, const em_side_t *B, uint32_t *final_refs, uint32_t *ord_A,
+                      uint32_t *ord_B, uint32_t *d_S, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Exact record lengths (Everett, "GPU construction experiment": the c_i
+ * control equation and the record grammar paragraph).  For survivor i with
+ * key length k_i bits and exact bit LCP l_i with survivor i-1 (l_0 = 0,
+ * clamped to the shorter key): c_i = 1 + l_i when i mod 15 = 0, else
+ * k_{i-1} - l_i; v_i = 1 for a tombstone, else 1 + E(len) + 8 len;
+ * len_bits[i] = E(c_i) + E(k_i - l_i) + (k_i - l_i) + v_i with
+ * E(x) = 2 floor(log2(x+1)) + 1.  S is the host value read from d_S.
+ * len_bits: S u32.  lcp_bits: S u32 receiving l_i (nullable; em_emit reuses it).
+ */
+int em_fc_lengths(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs, uint32_t S,
+                  uint32_t *len_bits, uint32_t *lcp_bits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Exclusive scan of record lengths into 64-bit bit offsets (Everett, "GPU
+ * construction experiment": one global scan, no per-chunk reset).
+ * off: S+1 u64; off[0] = 0, off[i+1] = off[i] + len_bits[i], off[S] = T.
+ */
+int em_scan(const uint32_t *len_bits, uint32_t S, uint64_t *off, void *ws, size_t ws_bytes,
+            void *stream);
+
+/*
+ * Word-owned payload emission (Everett, "GPU construction experiment": one
+ * invocation owns each final 32-bit word, gathers its bits and writes it
+ * once; payload bits are MSB first; no padding between records; unused final
+ * bits are zero; the output key suffix is copied from the selected source
+ * record's own key).  Record i occupies bits [off[i], off[i+1]):
+ * EG0(c_i) EG0(k_i - l_i) key bits [l_i, k_i) then 0 (tombstone) or
+ * 1 EG0(value length) value bytes.  EG0(x) is floor(log2(x+1)) zero bits
+ * followed by x+1 in binary.  Stream bit p is bit 7 - (p mod 8) of payload
+ * byte p / 8, so each u32 word holds four consecutive stream bytes.
+ * Writes exactly ceil(T / 32) words; payload_words is the capacity.
+ * lcp_bits from em_fc_lengths (nullable: recomputed when NULL).  T is the host
+ * value off[S].
+ */
+int em_emit(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs,
+            const uint32_t *lcp_bits, uint32_t S, const uint64_t *off, uint64_t T, uint32_t *payload,
+            uint64_t payload_words, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Rank512 probe (Everett, "Collision bitmap and rank experiment",
+ * "Validation and measurement plan": compare GPU rank queries against scalar
+ * prefix counts).  Builds the same temporary rank512 directory that
+ * em_collision_rank uses from `bitmap` (nbits bits; bit q is bit q mod 32 of
+ * u32 word q / 32; bits >= nbits are ignored) and writes, for each of the
+ * npos positions p <= nbits, out[t] = number of set bits below p.
+ * nbits < 2^24 + 2^13.
+ */
+int em_rank512_probe(const uint32_t *bitmap, uint32_t nbits, const uint32_t *positions, uint32_t npos,
+                     uint32_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes em_rank512_probe needs for nbits bits (host only). */
+size_t em_rank512_workspace_bytes(uint32_t nbits);
+
+/* Text for an EM_* code (static string). */
+const char *em_strerror(int code);
+
+/* The hipError_t of the most recent EM_EDEVICE return on this thread (0 if none). */
+int em_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EM_H */

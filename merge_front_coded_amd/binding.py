@@ -1,0 +1,191 @@
+"""ctypes binding of the C ABI in include/em.h: same names, marshalling only.
+
+Device buffers are torch tensors (PyTorch-ROCm supplies device memory and
+streams); every step of the path runs in the HIP library.  If ``libem.so``
+has not been built the import fails loudly: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libem.so")
+
+EM_OK = 0
+EM_EINVAL = -1
+EM_ERANGE = -2
+EM_ENOSPC = -3
+EM_EDEVICE = -4
+EM_NONE = 0xFFFFFFFF
+EM_MAX_RECORDS = 1 << 24
+EM_ARENA_PAD = 32
+EM_MAX_ITEMS_PER_PART = 4096
+
+
+class EmError(RuntimeError):
+    def __init__(self, code: int, call: str, lib):
+        msg = lib.em_strerror(code).decode()
+        if code == EM_EDEVICE:
+            msg += f" (hipError {lib.em_last_hip_error()})"
+        super().__init__(f"{call}: {msg} [{code}]")
+        self.code = code
+
+
+class em_side_t(ctypes.Structure):
+    _fields_ = [("keys", ctypes.c_void_p), ("key_off", ctypes.c_void_p),
+                ("vals", ctypes.c_void_p), ("val_off", ctypes.c_void_p),
+                ("tomb", ctypes.c_void_p), ("n", ctypes.c_uint32),
+                ("key_bytes", ctypes.c_uint64), ("val_bytes", ctypes.c_uint64)]
+
+
+def load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m merge_front_coded_amd.build` "
+                          "(the merge path runs only in the HIP library)")
+    lib = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.POINTER(em_side_t)
+    u32, u64, sz, i32 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_int
+    sig = {
+        "em_workspace_bytes": (sz, [u32, u32, u32]),
+        "em_payload_bound_bits": (i32, [S, S, ctypes.POINTER(u64)]),
+        "em_partition": (i32, [S, S, u32, P, P, sz, P]),
+        "em_merge_keep": (i32, [S, S, P, u32, P, P, P, P, P, sz, P]),
+        "em_collision_rank": (i32, [S, S, P, P, P, P, P, sz, P]),
+        "em_fc_lengths": (i32, [S, S, P, u32, P, P, P, sz, P]),
+        "em_scan": (i32, [P, u32, P, P, sz, P]),
+        "em_emit": (i32, [S, S, P, P, u32, P, u64, P, u64, P, sz, P]),
+        "em_rank512_probe": (i32, [P, u32, P, u32, P, P, sz, P]),
+        "em_rank512_workspace_bytes": (sz, [u32]),
+        "em_strerror": (ctypes.c_char_p, [i32]),
+        "em_last_hip_error": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = load_library()
+    return _lib
+
+
+def _p(t) -> int | None:
+    """Device address of a tensor (None for None)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("buffers passed to the HIP library must be device tensors")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(rc: int, call: str):
+    if rc != EM_OK:
+        raise EmError(rc, call, lib())
+
+
+class DeviceSide:
+    """One input side in device memory, laid out as em_side_t requires."""
+
+    def __init__(self, keys, key_off, vals, val_off, tomb, n: int, key_bytes: int, val_bytes: int):
+        self.keys, self.key_off, self.vals, self.val_off, self.tomb = keys, key_off, vals, val_off, tomb
+        self.n, self.key_bytes, self.val_bytes = int(n), int(key_bytes), int(val_bytes)
+        self._struct = em_side_t(_p(keys), _p(key_off), _p(vals), _p(val_off), _p(tomb), self.n,
+                                 self.key_bytes, self.val_bytes)
+
+    @property
+    def struct(self) -> em_side_t:
+        return self._struct
+
+    @staticmethod
+    def _arena(data, device) -> torch.Tensor:
+        n = int(data.shape[0])
+        t = torch.zeros(((n + 15) // 16) * 16 + EM_ARENA_PAD, dtype=torch.uint8, device=device)
+        if n:
+            t[:n].copy_(torch.from_numpy(data))
+        return t
+
+    @classmethod
+    def from_host(cls, hs, device="cuda"):
+        """Upload a host side (key/value arenas, u32 offsets, tombstone bytes)."""
+        keys = cls._arena(hs.keys, device)
+        vals = cls._arena(hs.vals, device)
+        key_off = torch.from_numpy(hs.key_off.view("int32")).to(device)
+        val_off = torch.from_numpy(hs.val_off.view("int32")).to(device)
+        tomb = torch.from_numpy(hs.tomb).to(device) if hs.tomb.size else \
+            torch.zeros(16, dtype=torch.uint8, device=device)
+        return cls(keys, key_off, vals, val_off, tomb, hs.tomb.shape[0], int(hs.key_off[-1]),
+                   int(hs.val_off[-1]))
+
+    def nbytes(self) -> int:
+        """Input bytes of this side: arenas, offsets and tombstone flags."""
+        return self.key_bytes + self.val_bytes + 8 * (self.n + 1) + self.n
+
+
+# ---- the C ABI, one wrapper per entry point ----
+
+def em_workspace_bytes(nA: int, nB: int, items_per_part: int) -> int:
+    return int(lib().em_workspace_bytes(nA, nB, items_per_part))
+
+
+def em_rank512_workspace_bytes(nbits: int) -> int:
+    return int(lib().em_rank512_workspace_bytes(nbits))
+
+
+def em_payload_bound_bits(A: DeviceSide, B: DeviceSide) -> int:
+    out = ctypes.c_uint64()
+    _check(lib().em_payload_bound_bits(ctypes.byref(A.struct), ctypes.byref(B.struct),
+                                       ctypes.byref(out)), "em_payload_bound_bits")
+    return int(out.value)
+
+
+def em_partition(A, B, items_per_part, splits, ws, stream=None):
+    _check(lib().em_partition(ctypes.byref(A.struct), ctypes.byref(B.struct), items_per_part,
+                              _p(splits), _p(ws), ws.numel(), _stream(stream)), "em_partition")
+
+
+def em_merge_keep(A, B, splits, items_per_part, final_refs, ord_A, ord_B, d_S, ws, stream=None):
+    _check(lib().em_merge_keep(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(splits),
+                               items_per_part, _p(final_refs), _p(ord_A), _p(ord_B), _p(d_S), _p(ws),
+                               ws.numel(), _stream(stream)), "em_merge_keep")
+
+
+def em_collision_rank(A, B, final_refs, ord_A, ord_B, d_S, ws, stream=None):
+    _check(lib().em_collision_rank(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs),
+                                   _p(ord_A), _p(ord_B), _p(d_S), _p(ws), ws.numel(),
+                                   _stream(stream)), "em_collision_rank")
+
+
+def em_fc_lengths(A, B, final_refs, S, len_bits, lcp_bits, ws, stream=None):
+    _check(lib().em_fc_lengths(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), S,
+                               _p(len_bits), _p(lcp_bits), _p(ws), ws.numel(), _stream(stream)),
+           "em_fc_lengths")
+
+
+def em_scan(len_bits, S, off, ws, stream=None):
+    _check(lib().em_scan(_p(len_bits), S, _p(off), _p(ws), ws.numel(), _stream(stream)), "em_scan")
+
+
+def em_emit(A, B, final_refs, lcp_bits, S, off, T, payload, ws, stream=None):
+    _check(lib().em_emit(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), _p(lcp_bits),
+                         S, _p(off), T, _p(payload), payload.numel(), _p(ws), ws.numel(),
+                         _stream(stream)), "em_emit")
+
+
+def em_rank512_probe(bitmap, nbits, positions, out, ws, stream=None):
+    _check(lib().em_rank512_probe(_p(bitmap), nbits, _p(positions), positions.numel(), _p(out), _p(ws),
+                                  ws.numel(), _stream(stream)), "em_rank512_probe")

@@ -1,0 +1,71 @@
+"""Host orchestration of the hot path: the six C-ABI calls in order.
+
+partition -> merge_keep (or collision_rank) -> [host reads S] -> fc_lengths
+-> scan -> [host reads T] -> emit.  All buffers are allocated once up front
+(sized from em_workspace_bytes and em_payload_bound_bits) and reused by every
+run, so a run enqueues kernels and performs exactly the two small reads.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as em
+
+
+class Pipeline:
+    def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int = 2048,
+                 path: str = "merge", keep_ordinals: bool = True, keep_lcp: bool = True,
+                 device="cuda"):
+        if path not in ("merge", "collision"):
+            raise ValueError("path is 'merge' or 'collision'")
+        self.A, self.B = A, B
+        self.items = int(items_per_part)
+        self.path = path
+        N = A.n + B.n
+        self.N = N
+        P = (N + self.items - 1) // self.items
+        i32 = dict(dtype=torch.int32, device=device)
+        self.splits = torch.empty(P + 1, **i32)
+        self.final = torch.empty(max(N, 1), **i32)
+        self.ord_A = torch.empty(max(A.n, 1), **i32) if keep_ordinals else None
+        self.ord_B = torch.empty(max(B.n, 1), **i32) if keep_ordinals else None
+        self.d_S = torch.zeros(1, **i32)
+        self.len_bits = torch.empty(max(N, 1) + 4, **i32)
+        self.lcp = torch.empty(max(N, 1), **i32) if keep_lcp else None
+        self.off = torch.empty(N + 1, dtype=torch.int64, device=device)
+        self.bound_bits = em.em_payload_bound_bits(A, B)
+        self.payload = torch.empty((self.bound_bits + 31) // 32 + 1, **i32)
+        ws_bytes = em.em_workspace_bytes(A.n, B.n, self.items)
+        self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
+        self.S = 0
+        self.T = 0
+
+    def run(self, stream=None):
+        """One pass of the whole path.  Returns (S, T)."""
+        A, B = self.A, self.B
+        if self.path == "merge":
+            em.em_partition(A, B, self.items, self.splits, self.ws, stream)
+            em.em_merge_keep(A, B, self.splits, self.items, self.final, self.ord_A, self.ord_B,
+                             self.d_S, self.ws, stream)
+        else:
+            em.em_collision_rank(A, B, self.final, self.ord_A, self.ord_B, self.d_S, self.ws, stream)
+        S = int(self.d_S.item()) & 0xFFFFFFFF
+        em.em_fc_lengths(A, B, self.final, S, self.len_bits, self.lcp, self.ws, stream)
+        em.em_scan(self.len_bits, S, self.off, self.ws, stream)
+        T = int(self.off[S].item())
+        em.em_emit(A, B, self.final, self.lcp, S, self.off, T, self.payload, self.ws, stream)
+        self.S, self.T = S, T
+        return S, T
+
+    # ---- host copies of the results (for checks; not part of a run) ----
+
+    def payload_bytes(self) -> bytes:
+        nw = (self.T + 31) // 32
+        return self.payload[:nw].cpu().numpy().tobytes()
+
+    def host(self, name: str, count: int | None = None):
+        t = getattr(self, name)
+        if count is not None:
+            t = t[:count]
+        a = t.cpu().numpy()
+        return a.view("uint32") if a.dtype.itemsize == 4 else a.view("uint64")

@@ -1,0 +1,100 @@
+"""The C ABI on the CPU: the built library loads and exports every function
+include/em.h declares; host-only calls and argument checks behave as the
+header states.  Nothing here launches GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "em.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(em_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from merge_front_coded_amd import binding
+    return binding.load_library()
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("em_partition", "em_merge_keep", "em_collision_rank", "em_fc_lengths", "em_scan",
+              "em_emit", "em_workspace_bytes", "em_payload_bound_bits", "em_rank512_probe",
+              "em_strerror", "em_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, f"libem.so lacks {missing}"
+
+
+def test_binding_wraps_every_declared_symbol():
+    from merge_front_coded_amd import binding
+    missing = [n for n in _declared() if n not in ("em_strerror", "em_last_hip_error")
+               and not hasattr(binding, n)]
+    assert not missing
+
+
+def test_strerror_and_last_error(lib):
+    assert lib.em_strerror(0) == b"success"
+    assert b"capacity" in lib.em_strerror(-3)
+    assert lib.em_strerror(-99) == b"unknown error code"
+    assert lib.em_last_hip_error() == 0
+
+
+def _side(n=0, key_bytes=0, val_bytes=0, ptr=0x1000):
+    from merge_front_coded_amd.binding import em_side_t
+    return em_side_t(ptr, ptr, ptr, ptr, None, n, key_bytes, val_bytes)
+
+
+def test_payload_bound(lib):
+    A, B = _side(10, 100, 50), _side(5, 40, 0)
+    out = ctypes.c_uint64()
+    assert lib.em_payload_bound_bits(ctypes.byref(A), ctypes.byref(B), ctypes.byref(out)) == 0
+    assert out.value == 8 * (100 + 50 + 40) + 15 * 184
+    big = _side(1 << 24, 0, 0)
+    assert lib.em_payload_bound_bits(ctypes.byref(big), ctypes.byref(B), ctypes.byref(out)) == -2
+    assert lib.em_payload_bound_bits(None, ctypes.byref(B), ctypes.byref(out)) == -1
+
+
+def test_workspace_sizes_grow_with_inputs(lib):
+    small = lib.em_workspace_bytes(1000, 1000, 2048)
+    large = lib.em_workspace_bytes(8_000_000, 8_000_000, 2048)
+    assert 0 < small < large and large % 256 == 0
+    assert lib.em_workspace_bytes(8_000_000, 8_000_000, 1) > large  # one descriptor per output
+    assert lib.em_rank512_workspace_bytes(0) > 0
+
+
+def test_argument_errors_before_any_launch(lib):
+    A, B = _side(), _side()
+    buf = ctypes.c_void_p(0x100000)
+    # null splits, zero or oversized partition sizes
+    assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 16, None, None, 0, None) == -1
+    assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 0, buf, None, 0, None) == -1
+    assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 4097, buf, None, 0, None) == -1
+    # misaligned arena
+    bad = _side(ptr=0x1001)
+    assert lib.em_partition(ctypes.byref(bad), ctypes.byref(B), 16, buf, None, 0, None) == -1
+    # record cap
+    big = _side(n=(1 << 24) - 1)
+    one = _side(n=1)
+    assert lib.em_partition(ctypes.byref(big), ctypes.byref(one), 16, buf, None, 0, None) == -2
+    # workspace too small
+    A5 = _side(n=5, key_bytes=5, val_bytes=0)
+    assert lib.em_merge_keep(ctypes.byref(A5), ctypes.byref(B), buf, 4, buf, None, None, buf,
+                             ctypes.c_void_p(0x100000), 0, None) == -3
+    assert lib.em_scan(buf, 10, buf, ctypes.c_void_p(0x100000), 0, None) == -3
+    # emit: S and T must agree on emptiness; payload capacity
+    assert lib.em_emit(ctypes.byref(A5), ctypes.byref(B), buf, None, 0, buf, 5, buf, 1, buf, 0,
+                       None) == -1
+    assert lib.em_emit(ctypes.byref(A5), ctypes.byref(B), buf, None, 2, buf, 100, buf, 3, buf, 0,
+                       None) == -3
+    assert lib.em_rank512_probe(None, 5, None, 0, None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
