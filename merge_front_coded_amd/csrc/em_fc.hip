@@ -84,35 +84,40 @@ __global__ __launch_bounds__(kLenBlock) void k_fc_lengths(em_side_t A, em_side_t
 // word whose first bit lies inside them; the last such word may continue into
 // up to kEmitExtra following records (each record is at least 3 bits long:
 // one bit for each EG0 field when its argument is 0, one value bit).
+//
+// The workgroup first turns its records into a table of bit segments in LDS,
+// five per record: the EG0 control field(s) as immediate bits, the key suffix
+// as a span of source bits, the presence bit and EG0(value length) as
+// immediate bits, and the value bytes as a span of source bits.  A map from
+// each owned word to the segment holding its first bit follows.  Each thread
+// then assembles whole 32-bit words: a map read, and per segment piece either
+// a shift of an immediate or two aligned dword loads and a funnel shift.
 
 constexpr int kEmitBlock = 256;
 constexpr uint32_t kEmitRecs = 256;
 constexpr uint32_t kEmitExtra = 16;
 constexpr uint32_t kEmitTable = kEmitRecs + kEmitExtra;
+constexpr uint32_t kSegPerRec = 5;
+constexpr uint32_t kEmitSegs = kEmitTable * kSegPerRec;
+constexpr uint32_t kEmitMapWords = 8192;
+constexpr uint32_t kRecPerThread = (kEmitTable + kEmitBlock - 1) / kEmitBlock;
 
+// segment kinds: 0 immediate, 1 A keys, 2 B keys, 3 A values, 4 B values
 struct EmitShared {
-  uint64_t off[kEmitTable + 1];  // record start bits; off[cnt] = end of the last
-  uint32_t c1[kEmitTable];       // c + 1 (the EG0 field value)
-  uint32_t s1[kEmitTable];       // k - l + 1
-  uint32_t kpos[kEmitTable];     // key byte offset in its arena
-  uint32_t l[kEmitTable];        // first emitted key bit
-  uint32_t klen[kEmitTable];     // k - l (bits); holds k until the controls are formed
-  uint32_t vpos[kEmitTable];     // value byte offset
-  uint32_t vlen[kEmitTable];     // value bytes (0 for a tombstone)
-  uint32_t info[kEmitTable];     // E(c) | E(k-l) << 8 | E(vlen) << 16 | side B << 24 | tomb << 25
+  uint64_t start[kEmitSegs];  // absolute first bit in the payload
+  uint64_t data[kEmitSegs];   // immediate bits, or first source bit in its arena
+  uint32_t len[kEmitSegs];    // bits
+  uint32_t kind[kEmitSegs];
+  uint16_t map[kEmitMapWords];
+  uint32_t kbits[kEmitTable];
   uint32_t kprev0;
 };
 
-__device__ __forceinline__ uint32_t field_bits(uint64_t v, uint32_t e, uint32_t o, uint32_t n) {
-  // n bits of the e-bit field v starting o bits after its most significant bit
-  return static_cast<uint32_t>((v >> (e - o - n)) & ((1ull << n) - 1));
-}
-
-__device__ __forceinline__ uint32_t stream_bits(const uint8_t* base, uint32_t pos, uint32_t bit,
-                                                uint32_t n) {
-  // n (<= 32) bits of the byte string at `pos`, starting at bit `bit`
-  const uint64_t w = load_be8(base, pos + (bit >> 3));
-  return static_cast<uint32_t>((w << (bit & 7)) >> (64 - n));
+__device__ __forceinline__ uint32_t source_bits(const uint8_t* base, uint64_t bitpos, uint32_t n) {
+  // n (1..32) bits of an arena's MSB-first bit stream starting at bitpos
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(base) + (bitpos >> 5);
+  const uint64_t x = (static_cast<uint64_t>(__builtin_bswap32(w[0])) << 32) | __builtin_bswap32(w[1]);
+  return static_cast<uint32_t>((x << (bitpos & 31)) >> (64 - n));
 }
 
 __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
@@ -126,8 +131,14 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
   const uint32_t nown = (S - R0) < kEmitRecs ? S - R0 : kEmitRecs;
   const uint32_t cnt = (S - R0) < kEmitTable ? S - R0 : kEmitTable;
 
-  // phase 1: per-record fields that need no neighbour
-  for (uint32_t j = tid; j < cnt; j += kEmitBlock) {
+  // phase 1: per-record fields (thread t takes records t and t + 256)
+  uint32_t r_kpos[kRecPerThread], r_l[kRecPerThread], r_vpos[kRecPerThread], r_vlen[kRecPerThread];
+  uint32_t r_info[kRecPerThread];
+  uint64_t r_off[kRecPerThread];
+#pragma unroll
+  for (uint32_t u = 0; u < kRecPerThread; ++u) {
+    const uint32_t j = tid + u * kEmitBlock;
+    if (j >= cnt) continue;
     const uint32_t r = R0 + j;
     uint32_t idx;
     const SideView s = pick(A, B, final_refs[r], idx);
@@ -145,16 +156,15 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     uint32_t vlen;
     bool tomb;
     value_bits(s, idx, vlen, tomb);
-    sh.off[j] = off[r];
-    sh.kpos[j] = x.pos;
-    sh.l[j] = l;
-    sh.klen[j] = 8u * x.len;
-    sh.vpos[j] = tomb ? 0u : s.val_off[idx];
-    sh.vlen[j] = vlen;
-    sh.info[j] = (s.isB ? 1u << 24 : 0u) | (tomb ? 1u << 25 : 0u);
+    r_kpos[u] = x.pos;
+    r_l[u] = l;
+    r_vpos[u] = tomb ? 0u : s.val_off[idx];
+    r_vlen[u] = vlen;
+    r_info[u] = (s.isB ? 1u : 0u) | (tomb ? 2u : 0u);
+    r_off[u] = off[r];
+    sh.kbits[j] = 8u * x.len;
   }
   if (tid == 0) {
-    sh.off[cnt] = off[R0 + cnt];
     uint32_t kp = 0;
     if (R0 > 0) {
       uint32_t pidx;
@@ -164,42 +174,88 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     sh.kprev0 = kp;
   }
   __syncthreads();
-  // phase 2: the controls need the predecessor's key length
-  uint32_t c_[2], k_[2];
-  for (uint32_t j = tid, u = 0; j < cnt; j += kEmitBlock, ++u) {
-    const uint32_t kprev = j ? sh.klen[j - 1] : sh.kprev0;
+
+  // phase 2: controls and the segment table
+#pragma unroll
+  for (uint32_t u = 0; u < kRecPerThread; ++u) {
+    const uint32_t j = tid + u * kEmitBlock;
+    if (j >= cnt) continue;
     const uint32_t r = R0 + j;
-    c_[u] = (r % 15u == 0) ? 1u + sh.l[j] : kprev - sh.l[j];
-    k_[u] = sh.klen[j];
+    const uint32_t k = sh.kbits[j], l = r_l[u];
+    const uint32_t kprev = j ? sh.kbits[j - 1] : sh.kprev0;
+    const uint32_t c = (r % 15u == 0) ? 1u + l : kprev - l;
+    const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l);
+    const bool isB = r_info[u] & 1u, tomb = r_info[u] & 2u;
+    const uint32_t base = j * kSegPerRec;
+    uint64_t at = r_off[u];
+    // EG0(c) EG0(k-l): one immediate when both fit in 64 bits
+    uint32_t len0, len1;
+    uint64_t d0, d1;
+    if (e1 + e2 <= 64) {
+      len0 = e1 + e2;
+      d0 = (static_cast<uint64_t>(c + 1u) << e2) | (k - l + 1u);
+      len1 = 0;
+      d1 = 0;
+    } else {
+      len0 = e1;
+      d0 = c + 1u;
+      len1 = e2;
+      d1 = k - l + 1u;
+    }
+    const uint32_t ev = eg0_len(r_vlen[u]);
+    const uint32_t lens[kSegPerRec] = {len0, len1, k - l, tomb ? 1u : 1u + ev, 8u * r_vlen[u]};
+    const uint64_t datas[kSegPerRec] = {
+        d0, d1, 8ull * r_kpos[u] + l,
+        tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(r_vlen[u]) + 1ull)), 8ull * r_vpos[u]};
+    const uint32_t kinds[kSegPerRec] = {0u, 0u, isB ? 2u : 1u, 0u, isB ? 4u : 3u};
+#pragma unroll
+    for (uint32_t q = 0; q < kSegPerRec; ++q) {
+      sh.start[base + q] = at;
+      sh.len[base + q] = lens[q];
+      sh.data[base + q] = datas[q];
+      sh.kind[base + q] = kinds[q];
+      at += lens[q];
+    }
   }
+  const uint32_t nseg = cnt * kSegPerRec;
+  const uint32_t nown_seg = nown * kSegPerRec;
   __syncthreads();
-  for (uint32_t j = tid, u = 0; j < cnt; j += kEmitBlock, ++u) {
-    const uint32_t c = c_[u], k = k_[u], l = sh.l[j];
-    sh.c1[j] = c + 1u;
-    sh.s1[j] = k - l + 1u;
-    sh.klen[j] = k - l;
-    sh.info[j] |= eg0_len(c) | (eg0_len(k - l) << 8) | (eg0_len(sh.vlen[j]) << 16);
+
+  // phase 3: map each owned word to the segment holding its first bit
+  const uint64_t w_end = (T + 31) >> 5;
+  const uint64_t bit_lo = sh.start[0];
+  const uint64_t bit_hi = nown < cnt ? sh.start[nown_seg] : sh.start[nseg - 1] + sh.len[nseg - 1];
+  const uint64_t w_lo = (bit_lo + 31) >> 5;
+  const uint64_t w_hi = min((bit_hi + 31) >> 5, w_end);
+  const bool use_map = w_hi > w_lo && (w_hi - w_lo) <= kEmitMapWords;
+  if (use_map) {
+    for (uint32_t q = tid; q < nown_seg; q += kEmitBlock) {
+      const uint32_t ln = sh.len[q];
+      if (!ln) continue;
+      const uint64_t st = sh.start[q];
+      const uint64_t a = (st + 31) >> 5, b = min((st + ln + 31) >> 5, w_hi);
+      for (uint64_t w = a; w < b; ++w) sh.map[w - w_lo] = static_cast<uint16_t>(q);
+    }
   }
   __syncthreads();
 
-  // phase 3: every word whose first bit lies in this block's own records
-  const uint64_t bit_lo = sh.off[0];
-  const uint64_t bit_hi = sh.off[nown];
-  const uint64_t w_lo = (bit_lo + 31) >> 5;
-  const uint64_t w_end = (T + 31) >> 5;
-  const uint64_t w_hi = min((bit_hi + 31) >> 5, w_end);
+  // phase 4: assemble and store every owned word once
   for (uint64_t w = w_lo + tid; w < w_hi; w += kEmitBlock) {
     uint64_t pos = w << 5;
-    // last own record starting at or before pos
-    uint32_t lo = 0, hi = nown - 1;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      if (sh.off[mid] <= pos)
-        lo = mid;
-      else
-        hi = mid - 1;
+    uint32_t si;
+    if (use_map) {
+      si = sh.map[w - w_lo];
+    } else {
+      uint32_t lo = 0, hi = nown_seg - 1;
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (sh.start[mid] <= pos)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      si = lo;
     }
-    uint32_t j = lo;
     uint64_t acc = 0;
     uint32_t need = 32;
     while (need) {
@@ -207,38 +263,23 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
         acc <<= need;
         break;
       }
-      while (j + 1 < cnt && pos >= sh.off[j + 1]) ++j;
-      const uint32_t info = sh.info[j];
-      const uint32_t e1 = info & 0xFF, e2 = (info >> 8) & 0xFF, ev = (info >> 16) & 0xFF;
-      const bool tomb = (info >> 25) & 1u;
-      const uint32_t rel = static_cast<uint32_t>(pos - sh.off[j]);
-      const uint32_t b1 = e1, b2 = b1 + e2, b3 = b2 + sh.klen[j];
-      const uint32_t b4 = b3 + (tomb ? 1u : 1u + ev);
-      uint32_t n, bits;
-      if (rel < b1) {
-        n = min(need, b1 - rel);
-        bits = field_bits(sh.c1[j], e1, rel, n);
-      } else if (rel < b2) {
-        n = min(need, b2 - rel);
-        bits = field_bits(sh.s1[j], e2, rel - b1, n);
-      } else if (rel < b3) {
-        n = min(need, b3 - rel);
-        const uint8_t* keys = (info >> 24) & 1u ? B.keys : A.keys;
-        bits = stream_bits(keys, sh.kpos[j], sh.l[j] + (rel - b2), n);
-      } else if (rel < b4) {
-        n = min(need, b4 - rel);
-        // presence bit then EG0(vlen): the field value is 2^ev + vlen + 1 over 1 + ev bits
-        const uint64_t vh = tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(sh.vlen[j]) + 1ull));
-        bits = field_bits(vh, b4 - b3, rel - b3, n);
+      while (si + 1 < nseg && pos >= sh.start[si] + sh.len[si]) ++si;
+      const uint64_t st = sh.start[si];
+      const uint32_t ln = sh.len[si];
+      if (pos >= st + ln) {  // cannot happen for offsets produced by em_scan
+        acc <<= need;
+        break;
+      }
+      const uint32_t rel = static_cast<uint32_t>(pos - st);
+      const uint32_t n = min(need, ln - rel);
+      const uint32_t kind = sh.kind[si];
+      const uint64_t d = sh.data[si];
+      uint32_t bits;
+      if (kind == 0) {
+        bits = static_cast<uint32_t>((d >> (ln - rel - n)) & ((1ull << n) - 1));
       } else {
-        const uint32_t b5 = b4 + 8u * sh.vlen[j];
-        if (rel >= b5) {  // cannot happen for offsets produced by em_scan
-          acc <<= need;
-          break;
-        }
-        n = min(need, b5 - rel);
-        const uint8_t* vals = (info >> 24) & 1u ? B.vals : A.vals;
-        bits = stream_bits(vals, sh.vpos[j], rel - b4, n);
+        const uint8_t* base = kind == 1 ? A.keys : kind == 2 ? B.keys : kind == 3 ? A.vals : B.vals;
+        bits = source_bits(base, d + rel, n);
       }
       acc = (acc << n) | bits;
       need -= n;

@@ -125,11 +125,15 @@ constexpr uint64_t kDescAgg = 1ull << 62;
 constexpr uint64_t kDescIncl = 2ull << 62;
 constexpr uint64_t kDescValue = (1ull << 62) - 1;
 
+// Relaxed agent-scope atomics: the status and the value travel in the same
+// word and no other memory is handed between tiles, so no ordering is needed.
+// (Acquire/release at agent scope would write back and invalidate the XCD's L2
+// on every access, which also evicts the key bytes the merge relies on.)
 __device__ __forceinline__ void desc_store(uint64_t* d, uint64_t v) {
-  __hip_atomic_store(d, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t desc_load(const uint64_t* d) {
-  return __hip_atomic_load(const_cast<uint64_t*>(d), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(const_cast<uint64_t*>(d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Called by all 64 lanes of ONE wave.  Publishes `aggregate` for `tile`,

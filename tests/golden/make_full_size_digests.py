@@ -1,0 +1,64 @@
+#!/usr/bin/env python3
+"""Write full_size_digests.json: SHA-256 digests of the CPU oracle's outputs on
+the five full-size seeded workloads, so that the GPU parity tests can compare
+every output element (through its digest) without rerunning the bit-at-a-time
+oracle on the GPU host.
+
+Calls only gen/ (inputs) and oracle/ (expected values).  Run from the
+repository root:  python tests/golden/make_full_size_digests.py [ids...]
+"""
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+import oracle  # noqa: E402
+
+OUT = os.path.join(HERE, "full_size_digests.json")
+ITEMS = 2048  # partition size of the benchmark's launch configuration
+
+
+def sha(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(a.tobytes())
+    return h.hexdigest()
+
+
+def input_digest(A, B) -> str:
+    return sha(A.keys, A.key_off, A.vals, A.val_off, A.tomb, B.keys, B.key_off, B.vals, B.val_off,
+               B.tomb)
+
+
+def main(ids):
+    data = {}
+    if os.path.exists(OUT):
+        with open(OUT) as f:
+            data = json.load(f)
+    for wid in ids:
+        t0 = time.time()
+        A, B = gen.make(wid)
+        refs = oracle.merge(A, B)
+        final, ord_A, ord_B, S = oracle.keep(A, B, refs)
+        len_bits, lcp_bits, off, T, payload = oracle.encode(A, B, final)
+        splits = oracle.splits(refs, A.n, ITEMS)
+        data[str(wid)] = {
+            "workload": gen.WORKLOADS[wid].name, "nA": A.n, "nB": B.n, "items_per_part": ITEMS,
+            "input": input_digest(A, B), "S": S, "T": T,
+            "splits": sha(splits), "final": sha(final), "ord_A": sha(ord_A), "ord_B": sha(ord_B),
+            "len_bits": sha(len_bits), "lcp_bits": sha(lcp_bits), "off": sha(off),
+            "payload": sha(payload), "payload_bytes": int(payload.size),
+        }
+        print(f"workload {wid}: S={S} T={T} ({time.time() - t0:.1f}s)", flush=True)
+        with open(OUT, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    main([int(x) for x in sys.argv[1:]] or [1, 2, 3, 4, 5])
