@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
     ap.add_argument("--path", choices=("merge", "collision"), default="merge")
-    ap.add_argument("--items", type=int, default=2048, help="outputs per merge partition")
+    ap.add_argument("--items", type=int, default=0,
+                    help="outputs per merge partition (0: chosen from the mean key length)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-scale", type=float, default=0.125,
                     help="fraction of the workload the CPU oracle is timed on")
@@ -124,7 +125,7 @@ def main():
     print(f"# generated {w.name}: {Ah.n}+{Bh.n} records in {t_gen:.1f}s", file=sys.stderr, flush=True)
     A = em.DeviceSide.from_host(Ah)
     B = em.DeviceSide.from_host(Bh)
-    pl = em.Pipeline(A, B, items_per_part=args.items, path=args.path)
+    pl = em.Pipeline(A, B, items_per_part=args.items or None, path=args.path)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -191,7 +192,7 @@ def main():
         "vs_baseline": None,
         "dtype": "u8",
         "data": "synthetic",
-        "config": {"workload": w.name, "nA": Ah.n, "nB": Bh.n, "items_per_part": args.items,
+        "config": {"workload": w.name, "nA": Ah.n, "nB": Bh.n, "items_per_part": pl.items,
                    "path": args.path, "parallelism": "single-gpu"},
         "survivors": pl.S,
         "payload_bits": pl.T,

@@ -22,6 +22,7 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    "-Wl,--no-undefined",  # a missing kernel stub must fail the build, not the load
     "-Wall",
     "-Wno-unused-function",
     # keep hipcc from forming packed fp32 instructions (none of this code is

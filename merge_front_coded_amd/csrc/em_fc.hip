@@ -80,106 +80,210 @@ __global__ __launch_bounds__(kLenBlock) void k_fc_lengths(em_side_t A, em_side_t
 }
 
 // ---------------------------------------------------------------------------
-// Emitter.  A workgroup owns kEmitRecs consecutive records and every payload
+// Emitter.  A workgroup takes `rpb` consecutive records and owns every payload
 // word whose first bit lies inside them; the last such word may continue into
 // up to kEmitExtra following records (each record is at least 3 bits long:
-// one bit for each EG0 field when its argument is 0, one value bit).
-//
-//  1. Per-record fields are loaded and turned into five bit segments per
-//     record in LDS: the EG0 control field(s) as immediate bits, the key
-//     suffix as a span of source bits, the presence bit and EG0(value length)
-//     as immediate bits, and the value bytes as a span of source bits.
-//  2. The records' source bytes lie in four contiguous arena spans (A keys,
-//     B keys, A values, B values: survivors of one side are increasing).
-//     They are staged into LDS with 16-byte loads when they fit; otherwise
-//     this workgroup reads them from global memory.
-//  3. Each thread assembles a contiguous run of output words, walking the
-//     segments sequentially, into an LDS output window that is then stored
-//     with consecutive lanes on consecutive words.  Every word is written once.
+// one bit for each EG0 field when its argument is 0, one value bit), which the
+// workgroup also encodes.  Steps:
+//  1. one thread per record loads its fields; the records' source bytes lie in
+//     four contiguous arena spans (A keys, B keys, A values, B values, since
+//     the survivors of one side are increasing), which are staged into LDS
+//     with 16-byte loads when they fit (otherwise read from global memory);
+//  2. each thread appends its record's bits -- EG0(c), EG0(k-l), the key
+//     suffix, the presence bit and EG0(value length), the value bytes -- to an
+//     LDS window of output words: words holding only its own bits are plain
+//     stores, the two boundary words it shares with its neighbours are ORed;
+//  3. the owned words are copied from the window to the payload with
+//     consecutive lanes on consecutive words, each word written once.
+// A window that would overflow LDS is processed in slices; each thread then
+// clips its record to the slice.
 
 constexpr int kEmitBlock = 256;
-constexpr uint32_t kEmitRecs = 128;
 constexpr uint32_t kEmitExtra = 16;
-constexpr uint32_t kEmitTable = kEmitRecs + kEmitExtra;
-constexpr uint32_t kSegPerRec = 5;
-constexpr uint32_t kEmitSegs = kEmitTable * kSegPerRec;
-constexpr uint32_t kEmitWindow = 4096;     // output words assembled per round
-constexpr uint32_t kEmitStage = 32 * 1024;  // bytes of staged source spans
+constexpr uint32_t kEmitMaxRecs = kEmitBlock - kEmitExtra;  // owned records per workgroup, at most
+constexpr uint32_t kEmitWindow = 6144;                      // output words per slice
+constexpr uint32_t kEmitStage = 24 * 1024;  // bytes of staged source spans (a multiple of 1 KB)
 
-// segment kinds: 0 immediate, 1 A keys, 2 B keys, 3 A values, 4 B values
 struct EmitShared {
-  uint64_t start[kEmitSegs];  // absolute first bit in the payload
-  uint64_t data[kEmitSegs];   // immediate bits, or first source bit in its arena
-  uint32_t len[kEmitSegs];    // bits
-  uint32_t kind[kEmitSegs];
-  uint32_t kbits[kEmitTable];
   uint32_t out[kEmitWindow];
   uint4 stage[kEmitStage / 16];
-  uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources (lo = ~0 when unused)
+  uint32_t kbits[kEmitBlock];
+  uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
   uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
   uint32_t kprev0;
+  uint64_t bit_lo, bit_hi, bit_ext;
 };
 
-// 64 source bits starting at the dword holding bit `bitpos`, big-endian
-__device__ __forceinline__ uint64_t window64(const uint32_t* w) {
-  return (static_cast<uint64_t>(__builtin_bswap32(w[0])) << 32) | __builtin_bswap32(w[1]);
+// Appends bits MSB-first at consecutive output positions inside the current
+// slice window.  Positions are relative to the slice's first bit.
+struct BitAppender {
+  uint32_t* out;
+  uint32_t w;      // word being filled
+  uint32_t fill;   // bits already in it
+  uint32_t acc;
+  bool shared;     // the word being filled also holds another record's bits
+
+  __device__ __forceinline__ void start(uint32_t* o, uint32_t pos) {
+    out = o;
+    w = pos >> 5;
+    fill = pos & 31u;
+    acc = 0;
+    shared = fill != 0;
+  }
+  __device__ __forceinline__ void store_full() {
+    if (shared)
+      atomicOr(out + w, acc);
+    else
+      out[w] = acc;
+    ++w;
+    acc = 0;
+    shared = false;
+  }
+  // n in 1..32, bits right-aligned
+  __device__ __forceinline__ void put(uint32_t bits, uint32_t n) {
+    const uint32_t space = 32u - fill;
+    if (n < space) {
+      acc |= bits << (space - n);
+      fill += n;
+      return;
+    }
+    const uint32_t rem = n - space;
+    acc |= rem ? bits >> rem : bits;
+    store_full();
+    acc = rem ? bits << (32u - rem) : 0u;
+    fill = rem;
+  }
+  __device__ __forceinline__ void put64(uint64_t v, uint32_t n) {  // n in 0..64
+    if (n > 32) {
+      put(static_cast<uint32_t>(v >> 32) & (0xFFFFFFFFu >> (64u - n)), n - 32);
+      n = 32;
+    }
+    if (n) put(static_cast<uint32_t>(v) & (0xFFFFFFFFu >> (32u - n)), n);
+  }
+  __device__ __forceinline__ void finish() {
+    if (fill) atomicOr(out + w, acc);  // the last word is shared with the next record
+  }
+};
+
+// 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
+__device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
+  const uint32_t* p = base + (bp >> 5);
+  const uint32_t hi = __builtin_bswap32(p[0]), lo = __builtin_bswap32(p[1]);
+  const uint32_t sh = static_cast<uint32_t>(bp & 31u);
+  // v_alignbit takes its shift modulo 32, so offset 0 is the high dword itself
+  return sh ? __builtin_amdgcn_alignbit(hi, lo, 32u - sh) : hi;
+}
+
+// Appends source bits [bp, bp + n) of a dword array.  After the first word
+// the output fill level stays fixed, so each further output word is one new
+// source dword and two funnel shifts.
+__device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, uint64_t bp, uint32_t n) {
+  if (n >= 32 && ap.shared) {  // the shared first word goes through the general path
+    ap.put(bits32_at(base, bp), 32);
+    bp += 32;
+    n -= 32;
+  }
+  if (n >= 32) {
+    const uint32_t* p = base + (bp >> 5);
+    const uint32_t sb = static_cast<uint32_t>(bp & 31u);
+    const uint32_t f = ap.fill;
+    uint32_t cur = __builtin_bswap32(p[0]);
+    uint32_t acc = ap.acc;
+    uint32_t* o = ap.out + ap.w;
+    const uint32_t full = n >> 5;
+    // source dword pair -> the 32 bits starting sb bits into the first one;
+    // v_alignbit takes its shift modulo 32, so sb = 0 selects the first dword
+    const uint32_t rs = 32u - sb;
+    auto src32 = [sb, rs](uint32_t a, uint32_t b) { return sb ? __builtin_amdgcn_alignbit(a, b, rs) : a; };
+    uint32_t t = 0;
+    for (; t + 4 <= full; t += 4) {  // four source dwords in flight per iteration
+      const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
+      const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
+      const uint32_t c0 = src32(cur, n1);
+      const uint32_t c1 = src32(n1, n2);
+      const uint32_t c2 = src32(n2, n3);
+      const uint32_t c3 = src32(n3, n4);
+      o[t] = acc | (c0 >> f);
+      o[t + 1] = __builtin_amdgcn_alignbit(c0, c1, f);
+      o[t + 2] = __builtin_amdgcn_alignbit(c1, c2, f);
+      o[t + 3] = __builtin_amdgcn_alignbit(c2, c3, f);
+      acc = __builtin_amdgcn_alignbit(c3, 0u, f);  // c3 << (32 - f), 0 when f = 0
+      cur = n4;
+    }
+    for (; t < full; ++t) {
+      const uint32_t nxt = __builtin_bswap32(p[t + 1]);
+      const uint32_t chunk = src32(cur, nxt);
+      o[t] = acc | (chunk >> f);
+      acc = __builtin_amdgcn_alignbit(chunk, 0u, f);
+      cur = nxt;
+    }
+    ap.acc = acc;
+    ap.w += full;
+    bp += 32ull * full;
+    n &= 31u;
+  }
+  if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
 }
 
 __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
                                                      const uint32_t* __restrict__ final_refs,
                                                      const uint32_t* __restrict__ lcp_in, uint32_t S,
                                                      const uint64_t* __restrict__ off, uint64_t T,
-                                                     uint32_t* __restrict__ payload) {
+                                                     uint32_t* __restrict__ payload, uint32_t rpb) {
   __shared__ EmitShared sh;
   const uint32_t tid = threadIdx.x;
-  const uint32_t R0 = blockIdx.x * kEmitRecs;
-  const uint32_t nown = (S - R0) < kEmitRecs ? S - R0 : kEmitRecs;
-  const uint32_t cnt = (S - R0) < kEmitTable ? S - R0 : kEmitTable;
+  const uint32_t R0 = blockIdx.x * rpb;
+  const uint32_t nown = (S - R0) < rpb ? S - R0 : rpb;
+  const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
   if (tid < 4) {
     sh.span_lo[tid] = 0xFFFFFFFFu;
     sh.span_hi[tid] = 0;
   }
   __syncthreads();
 
-  // ---- 1. per-record fields (one record per thread) ----
+  // ---- 1. this thread's record ----
   const uint32_t j = tid;
-  uint32_t r_kpos = 0, r_klen = 0, r_l = 0, r_vpos = 0, r_vlen = 0;
-  bool r_isB = false, r_tomb = false;
-  uint64_t r_off = 0;
-  if (j < cnt) {
+  const bool active = j < cnt;
+  uint32_t kpos = 0, klen = 0, l = 0, vpos = 0, vlen = 0;
+  bool isB = false, tomb = false;
+  uint64_t rec_off = 0, rec_end = 0;
+  if (active) {
     const uint32_t r = R0 + j;
+    const uint32_t ref = final_refs[r];
+    rec_off = off[r];
+    rec_end = off[r + 1];
+    const uint32_t lin = lcp_in ? lcp_in[r] : 0u;
     uint32_t idx;
-    const SideView s = pick(A, B, final_refs[r], idx);
+    const SideView s = pick(A, B, ref, idx);
     const KeyRef x = key_of(s, idx);
     if (lcp_in) {
-      r_l = min(lcp_in[r], 8u * x.len);  // a stale array must not send reads past the key
+      l = min(lin, 8u * x.len);  // a stale array must not send reads past the key
     } else if (r > 0) {
       uint32_t pidx;
       const SideView ps = pick(A, B, final_refs[r - 1], pidx);
-      r_l = lcp_bits(ps.keys, key_of(ps, pidx), s.keys, x);
+      l = lcp_bits(ps.keys, key_of(ps, pidx), s.keys, x);
     }
-    uint32_t vlen;
-    bool tomb;
-    value_bits(s, idx, vlen, tomb);
-    r_kpos = x.pos;
-    r_klen = x.len;
-    r_vpos = tomb ? 0u : s.val_off[idx];
-    r_vlen = vlen;
-    r_isB = s.isB;
-    r_tomb = tomb;
-    r_off = off[r];
+    bool t;
+    value_bits(s, idx, vlen, t);
+    tomb = t;
+    kpos = x.pos;
+    klen = x.len;
+    vpos = tomb ? 0u : s.val_off[idx];
+    isB = s.isB;
     sh.kbits[j] = 8u * x.len;
-    // source spans: the key bytes from the first emitted byte, the value bytes
-    const uint32_t kk = r_isB ? 1u : 0u;
-    const uint32_t klo = r_kpos + (r_l >> 3);
-    if (klo < r_kpos + r_klen) {
-      atomicMin(&sh.span_lo[kk], klo);
-      atomicMax(&sh.span_hi[kk], r_kpos + r_klen);
+    const uint32_t q = isB ? 1u : 0u;
+    const uint32_t klo = kpos + (l >> 3);
+    if (klo < kpos + klen) {
+      atomicMin(&sh.span_lo[q], klo);
+      atomicMax(&sh.span_hi[q], kpos + klen);
     }
-    if (r_vlen) {
-      atomicMin(&sh.span_lo[2 + kk], r_vpos);
-      atomicMax(&sh.span_hi[2 + kk], r_vpos + r_vlen);
+    if (vlen) {
+      atomicMin(&sh.span_lo[2 + q], vpos);
+      atomicMax(&sh.span_hi[2 + q], vpos + vlen);
     }
+    if (j == 0) sh.bit_lo = rec_off;
+    if (j == nown - 1) sh.bit_hi = rec_end;
+    if (j == cnt - 1) sh.bit_ext = rec_end;
   }
   if (tid == 0) {
     uint32_t kp = 0;
@@ -191,51 +295,13 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     sh.kprev0 = kp;
   }
   __syncthreads();
-
-  // ---- segment table ----
-  if (j < cnt) {
-    const uint32_t r = R0 + j;
-    const uint32_t k = 8u * r_klen, l = r_l;
-    const uint32_t kprev = j ? sh.kbits[j - 1] : sh.kprev0;
-    const uint32_t c = (r % 15u == 0) ? 1u + l : kprev - l;
-    const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l);
-    uint32_t len0, len1;
-    uint64_t d0, d1;
-    if (e1 + e2 <= 64) {  // EG0(c) EG0(k-l) as one immediate
-      len0 = e1 + e2;
-      d0 = (static_cast<uint64_t>(c + 1u) << e2) | (k - l + 1u);
-      len1 = 0;
-      d1 = 0;
-    } else {
-      len0 = e1;
-      d0 = c + 1u;
-      len1 = e2;
-      d1 = k - l + 1u;
-    }
-    const uint32_t ev = eg0_len(r_vlen);
-    const uint32_t lens[kSegPerRec] = {len0, len1, k - l, r_tomb ? 1u : 1u + ev, 8u * r_vlen};
-    const uint64_t datas[kSegPerRec] = {
-        d0, d1, 8ull * r_kpos + l,
-        r_tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(r_vlen) + 1ull)), 8ull * r_vpos};
-    const uint32_t kinds[kSegPerRec] = {0u, 0u, r_isB ? 2u : 1u, 0u, r_isB ? 4u : 3u};
-    const uint32_t base = j * kSegPerRec;
-    uint64_t at = r_off;
-#pragma unroll
-    for (uint32_t q = 0; q < kSegPerRec; ++q) {
-      sh.start[base + q] = at;
-      sh.len[base + q] = lens[q];
-      sh.data[base + q] = datas[q];
-      sh.kind[base + q] = kinds[q];
-      at += lens[q];
-    }
-  }
   if (tid == 0) {
     uint32_t at = 0;
     for (int q = 0; q < 4; ++q) {
       sh.stage_at[q] = at;
       if (sh.span_lo[q] < sh.span_hi[q]) {
         const uint32_t lo = sh.span_lo[q] & ~15u;
-        // a 64-bit window read at the last byte reaches at most 7 bytes past it
+        // a 32-bit read at the last byte reaches at most 7 bytes past it
         const uint32_t hi = (sh.span_hi[q] + 8u + 15u) & ~15u;
         sh.span_lo[q] = lo;
         sh.span_hi[q] = hi;
@@ -247,94 +313,102 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     }
     sh.stage_at[4] = at;
   }
-  __syncthreads();
-
-  // ---- 2. stage the source spans ----
-  const bool staged = sh.stage_at[4] <= kEmitStage;
-  if (staged) {
-    const uint32_t total16 = sh.stage_at[4] / 16;
-    for (uint32_t c = tid; c < total16; c += kEmitBlock) {
-      const uint32_t byte = c * 16;
-      uint32_t q = 0;
-      while (q < 3 && byte >= sh.stage_at[q + 1]) ++q;
-      const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
-      const uint32_t src = sh.span_lo[q] + (byte - sh.stage_at[q]);
-      sh.stage[c] = *reinterpret_cast<const uint4*>(base + src);
-    }
+  // controls (need the predecessor's key length)
+  uint32_t c = 0;
+  if (active) {
+    const uint32_t r = R0 + j;
+    const uint32_t kprev = j ? sh.kbits[j - 1] : sh.kprev0;
+    c = (r % 15u == 0) ? 1u + l : kprev - l;
   }
   __syncthreads();
 
-  // ---- 3. assemble the owned words ----
-  const uint32_t nseg = cnt * kSegPerRec;
-  const uint32_t nown_seg = nown * kSegPerRec;
-  const uint64_t w_end = (T + 31) >> 5;
-  const uint64_t bit_lo = sh.start[0];
-  const uint64_t bit_hi = nown < cnt ? sh.start[nown_seg] : sh.start[nseg - 1] + sh.len[nseg - 1];
-  const uint64_t w_lo = (bit_lo + 31) >> 5;
-  const uint64_t w_hi = min((bit_hi + 31) >> 5, w_end);
-  const uint32_t* stage32 = reinterpret_cast<const uint32_t*>(sh.stage);
-
-  for (uint64_t win = w_lo; win < w_hi; win += kEmitWindow) {
-    const uint32_t nw = static_cast<uint32_t>(min(static_cast<uint64_t>(kEmitWindow), w_hi - win));
-    const uint32_t per = (nw + kEmitBlock - 1) / kEmitBlock;
-    const uint32_t x0 = tid * per;
-    const uint32_t x1 = min(x0 + per, nw);
-    if (x0 < x1) {
-      uint64_t pos = (win + x0) << 5;
-      // segment holding `pos`: the last one starting at or before it
-      uint32_t lo = 0, hi = nseg - 1;
-      while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (sh.start[mid] <= pos)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      uint32_t si = lo;
-      for (uint32_t x = x0; x < x1; ++x) {
-        uint64_t acc = 0;
-        uint32_t need = 32;
-        while (need) {
-          if (pos >= T) {
-            acc <<= need;
-            break;
-          }
-          while (si + 1 < nseg && pos >= sh.start[si] + sh.len[si]) ++si;
-          const uint64_t st = sh.start[si];
-          const uint32_t ln = sh.len[si];
-          if (pos >= st + ln) {  // cannot happen for offsets produced by em_scan
-            acc <<= need;
-            break;
-          }
-          const uint32_t rel = static_cast<uint32_t>(pos - st);
-          const uint32_t n = min(need, ln - rel);
-          const uint32_t kind = sh.kind[si];
-          const uint64_t d = sh.data[si];
-          uint32_t bits;
-          if (kind == 0) {
-            bits = static_cast<uint32_t>((d >> (ln - rel - n)) & ((1ull << n) - 1));
-          } else {
-            const uint64_t bp = d + rel;  // absolute bit in the arena
-            uint64_t wv;
-            if (staged) {
-              const uint32_t q = kind - 1;
-              const uint64_t lb = bp - 8ull * sh.span_lo[q] + 8ull * sh.stage_at[q];
-              wv = window64(stage32 + (lb >> 5));
-            } else {
-              const uint8_t* base = kind == 1 ? A.keys : kind == 2 ? B.keys : kind == 3 ? A.vals : B.vals;
-              wv = window64(reinterpret_cast<const uint32_t*>(base) + (bp >> 5));
-            }
-            bits = static_cast<uint32_t>((wv << (bp & 31)) >> (64 - n));
-          }
-          acc = (acc << n) | bits;
-          need -= n;
-          pos += n;
-        }
-        sh.out[x] = __builtin_bswap32(static_cast<uint32_t>(acc));
+  // ---- stage the source spans ----
+  const bool staged = sh.stage_at[4] <= kEmitStage;
+  if (staged && sh.stage_at[4] > 0) {
+    // global -> LDS without registers: each wave moves 64 consecutive
+    // 16-byte chunks, lane i's chunk landing 16 i bytes after the wave's base
+    const uint32_t total16 = sh.stage_at[4] / 16;
+    const uint32_t at1 = sh.stage_at[1], at2 = sh.stage_at[2], at3 = sh.stage_at[3];
+    const uint32_t lane = tid & (kWave - 1);
+    for (uint32_t c0 = (tid / kWave) * kWave; c0 < total16; c0 += kEmitBlock) {
+      const uint32_t c = c0 + lane;
+      if (c < total16) {
+        const uint32_t byte = c * 16;
+        const uint32_t q = (byte >= at1) + (byte >= at2) + (byte >= at3);
+        const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
+        lds_dma16(base + sh.span_lo[q] + (byte - sh.stage_at[q]), sh.stage + c0);
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  // source bit positions of this record's key suffix and value bytes
+  const uint32_t* kbase;
+  const uint32_t* vbase;
+  uint64_t kbit, vbit;
+  {
+    const uint32_t qk = isB ? 1u : 0u, qv = 2u + qk;
+    if (staged) {
+      kbase = vbase = reinterpret_cast<const uint32_t*>(sh.stage);
+      // relative to the first emitted key byte, which lies inside the span
+      kbit = 8ull * (kpos + (l >> 3) - sh.span_lo[qk] + sh.stage_at[qk]) + (l & 7u);
+      vbit = 8ull * (vpos - sh.span_lo[qv] + sh.stage_at[qv]);
+    } else {
+      kbase = reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys);
+      vbase = reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals);
+      kbit = 8ull * kpos + l;
+      vbit = 8ull * vpos;
+    }
+  }
+  const uint32_t k = 8u * klen;
+  const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l), ev = eg0_len(vlen);
+  const uint32_t vhl = tomb ? 1u : 1u + ev;
+  const uint64_t vh = tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(vlen) + 1ull));
+  // segment ends relative to the record start
+  const uint32_t b1 = e1, b2 = b1 + e2, b3 = b2 + (k - l), b4 = b3 + vhl, b5 = b4 + 8u * vlen;
+  __syncthreads();
+
+  // ---- 2/3. slices of the output window ----
+  const uint64_t wb = (sh.bit_lo >> 5) << 5;           // first bit of window word 0
+  const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
+  const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
+  const uint64_t ext = sh.bit_ext;
+  for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
+    const uint64_t s1 = min(s0 + 32ull * kEmitWindow, ext);
+    const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
+    for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
     __syncthreads();
-    for (uint32_t x = tid; x < nw; x += kEmitBlock) payload[win + x] = sh.out[x];
+    if (active && rec_off < s1 && rec_end > s0 && b5 == rec_end - rec_off) {
+      // this record's bits inside [s0, s1), relative to the record start
+      const uint32_t from = rec_off >= s0 ? 0u : static_cast<uint32_t>(s0 - rec_off);
+      const uint32_t to = rec_end <= s1 ? b5 : static_cast<uint32_t>(s1 - rec_off);
+      BitAppender ap;
+      ap.start(sh.out, static_cast<uint32_t>(rec_off + from - s0));
+      // EG0(c), EG0(k-l), presence + EG0(value length): immediates
+      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
+        const uint32_t lo = max(a, from), hi = min(b, to);
+        if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
+      };
+      auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
+        const uint32_t lo = max(a, from), hi = min(b, to);
+        if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
+      };
+      imm(static_cast<uint64_t>(c) + 1u, 0, b1);
+      imm(static_cast<uint64_t>(k - l) + 1u, b1, b2);
+      span(kbase, kbit, b2, b3);
+      imm(vh, b3, b4);
+      span(vbase, vbit, b4, b5);
+      ap.finish();
+    }
+    __syncthreads();
+    // owned words of this slice: 16-byte stores between a scalar head and tail
+    const uint64_t o_lo = max(w_lo, s0 >> 5), o_hi = min(w_hi, (s1 + 31) >> 5);
+    const uint64_t wbase = s0 >> 5;  // global word number of window word 0
+    auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
+    const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
+    for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
+    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock)
+      *reinterpret_cast<uint4*>(payload + w) = uint4{win(w), win(w + 1), win(w + 2), win(w + 3)};
+    for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
     __syncthreads();
   }
 }
@@ -372,8 +446,15 @@ extern "C" int em_emit(const em_side_t* A, const em_side_t* B, const uint32_t* f
   if (S == 0) return EM_OK;
   if (!final_refs || !off || !payload) return EM_EINVAL;
   if (payload_words < (T + 31) / 32) return EM_ENOSPC;
-  const uint32_t blocks = (S + kEmitRecs - 1) / kEmitRecs;
+  // records per workgroup: keep the expected output window and staged
+  // source bytes of one workgroup at about half of their LDS capacity
+  const double mean_bits = static_cast<double>(T) / S;
+  double r1 = 0.5 * kEmitWindow * 32.0 / mean_bits;
+  double r2 = 0.5 * kEmitStage * 8.0 / mean_bits;
+  double r = r1 < r2 ? r1 : r2;
+  uint32_t rpb = r >= kEmitMaxRecs ? kEmitMaxRecs : (r < 16.0 ? 16u : static_cast<uint32_t>(r));
+  const uint32_t blocks = (S + rpb - 1) / rpb;
   hipLaunchKernelGGL(k_emit, dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream), *A, *B,
-                     final_refs, lcp_bits, S, off, T, payload);
+                     final_refs, lcp_bits, S, off, T, payload, rpb);
   return check_launch();
 }

@@ -72,6 +72,14 @@ __device__ __forceinline__ uint32_t eg0_len(uint64_t x) {
   return 2u * (63u - static_cast<uint32_t>(__builtin_clzll(x + 1))) + 1u;
 }
 
+// gfx950 global -> LDS load without registers: each active lane moves 16
+// bytes from `src` (per lane) to `lds_wave_base` + 16 * lane, where
+// `lds_wave_base` is the same for the whole wave.  The caller waits for the
+// loads (s_waitcnt vmcnt) and synchronises before reading the LDS.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src), lds_wave_base, 16, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Wave64 / block primitives.
 

@@ -28,24 +28,104 @@ namespace em {
 constexpr int kMergeBlock = 256;
 constexpr uint32_t kDrop = 0x80000000u;  // refs are < 2^24, bit 31 marks a dropped A
 
+// LDS for a partition's key bytes; the compaction arrays reuse it after the merge.
+// (a multiple of 1 KB: LDS-DMA fills it 64 chunks of 16 bytes at a time)
+template <int IPT>
+constexpr uint32_t merge_key_cap() {
+  return IPT <= 1 ? 13u * 1024 : IPT == 2 ? 26u * 1024 : IPT == 4 ? 44u * 1024 : 60u * 1024;
+}
+
 template <int IPT>
 struct MergeShared {
   static constexpr int kTile = kMergeBlock * IPT;
+  static constexpr uint32_t kKeyCap = merge_key_cap<IPT>();
+  static_assert(kKeyCap >= 8u * kTile, "compaction arrays reuse the key buffer");
   uint32_t a_off[kTile + 2];
   uint32_t b_off[kTile + 2];
-  uint32_t out[kTile];
-  uint32_t ords[kTile];
+  // prefix cache: each key's first 8 bytes, big-endian, zero padded
+  uint64_t a_pfx[kTile + 2];
+  uint64_t b_pfx[kTile + 2];
+  union {
+    uint4 keys[kKeyCap / 16];
+    struct {
+      uint32_t out[kTile];
+      uint32_t ords[kTile];
+    } c;
+  } u;
   uint32_t scan[kMergeBlock / kWave + 1];
-  uint32_t tile;
-  uint32_t base;
+  uint32_t tile, base;
 };
+
+// Merges this thread's slice of the partition.  Keys are read through
+// (base, position - lo + at) per side: the LDS copy when staged, the arenas
+// otherwise.  Returns the kept count; refs[] get the merged references with
+// kDrop on a replaced A.
+template <int IPT>
+__device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
+                                                const uint64_t* a_pfx, const uint64_t* b_pfx,
+                                                const uint8_t* abase, uint32_t a_adj,
+                                                const uint8_t* bbase, uint32_t b_adj, uint32_t k,
+                                                uint32_t len, uint32_t nA_t, uint32_t nB_t,
+                                                bool has_next_b, uint32_t i0, uint32_t nA_all,
+                                                uint32_t j0, uint32_t (&refs)[IPT]) {
+  // Prefix first; zero padding plus the lengths keep proper-prefix order exact
+  // (Everett, "GPU construction experiment", prefix-cache paragraph).
+  auto cmpAB = [&](uint32_t a, uint32_t b) -> int {
+    const uint64_t pa = a_pfx[a], pb = b_pfx[b];
+    if (pa != pb) return pa < pb ? -1 : 1;
+    const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
+    if (la <= 8 || lb <= 8) return (la > lb) - (la < lb);
+    return cmp_keys(abase, KeyRef{a_off[a] - a_adj + 8, la - 8}, bbase, KeyRef{b_off[b] - b_adj + 8, lb - 8});
+  };
+  uint32_t kept = 0;
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
+  if (k >= len) return 0;
+  uint32_t lo = k > nB_t ? k - nB_t : 0;
+  uint32_t hi = k < nA_t ? k : nA_t;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    const uint32_t j = k - mid;
+    const bool too_big = j < nB_t && cmpAB(mid - 1, j) > 0;
+    if (too_big)
+      hi = mid - 1;
+    else
+      lo = mid;
+  }
+  uint32_t a = lo, b = k - lo;
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) {
+    if (k + s < len) {
+      int c;
+      if (a < nA_t && b < nB_t) {
+        c = cmpAB(a, b);
+      } else if (a < nA_t) {
+        // B exhausted inside the partition: only the partition's last A can
+        // equal the next partition's first B.
+        c = (a == nA_t - 1 && has_next_b && cmpAB(a, nB_t) == 0) ? 0 : -1;
+      } else {
+        c = 1;
+      }
+      if (c <= 0) {
+        refs[s] = (i0 + a) | (c == 0 ? kDrop : 0u);
+        ++a;
+      } else {
+        refs[s] = nA_all + j0 + b;
+        ++b;
+      }
+      kept += c != 0;
+    }
+  }
+  return kept;
+}
 
 template <int IPT>
 __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
     em_side_t A, em_side_t B, const uint32_t* __restrict__ splits, uint32_t items, uint32_t P,
     uint32_t* __restrict__ final_refs, uint32_t* __restrict__ ord_A, uint32_t* __restrict__ ord_B,
     uint32_t* __restrict__ d_S, uint32_t* __restrict__ ticket, uint64_t* __restrict__ desc) {
-  __shared__ MergeShared<IPT> sh;
+  using Sh = MergeShared<IPT>;
+  __shared__ Sh sh;
   const uint32_t tid = threadIdx.x;
   if (tid == 0) sh.tile = atomicAdd(ticket, 1u);
   __syncthreads();
@@ -68,61 +148,79 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   const bool has_next_b = valid && j1 < B.n;
   const uint32_t nb_off = nB_t + (has_next_b ? 2u : 1u);
 
-  for (uint32_t x = tid; x <= nA_t; x += kMergeBlock) sh.a_off[x] = A.key_off[i0 + x];
-  for (uint32_t x = tid; x < nb_off; x += kMergeBlock) sh.b_off[x] = B.key_off[j0 + x];
+  {
+    // all offset loads first, then the LDS stores, so the loads overlap in flight
+    constexpr int kPer = IPT + 1;  // ceil((kTile + 2) / kMergeBlock)
+    uint32_t va[kPer], vb[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t x = tid + u * kMergeBlock;
+      va[u] = x <= nA_t ? A.key_off[i0 + x] : 0u;
+      vb[u] = x < nb_off ? B.key_off[j0 + x] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t x = tid + u * kMergeBlock;
+      if (x <= nA_t) sh.a_off[x] = va[u];
+      if (x < nb_off) sh.b_off[x] = vb[u];
+    }
+  }
   __syncthreads();
 
-  auto keyA = [&](uint32_t a) { return KeyRef{sh.a_off[a], sh.a_off[a + 1] - sh.a_off[a]}; };
-  auto keyB = [&](uint32_t b) { return KeyRef{sh.b_off[b], sh.b_off[b + 1] - sh.b_off[b]}; };
+  // ---- stage the partition's key bytes (A span, then B span) in LDS ----
+  // A compare reads 8-byte chunks through aligned dwords, up to 11 bytes past
+  // a key's last byte, so each span is staged with a 16-byte margin.
+  const uint32_t a_lo = sh.a_off[0] & ~15u;
+  const uint32_t a_bytes = len ? ((sh.a_off[nA_t] + 16u + 15u) & ~15u) - a_lo : 0u;
+  const uint32_t b_lo = sh.b_off[0] & ~15u;
+  const uint32_t b_bytes = len ? ((sh.b_off[nb_off - 1] + 16u + 15u) & ~15u) - b_lo : 0u;
+  const bool staged = a_bytes + b_bytes <= Sh::kKeyCap;
+  if (staged) {
+    // global -> LDS without registers: each wave moves 64 consecutive 16-byte
+    // chunks, lane i's chunk landing 16 i bytes after the wave's base
+    const uint32_t na16 = a_bytes / 16, total16 = (a_bytes + b_bytes) / 16;
+    const uint32_t lane = tid & (kWave - 1);
+    for (uint32_t c0 = (tid / kWave) * kWave; c0 < total16; c0 += kMergeBlock) {
+      const uint32_t c = c0 + lane;
+      if (c < total16) {
+        const uint8_t* src = c < na16 ? A.keys + a_lo + 16u * c : B.keys + b_lo + 16u * (c - na16);
+        lds_dma16(src, sh.u.keys + c0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  const uint32_t a_adj = staged ? a_lo : 0u, b_adj = staged ? b_lo - a_bytes : 0u;
+  {
+    const uint32_t nb_keys = nb_off - 1;
+    for (uint32_t x = tid; x < nA_t; x += kMergeBlock) {
+      const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
+      sh.a_pfx[x] = (staged ? load_be8(reinterpret_cast<const uint8_t*>(sh.u.keys), p0 - a_adj)
+                            : load_be8(A.keys, p0)) & be_mask(ln < 8 ? ln : 8);
+    }
+    for (uint32_t y = tid; y < nb_keys; y += kMergeBlock) {
+      const uint32_t p0 = sh.b_off[y], ln = sh.b_off[y + 1] - p0;
+      sh.b_pfx[y] = (staged ? load_be8(reinterpret_cast<const uint8_t*>(sh.u.keys), p0 - b_adj)
+                            : load_be8(B.keys, p0)) & be_mask(ln < 8 ? ln : 8);
+    }
+  }
+  __syncthreads();
 
   // ---- merge this thread's slice ----
   uint32_t refs[IPT];
-  uint32_t kept = 0;
   const uint32_t k = tid * IPT;
-  if (k < len) {
-    uint32_t lo = k > nB_t ? k - nB_t : 0;
-    uint32_t hi = k < nA_t ? k : nA_t;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi + 1) >> 1;
-      const uint32_t j = k - mid;
-      const bool too_big = j < nB_t && cmp_keys(A.keys, keyA(mid - 1), B.keys, keyB(j)) > 0;
-      if (too_big)
-        hi = mid - 1;
-      else
-        lo = mid;
-    }
-    uint32_t a = lo, b = k - lo;
-#pragma unroll
-    for (int s = 0; s < IPT; ++s) {
-      refs[s] = kDrop;  // placeholder for "no item"
-      if (k + s < len) {
-        int c;
-        if (a < nA_t && b < nB_t) {
-          c = cmp_keys(A.keys, keyA(a), B.keys, keyB(b));
-        } else if (a < nA_t) {
-          // B exhausted inside the partition: only the partition's last A can
-          // equal the next partition's first B.
-          c = (a == nA_t - 1 && has_next_b && cmp_keys(A.keys, keyA(a), B.keys, keyB(nB_t)) == 0) ? 0
-                                                                                                   : -1;
-        } else {
-          c = 1;
-        }
-        if (c <= 0) {
-          refs[s] = (i0 + a) | (c == 0 ? kDrop : 0u);
-          ++a;
-        } else {
-          refs[s] = A.n + j0 + b;
-          ++b;
-        }
-        kept += c != 0;
-      }
-    }
+  uint32_t kept;
+  if (staged) {
+    const uint8_t* st = reinterpret_cast<const uint8_t*>(sh.u.keys);
+    kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.a_pfx, sh.b_pfx, st, a_adj, st, b_adj, k, len, nA_t,
+                            nB_t, has_next_b, i0, A.n, j0, refs);
   } else {
-#pragma unroll
-    for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
+    kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.a_pfx, sh.b_pfx, A.keys, 0u, B.keys, 0u, k, len,
+                            nA_t, nB_t, has_next_b, i0, A.n, j0, refs);
   }
+  __syncthreads();  // the key buffer becomes the compaction arrays
 
-  // ---- keep scan inside the partition ----
+  // ---- keep scan inside the partition (the key buffer is free from here) ----
   uint32_t total;
   uint32_t ord = block_exclusive_scan<uint32_t, kMergeBlock>(kept, sh.scan, total);
 #pragma unroll
@@ -132,11 +230,11 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
     const uint32_t ref = r & ~kDrop;
     const bool drop = (r & kDrop) != 0;
     if (ref < A.n) {
-      sh.ords[ref - i0] = drop ? EM_NONE : ord;
+      sh.u.c.ords[ref - i0] = drop ? EM_NONE : ord;
     } else {
-      sh.ords[nA_t + (ref - A.n - j0)] = ord;
+      sh.u.c.ords[nA_t + (ref - A.n - j0)] = ord;
     }
-    if (!drop) sh.out[ord++] = ref;
+    if (!drop) sh.u.c.out[ord++] = ref;
   }
 
   // ---- survivor base of this partition (decoupled look-back) ----
@@ -150,14 +248,14 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   __syncthreads();
   const uint32_t base = sh.base;
 
-  for (uint32_t x = tid; x < total; x += kMergeBlock) final_refs[base + x] = sh.out[x];
+  for (uint32_t x = tid; x < total; x += kMergeBlock) final_refs[base + x] = sh.u.c.out[x];
   if (ord_A)
     for (uint32_t x = tid; x < nA_t; x += kMergeBlock) {
-      const uint32_t o = sh.ords[x];
+      const uint32_t o = sh.u.c.ords[x];
       ord_A[i0 + x] = o == EM_NONE ? EM_NONE : base + o;
     }
   if (ord_B)
-    for (uint32_t y = tid; y < nB_t; y += kMergeBlock) ord_B[j0 + y] = base + sh.ords[nA_t + y];
+    for (uint32_t y = tid; y < nB_t; y += kMergeBlock) ord_B[j0 + y] = base + sh.u.c.ords[nA_t + y];
 }
 
 __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }

@@ -12,14 +12,30 @@ import torch
 from . import binding as em
 
 
+# LDS bytes for a partition's keys in the merge kernel, by outputs per thread
+_KEY_CAP = {1: 13 * 1024, 2: 26 * 1024, 4: 44 * 1024, 8: 60 * 1024, 16: 60 * 1024}
+
+
+def choose_items_per_part(A: em.DeviceSide, B: em.DeviceSide) -> int:
+    """Largest partition (256..4096 outputs) whose keys are expected to fit the
+    merge kernel's LDS key buffer, so the partition's comparisons read LDS."""
+    n = A.n + B.n
+    mean = (A.key_bytes + B.key_bytes) / n if n else 0.0
+    best = 256
+    for items in (256, 512, 1024, 2048, 4096):
+        if items * (mean * 1.1 + 4) <= _KEY_CAP[items // 256]:
+            best = items
+    return best
+
+
 class Pipeline:
-    def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int = 2048,
+    def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int | None = None,
                  path: str = "merge", keep_ordinals: bool = True, keep_lcp: bool = True,
                  device="cuda"):
         if path not in ("merge", "collision"):
             raise ValueError("path is 'merge' or 'collision'")
         self.A, self.B = A, B
-        self.items = int(items_per_part)
+        self.items = int(items_per_part) if items_per_part else choose_items_per_part(A, B)
         self.path = path
         N = A.n + B.n
         self.N = N

@@ -21,7 +21,7 @@ import gen  # noqa: E402
 import oracle  # noqa: E402
 
 OUT = os.path.join(HERE, "full_size_digests.json")
-ITEMS = 2048  # partition size of the benchmark's launch configuration
+ITEM_SIZES = (256, 512, 1024, 2048, 4096)  # every partition size the library accepts in tiles
 
 
 def sha(*arrays) -> str:
@@ -47,11 +47,11 @@ def main(ids):
         refs = oracle.merge(A, B)
         final, ord_A, ord_B, S = oracle.keep(A, B, refs)
         len_bits, lcp_bits, off, T, payload = oracle.encode(A, B, final)
-        splits = oracle.splits(refs, A.n, ITEMS)
         data[str(wid)] = {
-            "workload": gen.WORKLOADS[wid].name, "nA": A.n, "nB": B.n, "items_per_part": ITEMS,
+            "workload": gen.WORKLOADS[wid].name, "nA": A.n, "nB": B.n,
             "input": input_digest(A, B), "S": S, "T": T,
-            "splits": sha(splits), "final": sha(final), "ord_A": sha(ord_A), "ord_B": sha(ord_B),
+            "splits": {str(i): sha(oracle.splits(refs, A.n, i)) for i in ITEM_SIZES},
+            "final": sha(final), "ord_A": sha(ord_A), "ord_B": sha(ord_B),
             "len_bits": sha(len_bits), "lcp_bits": sha(lcp_bits), "off": sha(off),
             "payload": sha(payload), "payload_bytes": int(payload.size),
         }
