@@ -2,11 +2,15 @@
 """Throughput of the whole merge -> keep -> lengths -> scan -> emit path on one
 MI355X, on the 8M+8M base64-key workload (or another named workload).
 
-One step is one pass of the hot path over inputs already resident in HBM:
-em_partition, em_merge_keep (or em_collision_rank), the host read of S,
-em_fc_lengths, em_scan, the host read of T, em_emit.  W untimed warm-up steps,
-then exactly K timed steps between two device synchronisations.  Prints one
-JSON line.
+One step is one pass of the whole hot path over inputs already resident in
+HBM.  Paths:
+  fused (default)  em_partition (coarse) + em_merge_fc: co-rank, merge,
+                   keep-newer, lengths, bit offsets and emission in one kernel
+  merge            em_partition, em_merge_keep, host read of S, em_fc_lengths,
+                   em_scan, host read of T, em_emit
+  collision        em_collision_rank in place of partition + merge_keep
+W untimed warm-up steps, then exactly K timed steps between two device
+synchronisations.  Prints one JSON line.
 
   value      merged records/s = (|A| + |B|) * K / elapsed
   GB/s       B_io / step time, B_io = both sides' key and value arenas, u32
@@ -36,9 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
-    ap.add_argument("--path", choices=("merge", "collision"), default="merge")
+    ap.add_argument("--path", choices=("fused", "merge", "collision"), default="merge")
     ap.add_argument("--items", type=int, default=0,
                     help="outputs per merge partition (0: chosen from the mean key length)")
+    ap.add_argument("--coarse-parts", type=int, default=0,
+                    help="fused path: partitions per coarse partition (0: library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-scale", type=float, default=0.125,
                     help="fraction of the workload the CPU oracle is timed on")
@@ -57,8 +63,8 @@ def algorithmic_bytes(Ah, Bh, pl, path):
     S, T, N = pl.S, pl.T, Ah.n + Bh.n
     keys = int(Ah.keys.size + Bh.keys.size)
     offs = 4 * (Ah.n + 1 + Bh.n + 1)
-    final = pl.host("final", S)
-    lcp = pl.host("lcp", S)
+    final = pl.final_host if pl.path == "fused" else pl.host("final", S)
+    lcp = pl.lcp_host if pl.path == "fused" else pl.host("lcp", S)
     nA = Ah.n
     isA = final < nA
     ia = final[isA].astype(np.int64)
@@ -83,6 +89,8 @@ def algorithmic_bytes(Ah, Bh, pl, path):
         "em_emit": S * per_rec_meta + suffix_bytes + value_bytes + payload,
         "em_partition": 0,
         "em_collision_rank": keys + offs + 4 * S + 4 * N,
+        # the whole path: every input byte once, the payload once
+        "em_merge_fc": side_bytes(Ah) + side_bytes(Bh) + payload,
     }
     return out
 
@@ -125,7 +133,9 @@ def main():
     print(f"# generated {w.name}: {Ah.n}+{Bh.n} records in {t_gen:.1f}s", file=sys.stderr, flush=True)
     A = em.DeviceSide.from_host(Ah)
     B = em.DeviceSide.from_host(Bh)
-    pl = em.Pipeline(A, B, items_per_part=args.items or None, path=args.path)
+    fused = args.path == "fused"
+    extra = {"coarse_parts": args.coarse_parts} if (fused and args.coarse_parts) else {}
+    pl = em.Pipeline(A, B, items_per_part=args.items or None, path=args.path, keep_all=not fused, **extra)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -136,8 +146,9 @@ def main():
     # per-call HIP events on the launch stream (torch's current stream, which
     # the binding passes to the library)
     stream = torch.cuda.current_stream()
-    calls = ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"] \
-        if args.path == "merge" else ["em_collision_rank", "em_fc_lengths", "em_scan", "em_emit"]
+    calls = {"merge": ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"],
+             "collision": ["em_collision_rank", "em_fc_lengths", "em_scan", "em_emit"],
+             "fused": ["em_partition", "em_merge_fc"]}[args.path]
     ev = {c: [] for c in calls}
     orig = {c: getattr(em.pipeline.em, c) for c in calls}
 
@@ -161,13 +172,22 @@ def main():
     try:
         start.record(stream)
         for _ in range(args.steps):
-            pl.run()
+            pl.run(read_counts=not fused)  # the fused path needs no host read inside a step
         end.record(stream)
         torch.cuda.synchronize()
     finally:
         for c in calls:
             setattr(em.pipeline.em, c, orig[c])
     wall = time.perf_counter() - t0
+    if fused:
+        pl.read_counts()
+        # the per-record arrays, for the algorithmic-byte count only (not timed)
+        pl2 = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
+        pl2.run()
+        torch.cuda.synchronize()
+        assert (pl2.S, pl2.T) == (pl.S, pl.T)
+        pl.final_host, pl.lcp_host = pl2.host("final", pl.S), pl2.host("lcp", pl.S)
+        del pl2
     dev_ms = start.elapsed_time(end)
     ms_per_step = dev_ms / args.steps
     per_call_ms = {c: sum(s.elapsed_time(e) for s, e in ev[c]) / len(ev[c]) for c in calls}
@@ -193,7 +213,8 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": w.name, "nA": Ah.n, "nB": Bh.n, "items_per_part": pl.items,
-                   "path": args.path, "parallelism": "single-gpu"},
+                   "path": args.path, "parallelism": "single-gpu",
+                   **({"coarse_items": pl.coarse} if fused else {})},
         "survivors": pl.S,
         "payload_bits": pl.T,
         "B_io_bytes": b_io,

@@ -103,7 +103,8 @@ int em_payload_bound_bits(const em_side_t *A, const em_side_t *B, uint64_t *boun
  * P = ceil(N / items_per_part), N = |A| + |B|, writes splits[p] = the co-rank
  * of diagonal d_p = min(p * items_per_part, N): the number of A records among
  * the first d_p outputs of the stable merge in which equal keys put A first.
- * splits: P+1 u32.  1 <= items_per_part <= EM_MAX_ITEMS_PER_PART.
+ * splits: P+1 u32.  items_per_part >= 1 (em_merge_keep needs at most
+ * EM_MAX_ITEMS_PER_PART; em_merge_fc takes coarser splits).
  */
 int em_partition(const em_side_t *A, const em_side_t *B, uint32_t items_per_part, uint32_t *splits,
                  void *ws, size_t ws_bytes, void *stream);
@@ -176,6 +177,30 @@ int em_scan(const uint32_t *len_bits, uint32_t S, uint64_t *off, void *ws, size_
 int em_emit(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs,
             const uint32_t *lcp_bits, uint32_t S, const uint64_t *off, uint64_t T, uint32_t *payload,
             uint64_t payload_words, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole path in one pass (Everett, "GPU construction experiment": merge
+ * by diagonal partitions, keep-newer, exact lengths, one global scan of bit
+ * offsets, word-owned MSB-first emission).  One workgroup per partition of
+ * items_per_part (1..256) merged outputs finds its co-ranks inside the coarse
+ * partition given by coarse_splits (em_partition's output for
+ * coarse_items, a multiple of items_per_part), merges, keeps the newer
+ * record, computes LCPs and exact lengths, takes its survivor and bit bases
+ * from two decoupled look-backs, and stores its payload words once (a word
+ * belongs to the partition holding its last bit).  Writes:
+ *   payload[ceil(T/32)]  same bits as em_emit; payload_words is the capacity
+ *                        and must cover em_payload_bound_bits;
+ *   d_S[0] (u32), d_T[0] (u64)  survivor count and payload bits (device);
+ *   final_refs, ord_A, ord_B, len_bits, lcp_bits, off: optional (nullable),
+ *                        the same arrays the separate calls produce.
+ * Nothing has to be read by the host between steps.
+ */
+size_t em_merge_fc_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t items_per_part);
+int em_merge_fc(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_splits,
+                uint32_t coarse_items, uint32_t items_per_part, uint32_t *payload,
+                uint64_t payload_words, uint32_t *d_S, uint64_t *d_T, uint32_t *final_refs,
+                uint32_t *ord_A, uint32_t *ord_B, uint32_t *len_bits, uint32_t *lcp_bits,
+                uint64_t *off, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Rank512 probe (Everett, "Collision bitmap and rank experiment",

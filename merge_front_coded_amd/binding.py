@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH):
         "em_scan": (i32, [P, u32, P, P, sz, P]),
         "em_emit": (i32, [S, S, P, P, u32, P, u64, P, u64, P, sz, P]),
         "em_rank512_probe": (i32, [P, u32, P, u32, P, P, sz, P]),
+        "em_merge_fc_workspace_bytes": (sz, [u32, u32, u32]),
+        "em_merge_fc": (i32, [S, S, P, u32, u32, P, u64, P, P, P, P, P, P, P, P, P, sz, P]),
         "em_rank512_workspace_bytes": (sz, [u32]),
         "em_strerror": (ctypes.c_char_p, [i32]),
         "em_last_hip_error": (i32, []),
@@ -189,3 +191,17 @@ def em_emit(A, B, final_refs, lcp_bits, S, off, T, payload, ws, stream=None):
 def em_rank512_probe(bitmap, nbits, positions, out, ws, stream=None):
     _check(lib().em_rank512_probe(_p(bitmap), nbits, _p(positions), positions.numel(), _p(out), _p(ws),
                                   ws.numel(), _stream(stream)), "em_rank512_probe")
+
+
+def em_merge_fc_workspace_bytes(nA: int, nB: int, items_per_part: int) -> int:
+    return int(lib().em_merge_fc_workspace_bytes(nA, nB, items_per_part))
+
+
+def em_merge_fc(A, B, coarse_splits, coarse_items, items_per_part, payload, d_S, d_T, ws,
+                final_refs=None, ord_A=None, ord_B=None, len_bits=None, lcp_bits=None, off=None,
+                stream=None):
+    _check(lib().em_merge_fc(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(coarse_splits),
+                             coarse_items, items_per_part, _p(payload), payload.numel(), _p(d_S),
+                             _p(d_T), _p(final_refs), _p(ord_A), _p(ord_B), _p(len_bits),
+                             _p(lcp_bits), _p(off), _p(ws), ws.numel(), _stream(stream)),
+           "em_merge_fc")

@@ -12,46 +12,11 @@
 //    and writes it once; unused final bits are zero; the key suffix is copied
 //    from the selected record's own key (every distinct key survives, so the
 //    merged predecessor shares at least the source predecessor's prefix).
-#include "em_internal.h"
+#include "em_tile.h"
 
 namespace em {
 
 constexpr int kLenBlock = 256;
-
-// The fields of the side a reference names, chosen by value selects (taking
-// the address of a by-value kernel argument would force a private copy).
-struct SideView {
-  const uint8_t* keys;
-  const uint32_t* key_off;
-  const uint8_t* vals;
-  const uint32_t* val_off;
-  const uint8_t* tomb;
-  bool isB;
-};
-
-__device__ __forceinline__ SideView pick(const em_side_t& A, const em_side_t& B, uint32_t ref,
-                                         uint32_t& idx) {
-  // A reference outside [0, |A|+|B|) can only come from contract-violating
-  // inputs; it is clamped so that no access leaves the arrays.
-  const uint32_t N = A.n + B.n;
-  if (ref >= N) ref = N - 1;
-  const bool b = ref >= A.n;
-  idx = b ? ref - A.n : ref;
-  return SideView{b ? B.keys : A.keys, b ? B.key_off : A.key_off, b ? B.vals : A.vals,
-                  b ? B.val_off : A.val_off, b ? B.tomb : A.tomb, b};
-}
-
-__device__ __forceinline__ KeyRef key_of(const SideView& s, uint32_t r) {
-  const uint32_t p = s.key_off[r];
-  return KeyRef{p, s.key_off[r + 1] - p};
-}
-
-__device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, uint32_t& vlen,
-                                               bool& tomb) {
-  tomb = s.tomb != nullptr && s.tomb[idx] != 0;
-  vlen = tomb ? 0u : s.val_off[idx + 1] - s.val_off[idx];
-  return tomb ? 1u : 1u + eg0_len(vlen) + 8u * vlen;
-}
 
 __global__ __launch_bounds__(kLenBlock) void k_fc_lengths(em_side_t A, em_side_t B,
                                                           const uint32_t* __restrict__ final_refs,
@@ -101,8 +66,14 @@ __global__ __launch_bounds__(kLenBlock) void k_fc_lengths(em_side_t A, em_side_t
 constexpr int kEmitBlock = 256;
 constexpr uint32_t kEmitExtra = 16;
 constexpr uint32_t kEmitMaxRecs = kEmitBlock - kEmitExtra;  // owned records per workgroup, at most
-constexpr uint32_t kEmitWindow = 6144;                      // output words per slice
-constexpr uint32_t kEmitStage = 24 * 1024;  // bytes of staged source spans (a multiple of 1 KB)
+#ifndef EW
+#define EW 6144
+#endif
+constexpr uint32_t kEmitWindow = EW;
+#ifndef ES
+#define ES 24
+#endif
+constexpr uint32_t kEmitStage = ES * 1024;
 
 struct EmitShared {
   uint32_t out[kEmitWindow];
@@ -113,117 +84,6 @@ struct EmitShared {
   uint32_t kprev0;
   uint64_t bit_lo, bit_hi, bit_ext;
 };
-
-// Appends bits MSB-first at consecutive output positions inside the current
-// slice window.  Positions are relative to the slice's first bit.
-struct BitAppender {
-  uint32_t* out;
-  uint32_t w;      // word being filled
-  uint32_t fill;   // bits already in it
-  uint32_t acc;
-  bool shared;     // the word being filled also holds another record's bits
-
-  __device__ __forceinline__ void start(uint32_t* o, uint32_t pos) {
-    out = o;
-    w = pos >> 5;
-    fill = pos & 31u;
-    acc = 0;
-    shared = fill != 0;
-  }
-  __device__ __forceinline__ void store_full() {
-    if (shared)
-      atomicOr(out + w, acc);
-    else
-      out[w] = acc;
-    ++w;
-    acc = 0;
-    shared = false;
-  }
-  // n in 1..32, bits right-aligned
-  __device__ __forceinline__ void put(uint32_t bits, uint32_t n) {
-    const uint32_t space = 32u - fill;
-    if (n < space) {
-      acc |= bits << (space - n);
-      fill += n;
-      return;
-    }
-    const uint32_t rem = n - space;
-    acc |= rem ? bits >> rem : bits;
-    store_full();
-    acc = rem ? bits << (32u - rem) : 0u;
-    fill = rem;
-  }
-  __device__ __forceinline__ void put64(uint64_t v, uint32_t n) {  // n in 0..64
-    if (n > 32) {
-      put(static_cast<uint32_t>(v >> 32) & (0xFFFFFFFFu >> (64u - n)), n - 32);
-      n = 32;
-    }
-    if (n) put(static_cast<uint32_t>(v) & (0xFFFFFFFFu >> (32u - n)), n);
-  }
-  __device__ __forceinline__ void finish() {
-    if (fill) atomicOr(out + w, acc);  // the last word is shared with the next record
-  }
-};
-
-// 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
-__device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
-  const uint32_t* p = base + (bp >> 5);
-  const uint32_t hi = __builtin_bswap32(p[0]), lo = __builtin_bswap32(p[1]);
-  const uint32_t sh = static_cast<uint32_t>(bp & 31u);
-  // v_alignbit takes its shift modulo 32, so offset 0 is the high dword itself
-  return sh ? __builtin_amdgcn_alignbit(hi, lo, 32u - sh) : hi;
-}
-
-// Appends source bits [bp, bp + n) of a dword array.  After the first word
-// the output fill level stays fixed, so each further output word is one new
-// source dword and two funnel shifts.
-__device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, uint64_t bp, uint32_t n) {
-  if (n >= 32 && ap.shared) {  // the shared first word goes through the general path
-    ap.put(bits32_at(base, bp), 32);
-    bp += 32;
-    n -= 32;
-  }
-  if (n >= 32) {
-    const uint32_t* p = base + (bp >> 5);
-    const uint32_t sb = static_cast<uint32_t>(bp & 31u);
-    const uint32_t f = ap.fill;
-    uint32_t cur = __builtin_bswap32(p[0]);
-    uint32_t acc = ap.acc;
-    uint32_t* o = ap.out + ap.w;
-    const uint32_t full = n >> 5;
-    // source dword pair -> the 32 bits starting sb bits into the first one;
-    // v_alignbit takes its shift modulo 32, so sb = 0 selects the first dword
-    const uint32_t rs = 32u - sb;
-    auto src32 = [sb, rs](uint32_t a, uint32_t b) { return sb ? __builtin_amdgcn_alignbit(a, b, rs) : a; };
-    uint32_t t = 0;
-    for (; t + 4 <= full; t += 4) {  // four source dwords in flight per iteration
-      const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
-      const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
-      const uint32_t c0 = src32(cur, n1);
-      const uint32_t c1 = src32(n1, n2);
-      const uint32_t c2 = src32(n2, n3);
-      const uint32_t c3 = src32(n3, n4);
-      o[t] = acc | (c0 >> f);
-      o[t + 1] = __builtin_amdgcn_alignbit(c0, c1, f);
-      o[t + 2] = __builtin_amdgcn_alignbit(c1, c2, f);
-      o[t + 3] = __builtin_amdgcn_alignbit(c2, c3, f);
-      acc = __builtin_amdgcn_alignbit(c3, 0u, f);  // c3 << (32 - f), 0 when f = 0
-      cur = n4;
-    }
-    for (; t < full; ++t) {
-      const uint32_t nxt = __builtin_bswap32(p[t + 1]);
-      const uint32_t chunk = src32(cur, nxt);
-      o[t] = acc | (chunk >> f);
-      acc = __builtin_amdgcn_alignbit(chunk, 0u, f);
-      cur = nxt;
-    }
-    ap.acc = acc;
-    ap.w += full;
-    bp += 32ull * full;
-    n &= 31u;
-  }
-  if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
-}
 
 __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
                                                      const uint32_t* __restrict__ final_refs,

@@ -144,16 +144,18 @@ __device__ __forceinline__ uint64_t desc_load(const uint64_t* d) {
   return __hip_atomic_load(const_cast<uint64_t*>(d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Called by all 64 lanes of ONE wave.  Publishes `aggregate` for `tile`,
-// returns the exclusive prefix of all earlier tiles and publishes the
-// inclusive value.
-__device__ __forceinline__ uint64_t lookback(uint64_t* desc, uint32_t tile, uint64_t aggregate) {
+// Publishes `aggregate` for `tile` (tile 0 publishes it as its inclusive
+// value).  One lane suffices.  A tile publishes as early as it can and
+// resolves as late as it can, so that its successors rarely wait.
+__device__ __forceinline__ void lookback_publish(uint64_t* desc, uint32_t tile, uint64_t aggregate) {
+  desc_store(desc + tile, (tile == 0 ? kDescIncl : kDescAgg) | aggregate);
+}
+
+// Called by all 64 lanes of ONE wave after lookback_publish: returns the
+// exclusive prefix of all earlier tiles and publishes the inclusive value.
+__device__ __forceinline__ uint64_t lookback_resolve(uint64_t* desc, uint32_t tile, uint64_t aggregate) {
   const uint32_t lane = lane_id();
-  if (tile == 0) {
-    if (lane == 0) desc_store(desc, kDescIncl | aggregate);
-    return 0;
-  }
-  if (lane == 0) desc_store(desc + tile, kDescAgg | aggregate);
+  if (tile == 0) return 0;
   uint64_t excl = 0;
   int64_t base = static_cast<int64_t>(tile) - 1;
   while (true) {
@@ -182,6 +184,12 @@ __device__ __forceinline__ uint64_t lookback(uint64_t* desc, uint32_t tile, uint
   }
   if (lane == 0) desc_store(desc + tile, kDescIncl | (excl + aggregate));
   return excl;
+}
+
+// Publish and resolve in one go (called by all 64 lanes of ONE wave).
+__device__ __forceinline__ uint64_t lookback(uint64_t* desc, uint32_t tile, uint64_t aggregate) {
+  if (lane_id() == 0) lookback_publish(desc, tile, aggregate);
+  return lookback_resolve(desc, tile, aggregate);
 }
 
 // ---------------------------------------------------------------------------

@@ -21,12 +21,11 @@
 //    survivor base in the same pass;
 //  * survivors, ord_A and ord_B are staged in LDS and written with
 //    consecutive lanes on consecutive words.
-#include "em_internal.h"
+#include "em_tile.h"
 
 namespace em {
 
 constexpr int kMergeBlock = 256;
-constexpr uint32_t kDrop = 0x80000000u;  // refs are < 2^24, bit 31 marks a dropped A
 
 // LDS for a partition's key bytes; the compaction arrays reuse it after the merge.
 // (a multiple of 1 KB: LDS-DMA fills it 64 chunks of 16 bytes at a time)
@@ -55,69 +54,6 @@ struct MergeShared {
   uint32_t scan[kMergeBlock / kWave + 1];
   uint32_t tile, base;
 };
-
-// Merges this thread's slice of the partition.  Keys are read through
-// (base, position - lo + at) per side: the LDS copy when staged, the arenas
-// otherwise.  Returns the kept count; refs[] get the merged references with
-// kDrop on a replaced A.
-template <int IPT>
-__device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
-                                                const uint64_t* a_pfx, const uint64_t* b_pfx,
-                                                const uint8_t* abase, uint32_t a_adj,
-                                                const uint8_t* bbase, uint32_t b_adj, uint32_t k,
-                                                uint32_t len, uint32_t nA_t, uint32_t nB_t,
-                                                bool has_next_b, uint32_t i0, uint32_t nA_all,
-                                                uint32_t j0, uint32_t (&refs)[IPT]) {
-  // Prefix first; zero padding plus the lengths keep proper-prefix order exact
-  // (Everett, "GPU construction experiment", prefix-cache paragraph).
-  auto cmpAB = [&](uint32_t a, uint32_t b) -> int {
-    const uint64_t pa = a_pfx[a], pb = b_pfx[b];
-    if (pa != pb) return pa < pb ? -1 : 1;
-    const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
-    if (la <= 8 || lb <= 8) return (la > lb) - (la < lb);
-    return cmp_keys(abase, KeyRef{a_off[a] - a_adj + 8, la - 8}, bbase, KeyRef{b_off[b] - b_adj + 8, lb - 8});
-  };
-  uint32_t kept = 0;
-#pragma unroll
-  for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
-  if (k >= len) return 0;
-  uint32_t lo = k > nB_t ? k - nB_t : 0;
-  uint32_t hi = k < nA_t ? k : nA_t;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1) >> 1;
-    const uint32_t j = k - mid;
-    const bool too_big = j < nB_t && cmpAB(mid - 1, j) > 0;
-    if (too_big)
-      hi = mid - 1;
-    else
-      lo = mid;
-  }
-  uint32_t a = lo, b = k - lo;
-#pragma unroll
-  for (int s = 0; s < IPT; ++s) {
-    if (k + s < len) {
-      int c;
-      if (a < nA_t && b < nB_t) {
-        c = cmpAB(a, b);
-      } else if (a < nA_t) {
-        // B exhausted inside the partition: only the partition's last A can
-        // equal the next partition's first B.
-        c = (a == nA_t - 1 && has_next_b && cmpAB(a, nB_t) == 0) ? 0 : -1;
-      } else {
-        c = 1;
-      }
-      if (c <= 0) {
-        refs[s] = (i0 + a) | (c == 0 ? kDrop : 0u);
-        ++a;
-      } else {
-        refs[s] = nA_all + j0 + b;
-        ++b;
-      }
-      kept += c != 0;
-    }
-  }
-  return kept;
-}
 
 template <int IPT>
 __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(

@@ -12,12 +12,12 @@
 // locates the crossing, so the range shrinks 16-fold per round (six rounds
 // for 8M-record inputs) for 96 key reads per diagonal, against ~23 dependent
 // bisection steps or 256 reads for a whole-wave 64-way search.
-#include "em_internal.h"
+#include "em_tile.h"
 
 namespace em {
 
 constexpr int kPartBlock = 256;
-constexpr uint32_t kGroup = 16;  // lanes per diagonal
+constexpr uint32_t kGroup = 16;  // lanes per diagonal (corank16)
 
 __global__ __launch_bounds__(kPartBlock) void k_partition(em_side_t A, em_side_t B, uint32_t items,
                                                           uint32_t P, uint32_t* __restrict__ splits) {
@@ -31,26 +31,8 @@ __global__ __launch_bounds__(kPartBlock) void k_partition(em_side_t A, em_side_t
   const uint32_t d = live ? (d64 < N ? static_cast<uint32_t>(d64) : N) : 0;
   uint32_t lo = live ? (d > B.n ? d - B.n : 0) : 0;
   uint32_t hi = live ? (d < A.n ? d : A.n) : 0;
-  // Invariant: the co-rank lies in [lo, hi] and the "too large" test is false at lo.
-  while (lo < hi) {
-    const uint32_t span = hi - lo;
-    const uint32_t c = lo + static_cast<uint32_t>((static_cast<uint64_t>(t + 1) * span) / kGroup);
-    bool too_big = false;
-    if (c > 0 && d - c < B.n && c > lo) {
-      too_big = cmp_keys(A.keys, key_of(A, c - 1), B.keys, key_of(B, d - c)) > 0;
-    }
-    const uint32_t mask = static_cast<uint32_t>((__ballot(too_big) >> gshift) & 0xFFFFu);
-    // lanes [0, f) of the group are false and lanes [f, 16) true (monotone predicate)
-    const uint32_t f = mask ? static_cast<uint32_t>(__builtin_ctz(mask)) : kGroup;
-    const uint32_t c_prev = lo + static_cast<uint32_t>((static_cast<uint64_t>(f) * span) / kGroup);
-    if (f == kGroup) {
-      lo = hi;
-    } else {
-      const uint32_t c_f = lo + static_cast<uint32_t>((static_cast<uint64_t>(f + 1) * span) / kGroup);
-      lo = c_prev;
-      hi = c_f - 1;
-    }
-  }
+  // the co-rank lies in [lo, hi] and the "too large" test is false at lo
+  lo = corank16(A, B, d, lo, hi, t, gshift);
   if (live && t == 0) splits[diag] = lo;
 }
 
@@ -64,7 +46,7 @@ extern "C" int em_partition(const em_side_t* A, const em_side_t* B, uint32_t ite
   (void)ws_bytes;
   int rc = check_pair(A, B);
   if (rc) return rc;
-  if (!splits || items_per_part == 0 || items_per_part > EM_MAX_ITEMS_PER_PART) return EM_EINVAL;
+  if (!splits || items_per_part == 0) return EM_EINVAL;
   const uint32_t N = A->n + B->n;
   const uint32_t P = (N + items_per_part - 1) / items_per_part;
   const uint32_t groups = P + 1;

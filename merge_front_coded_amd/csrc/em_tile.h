@@ -1,0 +1,253 @@
+// Device building blocks shared by the merge, front-coding and fused kernels:
+// side selection by reference, the merge of one thread's slice of a
+// partition (with the 8-byte prefix cache), and the MSB-first bit appender
+// that writes records into an LDS window of output words.
+#pragma once
+
+#include "em_internal.h"
+
+namespace em {
+
+constexpr uint32_t kDrop = 0x80000000u;  // refs are < 2^24, bit 31 marks a dropped A
+
+// The fields of the side a reference names, chosen by value selects (taking
+// the address of a by-value kernel argument would force a private copy).
+struct SideView {
+  const uint8_t* keys;
+  const uint32_t* key_off;
+  const uint8_t* vals;
+  const uint32_t* val_off;
+  const uint8_t* tomb;
+  bool isB;
+};
+
+__device__ __forceinline__ SideView pick(const em_side_t& A, const em_side_t& B, uint32_t ref,
+                                         uint32_t& idx) {
+  // A reference outside [0, |A|+|B|) can only come from contract-violating
+  // inputs; it is clamped so that no access leaves the arrays.
+  const uint32_t N = A.n + B.n;
+  if (ref >= N) ref = N - 1;
+  const bool b = ref >= A.n;
+  idx = b ? ref - A.n : ref;
+  return SideView{b ? B.keys : A.keys, b ? B.key_off : A.key_off, b ? B.vals : A.vals,
+                  b ? B.val_off : A.val_off, b ? B.tomb : A.tomb, b};
+}
+
+__device__ __forceinline__ KeyRef key_of(const SideView& s, uint32_t r) {
+  const uint32_t p = s.key_off[r];
+  return KeyRef{p, s.key_off[r + 1] - p};
+}
+
+__device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, uint32_t& vlen,
+                                               bool& tomb) {
+  tomb = s.tomb != nullptr && s.tomb[idx] != 0;
+  vlen = tomb ? 0u : s.val_off[idx + 1] - s.val_off[idx];
+  return tomb ? 1u : 1u + eg0_len(vlen) + 8u * vlen;
+}
+
+// Merges this thread's slice of the partition.  Keys are read through
+// (base, position - lo + at) per side: the LDS copy when staged, the arenas
+// otherwise.  Returns the kept count; refs[] get the merged references with
+// kDrop on a replaced A.
+template <int IPT>
+__device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
+                                                const uint64_t* a_pfx, const uint64_t* b_pfx,
+                                                const uint8_t* abase, uint32_t a_adj,
+                                                const uint8_t* bbase, uint32_t b_adj, uint32_t k,
+                                                uint32_t len, uint32_t nA_t, uint32_t nB_t,
+                                                bool has_next_b, uint32_t i0, uint32_t nA_all,
+                                                uint32_t j0, uint32_t (&refs)[IPT]) {
+  // Prefix first; zero padding plus the lengths keep proper-prefix order exact
+  // (Everett, "GPU construction experiment", prefix-cache paragraph).
+  auto cmpAB = [&](uint32_t a, uint32_t b) -> int {
+    const uint64_t pa = a_pfx[a], pb = b_pfx[b];
+    if (pa != pb) return pa < pb ? -1 : 1;
+    const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
+    if (la <= 8 || lb <= 8) return (la > lb) - (la < lb);
+    return cmp_keys(abase, KeyRef{a_off[a] - a_adj + 8, la - 8}, bbase, KeyRef{b_off[b] - b_adj + 8, lb - 8});
+  };
+  uint32_t kept = 0;
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
+  if (k >= len) return 0;
+  uint32_t lo = k > nB_t ? k - nB_t : 0;
+  uint32_t hi = k < nA_t ? k : nA_t;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi + 1) >> 1;
+    const uint32_t j = k - mid;
+    const bool too_big = j < nB_t && cmpAB(mid - 1, j) > 0;
+    if (too_big)
+      hi = mid - 1;
+    else
+      lo = mid;
+  }
+  uint32_t a = lo, b = k - lo;
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) {
+    if (k + s < len) {
+      int c;
+      if (a < nA_t && b < nB_t) {
+        c = cmpAB(a, b);
+      } else if (a < nA_t) {
+        // B exhausted inside the partition: only the partition's last A can
+        // equal the next partition's first B.
+        c = (a == nA_t - 1 && has_next_b && cmpAB(a, nB_t) == 0) ? 0 : -1;
+      } else {
+        c = 1;
+      }
+      if (c <= 0) {
+        refs[s] = (i0 + a) | (c == 0 ? kDrop : 0u);
+        ++a;
+      } else {
+        refs[s] = nA_all + j0 + b;
+        ++b;
+      }
+      kept += c != 0;
+    }
+  }
+  return kept;
+}
+
+// Appends bits MSB-first at consecutive output positions inside the current
+// slice window.  Positions are relative to the slice's first bit.
+struct BitAppender {
+  uint32_t* out;
+  uint32_t w;      // word being filled
+  uint32_t fill;   // bits already in it
+  uint32_t acc;
+  bool shared;     // the word being filled also holds another record's bits
+
+  __device__ __forceinline__ void start(uint32_t* o, uint32_t pos) {
+    out = o;
+    w = pos >> 5;
+    fill = pos & 31u;
+    acc = 0;
+    shared = fill != 0;
+  }
+  __device__ __forceinline__ void store_full() {
+    if (shared)
+      atomicOr(out + w, acc);
+    else
+      out[w] = acc;
+    ++w;
+    acc = 0;
+    shared = false;
+  }
+  // n in 1..32, bits right-aligned
+  __device__ __forceinline__ void put(uint32_t bits, uint32_t n) {
+    const uint32_t space = 32u - fill;
+    if (n < space) {
+      acc |= bits << (space - n);
+      fill += n;
+      return;
+    }
+    const uint32_t rem = n - space;
+    acc |= rem ? bits >> rem : bits;
+    store_full();
+    acc = rem ? bits << (32u - rem) : 0u;
+    fill = rem;
+  }
+  __device__ __forceinline__ void put64(uint64_t v, uint32_t n) {  // n in 0..64
+    if (n > 32) {
+      put(static_cast<uint32_t>(v >> 32) & (0xFFFFFFFFu >> (64u - n)), n - 32);
+      n = 32;
+    }
+    if (n) put(static_cast<uint32_t>(v) & (0xFFFFFFFFu >> (32u - n)), n);
+  }
+  __device__ __forceinline__ void finish() {
+    if (fill) atomicOr(out + w, acc);  // the last word is shared with the next record
+  }
+};
+
+// 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
+__device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
+  const uint32_t* p = base + (bp >> 5);
+  const uint32_t hi = __builtin_bswap32(p[0]), lo = __builtin_bswap32(p[1]);
+  const uint32_t sh = static_cast<uint32_t>(bp & 31u);
+  // v_alignbit takes its shift modulo 32, so offset 0 is the high dword itself
+  return sh ? __builtin_amdgcn_alignbit(hi, lo, 32u - sh) : hi;
+}
+
+// Appends source bits [bp, bp + n) of a dword array.  After the first word
+// the output fill level stays fixed, so each further output word is one new
+// source dword and two funnel shifts.
+__device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, uint64_t bp, uint32_t n) {
+  if (n >= 32 && ap.shared) {  // the shared first word goes through the general path
+    ap.put(bits32_at(base, bp), 32);
+    bp += 32;
+    n -= 32;
+  }
+  if (n >= 32) {
+    const uint32_t* p = base + (bp >> 5);
+    const uint32_t sb = static_cast<uint32_t>(bp & 31u);
+    const uint32_t f = ap.fill;
+    uint32_t cur = __builtin_bswap32(p[0]);
+    uint32_t acc = ap.acc;
+    uint32_t* o = ap.out + ap.w;
+    const uint32_t full = n >> 5;
+    // source dword pair -> the 32 bits starting sb bits into the first one;
+    // v_alignbit takes its shift modulo 32, so sb = 0 selects the first dword
+    const uint32_t rs = 32u - sb;
+    auto src32 = [sb, rs](uint32_t a, uint32_t b) { return sb ? __builtin_amdgcn_alignbit(a, b, rs) : a; };
+    uint32_t t = 0;
+    for (; t + 4 <= full; t += 4) {  // four source dwords in flight per iteration
+      const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
+      const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
+      const uint32_t c0 = src32(cur, n1);
+      const uint32_t c1 = src32(n1, n2);
+      const uint32_t c2 = src32(n2, n3);
+      const uint32_t c3 = src32(n3, n4);
+      o[t] = acc | (c0 >> f);
+      o[t + 1] = __builtin_amdgcn_alignbit(c0, c1, f);
+      o[t + 2] = __builtin_amdgcn_alignbit(c1, c2, f);
+      o[t + 3] = __builtin_amdgcn_alignbit(c2, c3, f);
+      acc = __builtin_amdgcn_alignbit(c3, 0u, f);  // c3 << (32 - f), 0 when f = 0
+      cur = n4;
+    }
+    for (; t < full; ++t) {
+      const uint32_t nxt = __builtin_bswap32(p[t + 1]);
+      const uint32_t chunk = src32(cur, nxt);
+      o[t] = acc | (chunk >> f);
+      acc = __builtin_amdgcn_alignbit(chunk, 0u, f);
+      cur = nxt;
+    }
+    ap.acc = acc;
+    ap.w += full;
+    bp += 32ull * full;
+    n &= 31u;
+  }
+  if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
+}
+
+// Co-rank of diagonal d (A records among the first d outputs of the stable
+// merge, ties to A) inside [lo, hi], where the "too large" test A[i-1] > B[d-i]
+// is false at lo.  Searched by a group of 16 lanes: t is the lane in the
+// group, gshift the group's first lane in the wave.  Each round tests 16
+// evenly spaced candidates and a ballot finds the crossing, shrinking the
+// range 16-fold.
+__device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t& B, uint32_t d,
+                                             uint32_t lo, uint32_t hi, uint32_t t, uint32_t gshift) {
+  constexpr uint32_t G = 16;
+  while (lo < hi) {
+    const uint32_t span = hi - lo;
+    const uint32_t c = lo + static_cast<uint32_t>((static_cast<uint64_t>(t + 1) * span) / G);
+    bool too_big = false;
+    if (c > 0 && d - c < B.n && c > lo) {
+      too_big = cmp_keys(A.keys, key_of(A, c - 1), B.keys, key_of(B, d - c)) > 0;
+    }
+    const uint32_t mask = static_cast<uint32_t>((__ballot(too_big) >> gshift) & 0xFFFFu);
+    // lanes [0, f) of the group are false and lanes [f, 16) true (monotone predicate)
+    const uint32_t f = mask ? static_cast<uint32_t>(__builtin_ctz(mask)) : G;
+    const uint32_t c_prev = lo + static_cast<uint32_t>((static_cast<uint64_t>(f) * span) / G);
+    if (f == G) {
+      lo = hi;
+    } else {
+      const uint32_t c_f = lo + static_cast<uint32_t>((static_cast<uint64_t>(f + 1) * span) / G);
+      lo = c_prev;
+      hi = c_f - 1;
+    }
+  }
+  return lo;
+}
+
+}  // namespace em

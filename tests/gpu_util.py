@@ -23,11 +23,11 @@ def workload(wid: int, scale: float = 1.0):
     return gen.make(w)
 
 
-def run_gpu(Ah, Bh, items=2048, path="merge", keep_lcp=True):
+def run_gpu(Ah, Bh, items=2048, path="merge", keep_lcp=True, **kw):
     import merge_front_coded_amd as em
     A = em.DeviceSide.from_host(Ah)
     B = em.DeviceSide.from_host(Bh)
-    pl = em.Pipeline(A, B, items_per_part=items, path=path, keep_lcp=keep_lcp)
+    pl = em.Pipeline(A, B, items_per_part=items, path=path, keep_lcp=keep_lcp, **kw)
     pl.run()
     return pl
 
@@ -75,8 +75,10 @@ def compare(pl, ref, Ah, Bh, check_splits=True, label=""):
     assert bad.size == 0, f"{label}: payload differs first at byte {bad[0]} (bit {8 * bad[0]}) of {got.size}"
 
 
-def check_path(Ah, Bh, items=2048, path="merge", keep_lcp=True, label=""):
-    ref = oracle.run(Ah, Bh, items_per_part=items)
-    pl = run_gpu(Ah, Bh, items=items, path=path, keep_lcp=keep_lcp)
+def check_path(Ah, Bh, items=2048, path="merge", keep_lcp=True, label="", **kw):
+    if path == "fused" and items and items > 256:
+        items = 256
+    ref = oracle.run(Ah, Bh, items_per_part=items or 256)
+    pl = run_gpu(Ah, Bh, items=items, path=path, keep_lcp=keep_lcp, **kw)
     compare(pl, ref, Ah, Bh, label=label or f"{path}/items={items}")
     return pl, ref

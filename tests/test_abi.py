@@ -79,7 +79,13 @@ def test_argument_errors_before_any_launch(lib):
     # null splits, zero or oversized partition sizes
     assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 16, None, None, 0, None) == -1
     assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 0, buf, None, 0, None) == -1
-    assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 4097, buf, None, 0, None) == -1
+    # merge tiles hold at most EM_MAX_ITEMS_PER_PART outputs; the fused kernel 256
+    assert lib.em_merge_keep(ctypes.byref(A), ctypes.byref(B), buf, 4097, buf, None, None, buf,
+                             ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    for items, coarse in ((0, 256), (257, 514), (64, 100), (64, 0)):
+        assert lib.em_merge_fc(ctypes.byref(A), ctypes.byref(B), buf, coarse, items, buf, 1 << 20, buf,
+                               buf, None, None, None, None, None, None, ctypes.c_void_p(0x100000),
+                               1 << 20, None) == -1
     # misaligned arena
     bad = _side(ptr=0x1001)
     assert lib.em_partition(ctypes.byref(bad), ctypes.byref(B), 16, buf, None, 0, None) == -1

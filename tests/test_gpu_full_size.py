@@ -43,7 +43,7 @@ def test_full_size_workload_matches_oracle(wid):
     A, B = gen.make(wid)
     assert _sha(A.keys, A.key_off, A.vals, A.val_off, A.tomb, B.keys, B.key_off, B.vals, B.val_off,
                 B.tomb) == ref["input"], "generator output drifted from the digested inputs"
-    for path in ("merge", "collision"):
+    for path in ("fused", "merge", "collision"):
         print(f"  path {path}", flush=True)
         pl = run_gpu(A, B, items=None, path=path)
         torch.cuda.synchronize()

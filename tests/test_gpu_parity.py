@@ -56,6 +56,15 @@ def test_uniform_workload_full_10k():
     print("uniform-az 10k+10k", flush=True)
     check_path(A, B, items=2048)
     check_path(A, B, items=2048, path="collision")
+    check_path(A, B, items=256, path="fused")
+
+
+@pytest.mark.parametrize("items,coarse_parts", [(1, 1), (1, 16), (3, 5), (17, 16), (64, 2), (100, 3),
+                                                (255, 16), (256, 1), (256, 16)])
+def test_fused_every_partition_size(items, coarse_parts):
+    A, B = workload(1, 0.3)
+    print(f"fused uniform-az 3000+3000 items={items} coarse={coarse_parts}", flush=True)
+    check_path(A, B, items=items, path="fused", coarse_parts=coarse_parts)
 
 
 def test_empty_sides():
@@ -65,7 +74,7 @@ def test_empty_sides():
     empty = _records_side([])
     for A, B, name in ((empty, full, "A empty"), (full, empty, "B empty"), (empty, empty, "both empty")):
         print(name, flush=True)
-        for path in ("merge", "collision"):
+        for path in ("merge", "collision", "fused"):
             pl, ref = check_path(A, B, items=64, path=path, label=f"{name}/{path}")
             if name == "both empty":
                 assert pl.S == 0 and pl.T == 0
@@ -76,11 +85,11 @@ def test_all_and_no_collisions():
     keys = sorted({_rand_bytes(rng, 1, 20) for _ in range(5000)})
     A = _records_side([(k, _rand_bytes(rng, 0, 16)) for k in keys])
     B = _records_side([(k, None if rng.random() < 0.3 else _rand_bytes(rng, 0, 16)) for k in keys])
-    for path in ("merge", "collision"):
+    for path in ("merge", "collision", "fused"):
         check_path(A, B, items=256, path=path, label=f"all collide/{path}")
     A2 = _records_side([(k, b"a") for k in keys[::2]])
     B2 = _records_side([(k, b"b") for k in keys[1::2]])
-    for path in ("merge", "collision"):
+    for path in ("merge", "collision", "fused"):
         check_path(A2, B2, items=256, path=path, label=f"none collide/{path}")
 
 
@@ -96,7 +105,7 @@ def test_proper_prefix_and_binary_keys():
     for trial in range(4):
         A, B = _split(keys, rng, p_both=0.4, p_tomb=0.2, vmax=12, tomb_a=True)
         for items in (5, 256, 2048):
-            for path in ("merge", "collision"):
+            for path in ("merge", "collision", "fused"):
                 check_path(A, B, items=items, path=path, label=f"binary trial {trial}/{items}/{path}")
 
 
@@ -106,8 +115,10 @@ def test_long_records_span_many_words():
     recs = [(k, _rand_bytes(rng, 0, 3000)) for k in keys]
     A = _records_side(recs[::2])
     B = _records_side([(k, None if i % 4 == 0 else v) for i, (k, v) in enumerate(recs[1::2])])
-    for path in ("merge", "collision"):
+    for path in ("merge", "collision", "fused"):
         check_path(A, B, items=64, path=path)
+    # records much longer than a staging buffer or the output window
+    check_path(A, B, items=256, path="fused", label="fused, long records")
     # emitter recomputing l when no lcp array is kept
     check_path(A, B, items=64, keep_lcp=False, label="emit without lcp array")
 
@@ -118,6 +129,8 @@ def test_equal_pairs_split_by_partition_boundaries():
     A, B = _split(keys, rng, p_both=0.8, p_tomb=0.1, vmax=6)
     for items in (2, 3, 4, 5, 17, 256, 511):
         check_path(A, B, items=items, label=f"dense collisions items={items}")
+    for items in (2, 5, 17, 256):
+        check_path(A, B, items=items, path="fused", coarse_parts=3, label=f"fused dense items={items}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 14, 15, 16, 29, 30, 31, 46])
@@ -127,14 +140,16 @@ def test_w15_phase_counts(n):
     A = _records_side([(k, _rand_bytes(rng, 0, 5)) for k in keys[::2]])
     B = _records_side([(k, None if i % 3 == 0 else b"v") for i, k in enumerate(keys[1::2])])
     check_path(A, B, items=4)
+    check_path(A, B, items=4, path="fused", coarse_parts=2)
 
 
 @pytest.mark.parametrize("wid,scale", [(2, 0.02), (3, 0.002), (4, 0.001), (5, 0.005)])
 def test_scaled_workloads(wid, scale):
     A, B = workload(wid, scale)
     print(f"workload {wid} at {scale}: {A.n}+{B.n}", flush=True)
-    for path in ("merge", "collision"):
-        check_path(A, B, items=2048, path=path, label=f"w{wid}@{scale}/{path}")
+    for path in ("merge", "collision", "fused"):
+        check_path(A, B, items=None if path == "fused" else 2048, path=path,
+                   label=f"w{wid}@{scale}/{path}")
 
 
 def test_scan_random_lengths_many_tiles():
