@@ -66,14 +66,12 @@ __global__ __launch_bounds__(kLenBlock) void k_fc_lengths(em_side_t A, em_side_t
 constexpr int kEmitBlock = 256;
 constexpr uint32_t kEmitExtra = 16;
 constexpr uint32_t kEmitMaxRecs = kEmitBlock - kEmitExtra;  // owned records per workgroup, at most
-#ifndef EW
-#define EW 6144
-#endif
-constexpr uint32_t kEmitWindow = EW;
-#ifndef ES
-#define ES 24
-#endif
-constexpr uint32_t kEmitStage = ES * 1024;
+// LDS per workgroup is kept small (about 25 KB) so that six workgroups share
+// a compute unit: the emitter waits on three dependent global loads per
+// workgroup (records, their offsets, the source spans), and more workgroups
+// in flight hide them better than larger ones.
+constexpr uint32_t kEmitWindow = 2560;      // output words per slice (10 KB)
+constexpr uint32_t kEmitStage = 14 * 1024;  // staged source bytes
 
 struct EmitShared {
   uint32_t out[kEmitWindow];
@@ -84,6 +82,68 @@ struct EmitShared {
   uint32_t kprev0;
   uint64_t bit_lo, bit_hi, bit_ext;
 };
+
+// One record's fields for the slice loop; segment ends are relative to the
+// record start, kbit/vbit are the source bit positions of the key suffix and
+// the value bytes.
+struct EmitRecord {
+  bool live;
+  uint64_t off, end;
+  uint32_t c, k, l;
+  uint64_t vh;
+  uint32_t b1, b2, b3, b4, b5;
+  uint64_t kbit, vbit;
+};
+
+// Steps 2 and 3 for the workgroup: the records' bits go into the LDS window
+// slice by slice, and each slice's owned words are copied out.
+__device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r, const uint32_t* kbase,
+                                            const uint32_t* vbase, uint64_t T, uint32_t* payload) {
+  const uint32_t tid = threadIdx.x;
+  const uint64_t wb = (sh.bit_lo >> 5) << 5;           // first bit of window word 0
+  const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
+  const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
+  const uint64_t ext = sh.bit_ext;
+  for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
+    const uint64_t s1 = min(s0 + 32ull * kEmitWindow, ext);
+    const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
+    for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
+    __syncthreads();
+    if (r.live && r.off < s1 && r.end > s0) {
+      // this record's bits inside [s0, s1), relative to the record start
+      const uint32_t from = r.off >= s0 ? 0u : static_cast<uint32_t>(s0 - r.off);
+      const uint32_t to = r.end <= s1 ? r.b5 : static_cast<uint32_t>(s1 - r.off);
+      BitAppender ap;
+      ap.start(sh.out, static_cast<uint32_t>(r.off + from - s0));
+      // EG0(c), EG0(k-l), presence + EG0(value length): immediates
+      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
+        const uint32_t lo = max(a, from), hi = min(b, to);
+        if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
+      };
+      auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
+        const uint32_t lo = max(a, from), hi = min(b, to);
+        if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
+      };
+      imm(static_cast<uint64_t>(r.c) + 1u, 0, r.b1);
+      imm(static_cast<uint64_t>(r.k - r.l) + 1u, r.b1, r.b2);
+      span(kbase, r.kbit, r.b2, r.b3);
+      imm(r.vh, r.b3, r.b4);
+      span(vbase, r.vbit, r.b4, r.b5);
+      ap.finish();
+    }
+    __syncthreads();
+    // owned words of this slice: 16-byte stores between a scalar head and tail
+    const uint64_t o_lo = max(w_lo, s0 >> 5), o_hi = min(w_hi, (s1 + 31) >> 5);
+    const uint64_t wbase = s0 >> 5;  // global word number of window word 0
+    auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
+    const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
+    for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
+    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock)
+      *reinterpret_cast<uint4*>(payload + w) = uint4{win(w), win(w + 1), win(w + 2), win(w + 3)};
+    for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
+    __syncthreads();
+  }
+}
 
 __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
                                                      const uint32_t* __restrict__ final_refs,
@@ -202,74 +262,29 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     __builtin_amdgcn_s_waitcnt(0);
   }
   // source bit positions of this record's key suffix and value bytes
-  const uint32_t* kbase;
-  const uint32_t* vbase;
-  uint64_t kbit, vbit;
-  {
-    const uint32_t qk = isB ? 1u : 0u, qv = 2u + qk;
-    if (staged) {
-      kbase = vbase = reinterpret_cast<const uint32_t*>(sh.stage);
-      // relative to the first emitted key byte, which lies inside the span
-      kbit = 8ull * (kpos + (l >> 3) - sh.span_lo[qk] + sh.stage_at[qk]) + (l & 7u);
-      vbit = 8ull * (vpos - sh.span_lo[qv] + sh.stage_at[qv]);
-    } else {
-      kbase = reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys);
-      vbase = reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals);
-      kbit = 8ull * kpos + l;
-      vbit = 8ull * vpos;
-    }
-  }
   const uint32_t k = 8u * klen;
   const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l), ev = eg0_len(vlen);
   const uint32_t vhl = tomb ? 1u : 1u + ev;
   const uint64_t vh = tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(vlen) + 1ull));
   // segment ends relative to the record start
   const uint32_t b1 = e1, b2 = b1 + e2, b3 = b2 + (k - l), b4 = b3 + vhl, b5 = b4 + 8u * vlen;
+  EmitRecord rec{active && b5 == rec_end - rec_off, rec_off, rec_end, c, k, l, vh, b1, b2, b3, b4, b5, 0, 0};
   __syncthreads();
-
-  // ---- 2/3. slices of the output window ----
-  const uint64_t wb = (sh.bit_lo >> 5) << 5;           // first bit of window word 0
-  const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
-  const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
-  const uint64_t ext = sh.bit_ext;
-  for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
-    const uint64_t s1 = min(s0 + 32ull * kEmitWindow, ext);
-    const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
-    for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
-    __syncthreads();
-    if (active && rec_off < s1 && rec_end > s0 && b5 == rec_end - rec_off) {
-      // this record's bits inside [s0, s1), relative to the record start
-      const uint32_t from = rec_off >= s0 ? 0u : static_cast<uint32_t>(s0 - rec_off);
-      const uint32_t to = rec_end <= s1 ? b5 : static_cast<uint32_t>(s1 - rec_off);
-      BitAppender ap;
-      ap.start(sh.out, static_cast<uint32_t>(rec_off + from - s0));
-      // EG0(c), EG0(k-l), presence + EG0(value length): immediates
-      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
-        const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
-      };
-      auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
-        const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
-      };
-      imm(static_cast<uint64_t>(c) + 1u, 0, b1);
-      imm(static_cast<uint64_t>(k - l) + 1u, b1, b2);
-      span(kbase, kbit, b2, b3);
-      imm(vh, b3, b4);
-      span(vbase, vbit, b4, b5);
-      ap.finish();
-    }
-    __syncthreads();
-    // owned words of this slice: 16-byte stores between a scalar head and tail
-    const uint64_t o_lo = max(w_lo, s0 >> 5), o_hi = min(w_hi, (s1 + 31) >> 5);
-    const uint64_t wbase = s0 >> 5;  // global word number of window word 0
-    auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
-    const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
-    for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
-    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock)
-      *reinterpret_cast<uint4*>(payload + w) = uint4{win(w), win(w + 1), win(w + 2), win(w + 3)};
-    for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
-    __syncthreads();
+  // The two source kinds get separate code so that the staged one reads LDS
+  // with LDS instructions (a pointer that may be either would be read with
+  // flat loads).
+  if (staged) {
+    const uint32_t qk = isB ? 1u : 0u, qv = 2u + qk;
+    // relative to the first emitted key byte, which lies inside the span
+    rec.kbit = 8ull * (kpos + (l >> 3) - sh.span_lo[qk] + sh.stage_at[qk]) + (l & 7u);
+    rec.vbit = 8ull * (vpos - sh.span_lo[qv] + sh.stage_at[qv]);
+    const uint32_t* st = reinterpret_cast<const uint32_t*>(sh.stage);
+    emit_slices(sh, rec, st, st, T, payload);
+  } else {
+    rec.kbit = 8ull * kpos + l;
+    rec.vbit = 8ull * vpos;
+    emit_slices(sh, rec, reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys),
+                reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals), T, payload);
   }
 }
 
@@ -306,11 +321,16 @@ extern "C" int em_emit(const em_side_t* A, const em_side_t* B, const uint32_t* f
   if (S == 0) return EM_OK;
   if (!final_refs || !off || !payload) return EM_EINVAL;
   if (payload_words < (T + 31) / 32) return EM_ENOSPC;
-  // records per workgroup: keep the expected output window and staged
-  // source bytes of one workgroup at about half of their LDS capacity
+  // records per workgroup: the expected output bits and staged source bytes
+  // of one workgroup fill about 90% of the window and the stage (a workgroup
+  // above that takes its window in slices or reads its sources in place).
+  // Staged spans also hold the keys of replaced records and 16-byte margins,
+  // so the source estimate is all input bytes per survivor plus 4.
   const double mean_bits = static_cast<double>(T) / S;
-  double r1 = 0.5 * kEmitWindow * 32.0 / mean_bits;
-  double r2 = 0.5 * kEmitStage * 8.0 / mean_bits;
+  const double mean_src =
+      static_cast<double>(A->key_bytes + B->key_bytes + A->val_bytes + B->val_bytes) / S + 4.0;
+  double r1 = 0.9 * kEmitWindow * 32.0 / mean_bits;
+  double r2 = 0.9 * kEmitStage / mean_src;
   double r = r1 < r2 ? r1 : r2;
   uint32_t rpb = r >= kEmitMaxRecs ? kEmitMaxRecs : (r < 16.0 ? 16u : static_cast<uint32_t>(r));
   const uint32_t blocks = (S + rpb - 1) / rpb;

@@ -25,6 +25,8 @@
 // The partition's bit stream is built in an LDS window at local alignment and
 // stored shifted to its global bit base, in slices when it is longer than the
 // window.
+#include <type_traits>
+
 #include "em_tile.h"
 
 namespace em {
@@ -164,15 +166,14 @@ __global__ __launch_bounds__(kFuseBlock) void k_merge_fc(
   const uint32_t a_bytes = ((sh.a_off[na_off - 1] + 16u + 15u) & ~15u) - a_lo;
   const uint32_t b_lo = sh.b_off[0] & ~15u;
   const uint32_t b_bytes = ((sh.b_off[nb_off - 1] + 16u + 15u) & ~15u) - b_lo;
-  const bool keys_staged = a_bytes + b_bytes <= kFuseKeyCap;
   const uint32_t av_lo = sh.a_voff[0] & ~15u;
   const uint32_t av_bytes = ((sh.a_voff[nA_t] + 8u + 15u) & ~15u) - av_lo;
   const uint32_t bv_lo = sh.b_voff[0] & ~15u;
   const uint32_t bv_bytes = ((sh.b_voff[nB_t] + 8u + 15u) & ~15u) - bv_lo;
-  const bool vals_staged = av_bytes + bv_bytes <= kFuseValCap;
+  const bool staged = a_bytes + b_bytes <= kFuseKeyCap && av_bytes + bv_bytes <= kFuseValCap;
   {
-    const uint32_t nk16 = keys_staged ? (a_bytes + b_bytes) / 16 : 0u, na16 = a_bytes / 16;
-    const uint32_t nv16 = vals_staged ? (av_bytes + bv_bytes) / 16 : 0u, nav16 = av_bytes / 16;
+    const uint32_t nk16 = staged ? (a_bytes + b_bytes) / 16 : 0u, na16 = a_bytes / 16;
+    const uint32_t nv16 = staged ? (av_bytes + bv_bytes) / 16 : 0u, nav16 = av_bytes / 16;
     for (uint32_t c0 = (tid / kWave) * kWave; c0 < nk16; c0 += kFuseBlock) {
       const uint32_t c = c0 + lane;
       if (c < nk16)
@@ -186,274 +187,285 @@ __global__ __launch_bounds__(kFuseBlock) void k_merge_fc(
     __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  // key / value addressing: LDS copy when staged, the arenas otherwise
-  const uint8_t* kbA = keys_staged ? reinterpret_cast<const uint8_t*>(sh.keys) : A.keys;
-  const uint8_t* kbB = keys_staged ? reinterpret_cast<const uint8_t*>(sh.keys) : B.keys;
-  const uint32_t kadjA = keys_staged ? a_lo : 0u, kadjB = keys_staged ? b_lo - a_bytes : 0u;
-  const uint8_t* vbA = vals_staged ? reinterpret_cast<const uint8_t*>(sh.vals) : A.vals;
-  const uint8_t* vbB = vals_staged ? reinterpret_cast<const uint8_t*>(sh.vals) : B.vals;
-  const uint32_t vadjA = vals_staged ? av_lo : 0u, vadjB = vals_staged ? bv_lo - av_bytes : 0u;
+  // The rest of the partition's work is compiled twice, for the LDS copy and
+  // for the arenas, so that the staged variant reads LDS with LDS
+  // instructions (a pointer that may be either would be read with flat loads).
+  auto rest = [&](auto staged_tag) __attribute__((always_inline)) {
+    constexpr bool ST = decltype(staged_tag)::value;
+    const uint8_t* kbA = ST ? reinterpret_cast<const uint8_t*>(sh.keys) : A.keys;
+    const uint8_t* kbB = ST ? reinterpret_cast<const uint8_t*>(sh.keys) : B.keys;
+    const uint32_t kadjA = ST ? a_lo : 0u, kadjB = ST ? b_lo - a_bytes : 0u;
+    const uint8_t* vbA = ST ? reinterpret_cast<const uint8_t*>(sh.vals) : A.vals;
+    const uint8_t* vbB = ST ? reinterpret_cast<const uint8_t*>(sh.vals) : B.vals;
+    const uint32_t vadjA = ST ? av_lo : 0u, vadjB = ST ? bv_lo - av_bytes : 0u;
 
-  // ---- 4. prefix cache of the partition's merge keys ----
-  {
-    const uint32_t* ao = sh.a_off + a_first;
-    const uint32_t* bo = sh.b_off + b_first;
-    const uint32_t nbk = nB_t + (has_next_b ? 1u : 0u);
-    for (uint32_t x = tid; x < nA_t; x += kFuseBlock) {
-      const uint32_t ln = ao[x + 1] - ao[x];
-      sh.u.m.a_pfx[x] = load_be8(kbA, ao[x] - kadjA) & be_mask(ln < 8 ? ln : 8);
-    }
-    for (uint32_t y = tid; y < nbk; y += kFuseBlock) {
-      const uint32_t ln = bo[y + 1] - bo[y];
-      sh.u.m.b_pfx[y] = load_be8(kbB, bo[y] - kadjB) & be_mask(ln < 8 ? ln : 8);
-    }
-  }
-  __syncthreads();
-
-  // ---- 5. merge (one output per thread) and keep-newer ----
-  uint32_t refs[1];
-  const uint32_t kept = merge_slice<1>(sh.a_off + a_first, sh.b_off + b_first, sh.u.m.a_pfx, sh.u.m.b_pfx,
-                                       kbA, kadjA, kbB, kadjB, tid, len, nA_t, nB_t, has_next_b, i0, A.n,
-                                       j0, refs);
-  uint32_t n_kept;
-  const uint32_t ord = block_exclusive_scan<uint32_t, kFuseBlock>(kept, sh.scan32, n_kept);
-  if (tid < len) {
-    const uint32_t ref = refs[0] & ~kDrop;
-    const bool drop = (refs[0] & kDrop) != 0;
-    if (ref < A.n)
-      sh.ords[ref - i0] = drop ? EM_NONE : ord;
-    else
-      sh.ords[nA_t + (ref - A.n - j0)] = ord;
-    if (!drop) sh.surv[ord] = ref;
-  }
-
-  // ---- 6. publish the survivor count early; the base is resolved later ----
-  if (tid == 0) lookback_publish(desc_s, tile, n_kept);
-  __syncthreads();
-
-  // ---- 7. this thread's survivor: key, value, predecessor, LCP ----
-  const bool has = tid < n_kept;
-  uint32_t kpos = 0, klen = 0, l = 0, kprev = 0, vpos = 0, vlen = 0;
-  bool isB = false, tomb = false;
-  if (has) {
-    const uint32_t ref = sh.surv[tid];
-    isB = ref >= A.n;
-    uint32_t ko, kend;
-    if (isB) {
-      const uint32_t y = ref - A.n - j0;
-      ko = sh.b_off[b_first + y] - kadjB;
-      kend = sh.b_off[b_first + y + 1] - kadjB;
-      tomb = sh.b_tomb[y] != 0;
-      vlen = tomb ? 0u : sh.b_voff[y + 1] - sh.b_voff[y];
-      vpos = sh.b_voff[y] - vadjB;
-    } else {
-      const uint32_t x = ref - i0;
-      ko = sh.a_off[a_first + x] - kadjA;
-      kend = sh.a_off[a_first + x + 1] - kadjA;
-      tomb = sh.a_tomb[x] != 0;
-      vlen = tomb ? 0u : sh.a_voff[x + 1] - sh.a_voff[x];
-      vpos = sh.a_voff[x] - vadjA;
-    }
-    kpos = ko;
-    klen = kend - ko;
-    const uint8_t* xb = isB ? kbB : kbA;
-    const KeyRef xk{ko, klen};
-    // predecessor survivor's key
-    bool have_p = false;
-    const uint8_t* pb = nullptr;
-    KeyRef pk{0, 0};
-    if (tid > 0) {
-      const uint32_t pref = sh.surv[tid - 1];
-      have_p = true;
-      if (pref >= A.n) {
-        const uint32_t y = pref - A.n - j0;
-        pb = kbB;
-        pk = KeyRef{sh.b_off[b_first + y] - kadjB, sh.b_off[b_first + y + 1] - sh.b_off[b_first + y]};
-      } else {
-        const uint32_t x = pref - i0;
-        pb = kbA;
-        pk = KeyRef{sh.a_off[a_first + x] - kadjA, sh.a_off[a_first + x + 1] - sh.a_off[a_first + x]};
+    // ---- 4. prefix cache of the partition's merge keys ----
+    {
+      const uint32_t* ao = sh.a_off + a_first;
+      const uint32_t* bo = sh.b_off + b_first;
+      const uint32_t nbk = nB_t + (has_next_b ? 1u : 0u);
+      for (uint32_t x = tid; x < nA_t; x += kFuseBlock) {
+        const uint32_t ln = ao[x + 1] - ao[x];
+        sh.u.m.a_pfx[x] = load_be8(kbA, ao[x] - kadjA) & be_mask(ln < 8 ? ln : 8);
       }
-    } else if (d0 > 0) {
-      // The largest key before the partition: A[i0-1] unless it is the older
-      // copy of this very key (then A[i0-2]), or B[j0-1], whichever is larger.
-      // (With no survivor before the partition there is no such key.)
-      bool hA = false, hB = false;
-      KeyRef ka{0, 0}, kb{0, 0};
-      if (a_first >= 1) {
-        ka = KeyRef{sh.a_off[a_first - 1] - kadjA, sh.a_off[a_first] - sh.a_off[a_first - 1]};
-        hA = true;
-        if (cmp_keys(kbA, ka, xb, xk) == 0) {
-          hA = a_first >= 2;
-          if (hA) ka = KeyRef{sh.a_off[a_first - 2] - kadjA, sh.a_off[a_first - 1] - sh.a_off[a_first - 2]};
+      for (uint32_t y = tid; y < nbk; y += kFuseBlock) {
+        const uint32_t ln = bo[y + 1] - bo[y];
+        sh.u.m.b_pfx[y] = load_be8(kbB, bo[y] - kadjB) & be_mask(ln < 8 ? ln : 8);
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. merge (one output per thread) and keep-newer ----
+    uint32_t refs[1];
+    const uint32_t kept = merge_slice<1>(sh.a_off + a_first, sh.b_off + b_first, sh.u.m.a_pfx, sh.u.m.b_pfx,
+                                         kbA, kadjA, kbB, kadjB, tid, len, nA_t, nB_t, has_next_b, i0, A.n,
+                                         j0, refs);
+    uint32_t n_kept;
+    const uint32_t ord = block_exclusive_scan<uint32_t, kFuseBlock>(kept, sh.scan32, n_kept);
+    if (tid < len) {
+      const uint32_t ref = refs[0] & ~kDrop;
+      const bool drop = (refs[0] & kDrop) != 0;
+      if (ref < A.n)
+        sh.ords[ref - i0] = drop ? EM_NONE : ord;
+      else
+        sh.ords[nA_t + (ref - A.n - j0)] = ord;
+      if (!drop) sh.surv[ord] = ref;
+    }
+
+    // ---- 6. publish the survivor count early; the base is resolved later ----
+    if (tid == 0) lookback_publish(desc_s, tile, n_kept);
+    __syncthreads();
+
+    // ---- 7. this thread's survivor: key, value, predecessor, LCP ----
+    const bool has = tid < n_kept;
+    uint32_t kpos = 0, klen = 0, l = 0, kprev = 0, vpos = 0, vlen = 0;
+    bool isB = false, tomb = false;
+    if (has) {
+      const uint32_t ref = sh.surv[tid];
+      isB = ref >= A.n;
+      uint32_t ko, kend;
+      if (isB) {
+        const uint32_t y = ref - A.n - j0;
+        ko = sh.b_off[b_first + y] - kadjB;
+        kend = sh.b_off[b_first + y + 1] - kadjB;
+        tomb = sh.b_tomb[y] != 0;
+        vlen = tomb ? 0u : sh.b_voff[y + 1] - sh.b_voff[y];
+        vpos = sh.b_voff[y] - vadjB;
+      } else {
+        const uint32_t x = ref - i0;
+        ko = sh.a_off[a_first + x] - kadjA;
+        kend = sh.a_off[a_first + x + 1] - kadjA;
+        tomb = sh.a_tomb[x] != 0;
+        vlen = tomb ? 0u : sh.a_voff[x + 1] - sh.a_voff[x];
+        vpos = sh.a_voff[x] - vadjA;
+      }
+      kpos = ko;
+      klen = kend - ko;
+      const uint8_t* xb = isB ? kbB : kbA;
+      const KeyRef xk{ko, klen};
+      // predecessor survivor's key
+      bool have_p = false;
+      const uint8_t* pb = nullptr;
+      KeyRef pk{0, 0};
+      if (tid > 0) {
+        const uint32_t pref = sh.surv[tid - 1];
+        have_p = true;
+        if (pref >= A.n) {
+          const uint32_t y = pref - A.n - j0;
+          pb = kbB;
+          pk = KeyRef{sh.b_off[b_first + y] - kadjB, sh.b_off[b_first + y + 1] - sh.b_off[b_first + y]};
+        } else {
+          const uint32_t x = pref - i0;
+          pb = kbA;
+          pk = KeyRef{sh.a_off[a_first + x] - kadjA, sh.a_off[a_first + x + 1] - sh.a_off[a_first + x]};
+        }
+      } else if (d0 > 0) {
+        // The largest key before the partition: A[i0-1] unless it is the older
+        // copy of this very key (then A[i0-2]), or B[j0-1], whichever is larger.
+        // (With no survivor before the partition there is no such key.)
+        bool hA = false, hB = false;
+        KeyRef ka{0, 0}, kb{0, 0};
+        if (a_first >= 1) {
+          ka = KeyRef{sh.a_off[a_first - 1] - kadjA, sh.a_off[a_first] - sh.a_off[a_first - 1]};
+          hA = true;
+          if (cmp_keys(kbA, ka, xb, xk) == 0) {
+            hA = a_first >= 2;
+            if (hA) ka = KeyRef{sh.a_off[a_first - 2] - kadjA, sh.a_off[a_first - 1] - sh.a_off[a_first - 2]};
+          }
+        }
+        if (b_first >= 1) {
+          kb = KeyRef{sh.b_off[b_first - 1] - kadjB, sh.b_off[b_first] - sh.b_off[b_first - 1]};
+          hB = true;
+        }
+        if (hA && hB) {
+          const bool a_larger = cmp_keys(kbA, ka, kbB, kb) > 0;
+          pb = a_larger ? kbA : kbB;
+          pk = a_larger ? ka : kb;
+          have_p = true;
+        } else if (hA || hB) {
+          pb = hA ? kbA : kbB;
+          pk = hA ? ka : kb;
+          have_p = true;
         }
       }
-      if (b_first >= 1) {
-        kb = KeyRef{sh.b_off[b_first - 1] - kadjB, sh.b_off[b_first] - sh.b_off[b_first - 1]};
-        hB = true;
-      }
-      if (hA && hB) {
-        const bool a_larger = cmp_keys(kbA, ka, kbB, kb) > 0;
-        pb = a_larger ? kbA : kbB;
-        pk = a_larger ? ka : kb;
-        have_p = true;
-      } else if (hA || hB) {
-        pb = hA ? kbA : kbB;
-        pk = hA ? ka : kb;
-        have_p = true;
+      if (have_p) {
+        l = lcp_bits(pb, pk, xb, xk);
+        kprev = 8u * pk.len;
       }
     }
-    if (have_p) {
-      l = lcp_bits(pb, pk, xb, xk);
-      kprev = 8u * pk.len;
-    }
-  }
 
-  // ---- 8. survivor base (look-back 1), controls and exact lengths ----
-  if (tid < kWave) {
-    const uint64_t g = lookback_resolve(desc_s, tile, n_kept);
-    if (tid == 0) sh.g0 = static_cast<uint32_t>(g);
-  }
-  __syncthreads();
-  const uint32_t g0 = sh.g0;
-  if (out.final_refs)
-    for (uint32_t x = tid; x < n_kept; x += kFuseBlock) out.final_refs[g0 + x] = sh.surv[x];
-  if (out.ord_A)
-    for (uint32_t x = tid; x < nA_t; x += kFuseBlock) {
-      const uint32_t o = sh.ords[x];
-      out.ord_A[i0 + x] = o == EM_NONE ? EM_NONE : g0 + o;
-    }
-  if (out.ord_B)
-    for (uint32_t y = tid; y < nB_t; y += kFuseBlock) out.ord_B[j0 + y] = g0 + sh.ords[nA_t + y];
-  const uint32_t k = 8u * klen;
-  const uint32_t c = ((g0 + tid) % 15u == 0) ? 1u + l : kprev - l;
-  const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l), ev = eg0_len(vlen);
-  const uint32_t rb1 = e1, rb2 = rb1 + e2, rb3 = rb2 + (k - l), rb4 = rb3 + (tomb ? 1u : 1u + ev);
-  const uint32_t rb5 = rb4 + 8u * vlen;
-  const uint64_t rlen = has ? rb5 : 0u;
-
-  // ---- 9. local bit offsets; publish the bit total early ----
-  uint64_t tile_bits;
-  const uint64_t sb = block_exclusive_scan<uint64_t, kFuseBlock>(rlen, sh.scan64, tile_bits);
-  if (tid == 0) lookback_publish(desc_b, tile, tile_bits);
-
-  // ---- 10. emission: the local bit stream in window slices, stored shifted ----
-  // A single-slice partition builds its whole stream and publishes its tail
-  // before it resolves its bit base; a longer one resolves first.
-  const uint64_t nloc = (tile_bits + 31) >> 5;  // local words
-  const uint32_t nslices = nloc ? static_cast<uint32_t>((nloc + kFuseWin - 1) / kFuseWin) : 1u;
-  const bool early = nslices == 1;
-  if (!early) {
+    // ---- 8. survivor base (look-back 1), controls and exact lengths ----
     if (tid < kWave) {
-      const uint64_t b = lookback_resolve(desc_b, tile, tile_bits);
-      if (tid == 0) sh.b0 = b;
-    }
-  }
-  const bool last_tile = tile == P - 1;
-  const uint64_t vh = tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(vlen) + 1ull));
-  const uint32_t* kw = reinterpret_cast<const uint32_t*>(isB ? kbB : kbA);
-  const uint32_t* vw = reinterpret_cast<const uint32_t*>(isB ? vbB : vbA);
-  const uint64_t kbit = 8ull * kpos + l;
-  const uint64_t vbit = 8ull * vpos;
-  for (uint32_t sl = 0; sl < nslices; ++sl) {
-    const uint64_t w0 = static_cast<uint64_t>(sl) * kFuseWin;  // first local word of the slice
-    const uint64_t s0 = w0 << 5, s1 = min(s0 + 32ull * kFuseWin, tile_bits);
-    const uint32_t nz = static_cast<uint32_t>(min(static_cast<uint64_t>(kFuseWin), nloc - min(nloc, w0))) + 2;
-    for (uint32_t i = tid; i < nz; i += kFuseBlock) sh.u.win[i] = 0;
-    __syncthreads();
-    if (has && sb < s1 && sb + rlen > s0) {
-      const uint32_t from = sb >= s0 ? 0u : static_cast<uint32_t>(s0 - sb);
-      const uint32_t to = sb + rlen <= s1 ? rb5 : static_cast<uint32_t>(s1 - sb);
-      BitAppender ap;
-      ap.start(sh.u.win, static_cast<uint32_t>(sb + from - s0));
-      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
-        const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
-      };
-      auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
-        const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
-      };
-      imm(static_cast<uint64_t>(c) + 1u, 0, rb1);
-      imm(static_cast<uint64_t>(k - l) + 1u, rb1, rb2);
-      span(kw, kbit, rb2, rb3);
-      imm(vh, rb3, rb4);
-      span(vw, vbit, rb4, rb5);
-      ap.finish();
+      const uint64_t g = lookback_resolve(desc_s, tile, n_kept);
+      if (tid == 0) sh.g0 = static_cast<uint32_t>(g);
     }
     __syncthreads();
-    auto loc = [&](uint64_t w) -> uint32_t {  // local word w, for w in [w0 - 1, w0 + kFuseWin]
-      if (w + 1 == 0) return sh.prev_tail;     // w = -1: the bits before the partition
-      if (w < w0) return sh.carry;             // the previous slice's last word
-      return sh.u.win[w - w0];
-    };
-    if (sl == nslices - 1 && tid == 0) {
-      // publish this partition's tail: the last 32 bits of the stream up to its end
-      uint32_t tv, tn;
-      if (tile_bits >= 32) {
-        const uint64_t e = tile_bits - 32, ew = e >> 5;
-        const uint32_t r = static_cast<uint32_t>(e & 31u);
-        tv = r ? __builtin_amdgcn_alignbit(loc(ew), loc(ew + 1), 32u - r) : loc(ew);
-        tn = 32;
-      } else {
-        uint64_t pv = 0, pn = 0;
-        if (tile > 0) {
-          uint64_t t;
-          while (!((t = desc_load(tail + tile - 1)) & kTailReady)) __builtin_amdgcn_s_sleep(1);
-          pv = t & 0xFFFFFFFFu;
-          pn = (t >> 32) & 63u;
-        }
-        const uint32_t tb = static_cast<uint32_t>(tile_bits);
-        const uint64_t mine = tb ? (sh.u.win[0] >> (32u - tb)) : 0u;
-        tv = static_cast<uint32_t>((pv << tb) | mine);
-        tn = static_cast<uint32_t>(min(pn + tb, 32ull));
+    const uint32_t g0 = sh.g0;
+    if (out.final_refs)
+      for (uint32_t x = tid; x < n_kept; x += kFuseBlock) out.final_refs[g0 + x] = sh.surv[x];
+    if (out.ord_A)
+      for (uint32_t x = tid; x < nA_t; x += kFuseBlock) {
+        const uint32_t o = sh.ords[x];
+        out.ord_A[i0 + x] = o == EM_NONE ? EM_NONE : g0 + o;
       }
-      desc_store(tail + tile, kTailReady | (static_cast<uint64_t>(tn) << 32) | tv);
-    }
-    if (sl == 0) {
-      if (early && tid < kWave) {
+    if (out.ord_B)
+      for (uint32_t y = tid; y < nB_t; y += kFuseBlock) out.ord_B[j0 + y] = g0 + sh.ords[nA_t + y];
+    const uint32_t k = 8u * klen;
+    const uint32_t c = ((g0 + tid) % 15u == 0) ? 1u + l : kprev - l;
+    const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l), ev = eg0_len(vlen);
+    const uint32_t rb1 = e1, rb2 = rb1 + e2, rb3 = rb2 + (k - l), rb4 = rb3 + (tomb ? 1u : 1u + ev);
+    const uint32_t rb5 = rb4 + 8u * vlen;
+    const uint64_t rlen = has ? rb5 : 0u;
+
+    // ---- 9. local bit offsets; publish the bit total early ----
+    uint64_t tile_bits;
+    const uint64_t sb = block_exclusive_scan<uint64_t, kFuseBlock>(rlen, sh.scan64, tile_bits);
+    if (tid == 0) lookback_publish(desc_b, tile, tile_bits);
+
+    // ---- 10. emission: the local bit stream in window slices, stored shifted ----
+    // A single-slice partition builds its whole stream and publishes its tail
+    // before it resolves its bit base; a longer one resolves first.
+    const uint64_t nloc = (tile_bits + 31) >> 5;  // local words
+    const uint32_t nslices = nloc ? static_cast<uint32_t>((nloc + kFuseWin - 1) / kFuseWin) : 1u;
+    const bool early = nslices == 1;
+    if (!early) {
+      if (tid < kWave) {
         const uint64_t b = lookback_resolve(desc_b, tile, tile_bits);
         if (tid == 0) sh.b0 = b;
       }
-      if (tid == 0) {
-        uint32_t pt = 0;
-        if ((sh.b0 & 31u) && tile > 0) {  // this partition's first word starts with earlier bits
-          uint64_t t;
-          while (!((t = desc_load(tail + tile - 1)) & kTailReady)) __builtin_amdgcn_s_sleep(1);
-          pt = static_cast<uint32_t>(t);
-        }
-        sh.prev_tail = pt;
+    }
+    const bool last_tile = tile == P - 1;
+    const uint64_t vh = tomb ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(vlen) + 1ull));
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(isB ? kbB : kbA);
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(isB ? vbB : vbA);
+    const uint64_t kbit = 8ull * kpos + l;
+    const uint64_t vbit = 8ull * vpos;
+    for (uint32_t sl = 0; sl < nslices; ++sl) {
+      const uint64_t w0 = static_cast<uint64_t>(sl) * kFuseWin;  // first local word of the slice
+      const uint64_t s0 = w0 << 5, s1 = min(s0 + 32ull * kFuseWin, tile_bits);
+      const uint32_t nz =
+          static_cast<uint32_t>(min(static_cast<uint64_t>(kFuseWin), nloc - min(nloc, w0))) + 2;
+      for (uint32_t i = tid; i < nz; i += kFuseBlock) sh.u.win[i] = 0;
+      __syncthreads();
+      if (has && sb < s1 && sb + rlen > s0) {
+        const uint32_t from = sb >= s0 ? 0u : static_cast<uint32_t>(s0 - sb);
+        const uint32_t to = sb + rlen <= s1 ? rb5 : static_cast<uint32_t>(s1 - sb);
+        BitAppender ap;
+        ap.start(sh.u.win, static_cast<uint32_t>(sb + from - s0));
+        auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
+          const uint32_t lo = max(a, from), hi = min(b, to);
+          if (lo < hi)
+            ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
+        };
+        auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
+          const uint32_t lo = max(a, from), hi = min(b, to);
+          if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
+        };
+        imm(static_cast<uint64_t>(c) + 1u, 0, rb1);
+        imm(static_cast<uint64_t>(k - l) + 1u, rb1, rb2);
+        span(kw, kbit, rb2, rb3);
+        imm(vh, rb3, rb4);
+        span(vw, vbit, rb4, rb5);
+        ap.finish();
       }
+      __syncthreads();
+      auto loc = [&](uint64_t w) -> uint32_t {  // local word w, for w in [w0 - 1, w0 + kFuseWin]
+        if (w + 1 == 0) return sh.prev_tail;     // w = -1: the bits before the partition
+        if (w < w0) return sh.carry;             // the previous slice's last word
+        return sh.u.win[w - w0];
+      };
+      if (sl == nslices - 1 && tid == 0) {
+        // publish this partition's tail: the last 32 bits of the stream up to its end
+        uint32_t tv, tn;
+        if (tile_bits >= 32) {
+          const uint64_t e = tile_bits - 32, ew = e >> 5;
+          const uint32_t r = static_cast<uint32_t>(e & 31u);
+          tv = r ? __builtin_amdgcn_alignbit(loc(ew), loc(ew + 1), 32u - r) : loc(ew);
+          tn = 32;
+        } else {
+          uint64_t pv = 0, pn = 0;
+          if (tile > 0) {
+            uint64_t t;
+            while (!((t = desc_load(tail + tile - 1)) & kTailReady)) __builtin_amdgcn_s_sleep(1);
+            pv = t & 0xFFFFFFFFu;
+            pn = (t >> 32) & 63u;
+          }
+          const uint32_t tb = static_cast<uint32_t>(tile_bits);
+          const uint64_t mine = tb ? (sh.u.win[0] >> (32u - tb)) : 0u;
+          tv = static_cast<uint32_t>((pv << tb) | mine);
+          tn = static_cast<uint32_t>(min(pn + tb, 32ull));
+        }
+        desc_store(tail + tile, kTailReady | (static_cast<uint64_t>(tn) << 32) | tv);
+      }
+      if (sl == 0) {
+        if (early && tid < kWave) {
+          const uint64_t b = lookback_resolve(desc_b, tile, tile_bits);
+          if (tid == 0) sh.b0 = b;
+        }
+        if (tid == 0) {
+          uint32_t pt = 0;
+          if ((sh.b0 & 31u) && tile > 0) {  // this partition's first word starts with earlier bits
+            uint64_t t;
+            while (!((t = desc_load(tail + tile - 1)) & kTailReady)) __builtin_amdgcn_s_sleep(1);
+            pt = static_cast<uint32_t>(t);
+          }
+          sh.prev_tail = pt;
+        }
+      }
+      __syncthreads();
+      // owned words (a word belongs to the partition holding its last bit)
+      const uint64_t b0 = sh.b0;
+      const uint32_t s_sh = static_cast<uint32_t>(b0 & 31u);
+      const uint64_t q = b0 >> 5;
+      const uint64_t b_end = b0 + tile_bits;
+      const uint64_t g_hi = (b_end >> 5) + ((last_tile && (b_end & 31u)) ? 1u : 0u);
+      const uint64_t ga = q + w0, gb = min(g_hi, q + w0 + kFuseWin);
+      for (uint64_t g = ga + tid; g < gb; g += kFuseBlock) {
+        const uint64_t li = g - q;  // local word holding the word's last bits
+        const uint32_t lo_w = loc(li);
+        const uint32_t hi_w = s_sh ? loc(li - 1) : 0u;
+        out.payload[g] = __builtin_bswap32(s_sh ? __builtin_amdgcn_alignbit(hi_w, lo_w, s_sh) : lo_w);
+      }
+      __syncthreads();
+      if (tid == 0) sh.carry = sh.u.win[kFuseWin - 1];
+      __syncthreads();
     }
-    __syncthreads();
-    // owned words (a word belongs to the partition holding its last bit)
     const uint64_t b0 = sh.b0;
-    const uint32_t s_sh = static_cast<uint32_t>(b0 & 31u);
-    const uint64_t q = b0 >> 5;
-    const uint64_t b_end = b0 + tile_bits;
-    const uint64_t g_hi = (b_end >> 5) + ((last_tile && (b_end & 31u)) ? 1u : 0u);
-    const uint64_t ga = q + w0, gb = min(g_hi, q + w0 + kFuseWin);
-    for (uint64_t g = ga + tid; g < gb; g += kFuseBlock) {
-      const uint64_t li = g - q;  // local word holding the word's last bits
-      const uint32_t lo_w = loc(li);
-      const uint32_t hi_w = s_sh ? loc(li - 1) : 0u;
-      out.payload[g] = __builtin_bswap32(s_sh ? __builtin_amdgcn_alignbit(hi_w, lo_w, s_sh) : lo_w);
+    if (has) {
+      if (out.len_bits) out.len_bits[g0 + tid] = static_cast<uint32_t>(rlen);
+      if (out.lcp_bits) out.lcp_bits[g0 + tid] = l;
+      if (out.off) out.off[g0 + tid] = b0 + sb;
     }
-    __syncthreads();
-    if (tid == 0) sh.carry = sh.u.win[kFuseWin - 1];
-    __syncthreads();
-  }
-  const uint64_t b0 = sh.b0;
-  if (has) {
-    if (out.len_bits) out.len_bits[g0 + tid] = static_cast<uint32_t>(rlen);
-    if (out.lcp_bits) out.lcp_bits[g0 + tid] = l;
-    if (out.off) out.off[g0 + tid] = b0 + sb;
-  }
-  if (last_tile && tid == 0) {
-    out.d_S[0] = g0 + n_kept;
-    out.d_T[0] = b0 + tile_bits;
-    if (out.off) out.off[g0 + n_kept] = b0 + tile_bits;
-  }
+    if (last_tile && tid == 0) {
+      out.d_S[0] = g0 + n_kept;
+      out.d_T[0] = b0 + tile_bits;
+      if (out.off) out.off[g0 + n_kept] = b0 + tile_bits;
+    }
+  };
+  if (staged)
+    rest(std::true_type{});
+  else
+    rest(std::false_type{});
 }
 
 size_t fused_ws(uint32_t N, uint32_t items) {

@@ -49,6 +49,13 @@ __device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, 
 // (base, position - lo + at) per side: the LDS copy when staged, the arenas
 // otherwise.  Returns the kept count; refs[] get the merged references with
 // kDrop on a replaced A.
+//
+// Most comparisons are settled by the 8-byte prefixes and the lengths.  The
+// rest (equal prefixes, both keys longer than 8 bytes: above all an A key and
+// its replacing B key) need the suffixes.  A lane that meets one parks it;
+// the other lanes keep stepping, and the parked comparisons of the whole wave
+// are then done together, so a wave pays about one suffix comparison per
+// lane instead of one per step at which any of its lanes ties.
 template <int IPT>
 __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
                                                 const uint64_t* a_pfx, const uint64_t* b_pfx,
@@ -59,53 +66,124 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
                                                 uint32_t j0, uint32_t (&refs)[IPT]) {
   // Prefix first; zero padding plus the lengths keep proper-prefix order exact
   // (Everett, "GPU construction experiment", prefix-cache paragraph).
-  auto cmpAB = [&](uint32_t a, uint32_t b) -> int {
+  // Returns false when the suffixes must decide.
+  auto quick = [&](uint32_t a, uint32_t b, int& c) -> bool {
     const uint64_t pa = a_pfx[a], pb = b_pfx[b];
-    if (pa != pb) return pa < pb ? -1 : 1;
+    if (pa != pb) {
+      c = pa < pb ? -1 : 1;
+      return true;
+    }
     const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
-    if (la <= 8 || lb <= 8) return (la > lb) - (la < lb);
-    return cmp_keys(abase, KeyRef{a_off[a] - a_adj + 8, la - 8}, bbase, KeyRef{b_off[b] - b_adj + 8, lb - 8});
+    c = (la > lb) - (la < lb);
+    return la <= 8 || lb <= 8;
   };
-  uint32_t kept = 0;
+  auto suffix = [&](uint32_t a, uint32_t b) -> int {
+    const uint32_t pa = a_off[a], pb = b_off[b];
+    return cmp_keys(abase, KeyRef{pa - a_adj + 8, a_off[a + 1] - pa - 8}, bbase,
+                    KeyRef{pb - b_adj + 8, b_off[b + 1] - pb - 8});
+  };
 #pragma unroll
   for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
   if (k >= len) return 0;
+
+  // co-rank of diagonal k inside the partition: the largest a with
+  // A[a-1] <= B[k-a] (A first on equal keys)
   uint32_t lo = k > nB_t ? k - nB_t : 0;
   uint32_t hi = k < nA_t ? k : nA_t;
-  while (lo < hi) {
-    const uint32_t mid = (lo + hi + 1) >> 1;
-    const uint32_t j = k - mid;
-    const bool too_big = j < nB_t && cmpAB(mid - 1, j) > 0;
-    if (too_big)
-      hi = mid - 1;
-    else
-      lo = mid;
+  for (;;) {
+    bool park = false;
+    uint32_t pmid = 0;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      const uint32_t j = k - mid;
+      int c = -1;
+      if (j < nB_t && !quick(mid - 1, j, c)) {
+        park = true;
+        pmid = mid;
+        break;
+      }
+      if (c > 0)
+        hi = mid - 1;
+      else
+        lo = mid;
+    }
+    if (__ballot(park) == 0) break;
+    if (park) {
+      if (suffix(pmid - 1, k - pmid) > 0)
+        hi = pmid - 1;
+      else
+        lo = pmid;
+    }
   }
-  uint32_t a = lo, b = k - lo;
-#pragma unroll
-  for (int s = 0; s < IPT; ++s) {
-    if (k + s < len) {
+
+  // the thread's IPT outputs, recorded as bit masks (bit s: output s is an A,
+  // and whether that A is replaced) so that parking needs no dynamic index
+  // into refs[]
+  const uint32_t a0 = lo, b0 = k - lo;
+  const uint32_t n = len - k < static_cast<uint32_t>(IPT) ? len - k : static_cast<uint32_t>(IPT);
+  uint32_t a = a0, b = b0, s = 0, amask = 0, dmask = 0;
+  for (;;) {
+    bool park = false, boundary = false;
+    while (s < n) {
       int c;
       if (a < nA_t && b < nB_t) {
-        c = cmpAB(a, b);
+        if (!quick(a, b, c)) {
+          park = true;
+          break;
+        }
       } else if (a < nA_t) {
         // B exhausted inside the partition: only the partition's last A can
         // equal the next partition's first B.
-        c = (a == nA_t - 1 && has_next_b && cmpAB(a, nB_t) == 0) ? 0 : -1;
+        c = -1;
+        if (a == nA_t - 1 && has_next_b) {
+          int e;
+          if (!quick(a, nB_t, e)) {
+            park = boundary = true;
+            break;
+          }
+          if (e == 0) c = 0;
+        }
       } else {
         c = 1;
       }
       if (c <= 0) {
-        refs[s] = (i0 + a) | (c == 0 ? kDrop : 0u);
+        amask |= 1u << s;
+        if (c == 0) dmask |= 1u << s;
         ++a;
       } else {
-        refs[s] = nA_all + j0 + b;
         ++b;
       }
-      kept += c != 0;
+      ++s;
+    }
+    if (__ballot(park) == 0) break;
+    if (park) {
+      int c = suffix(a, boundary ? nB_t : b);
+      if (boundary) c = c == 0 ? 0 : -1;
+      if (c <= 0) {
+        amask |= 1u << s;
+        if (c == 0) dmask |= 1u << s;
+        ++a;
+      } else {
+        ++b;
+      }
+      ++s;
     }
   }
-  return kept;
+  a = a0;
+  b = b0;
+#pragma unroll
+  for (int t = 0; t < IPT; ++t) {
+    if (static_cast<uint32_t>(t) < n) {
+      if ((amask >> t) & 1u) {
+        refs[t] = (i0 + a) | (((dmask >> t) & 1u) ? kDrop : 0u);
+        ++a;
+      } else {
+        refs[t] = nA_all + j0 + b;
+        ++b;
+      }
+    }
+  }
+  return n - static_cast<uint32_t>(__builtin_popcount(dmask));
 }
 
 // Appends bits MSB-first at consecutive output positions inside the current
