@@ -8,7 +8,9 @@
 // arrays in parallel": each worker starts from its own co-rank and takes
 // exactly as many steps as its slice is long.
 //
-// gfx950 design (one workgroup = one partition of `items_per_part` outputs):
+// gfx950 design (one 512-thread workgroup = one partition of `items_per_part`
+// outputs; eight waves per partition keep the merge's dependent LDS steps
+// overlapped):
 //  * the partition's A and B key offsets are staged in LDS once;
 //  * each thread finds its slice's co-rank inside the partition by bisection
 //    on the staged offsets and merges IPT outputs; the comparison that decides
@@ -25,13 +27,13 @@
 
 namespace em {
 
-constexpr int kMergeBlock = 256;
+constexpr int kMergeBlock = 512;
 
 // LDS for a partition's key bytes; the compaction arrays reuse it after the merge.
 // (a multiple of 1 KB: LDS-DMA fills it 64 chunks of 16 bytes at a time)
 template <int IPT>
 constexpr uint32_t merge_key_cap() {
-  return IPT <= 1 ? 13u * 1024 : IPT == 2 ? 26u * 1024 : IPT == 4 ? 44u * 1024 : 60u * 1024;
+  return IPT <= 1 ? 26u * 1024 : IPT == 2 ? 48u * 1024 : IPT == 4 ? 60u * 1024 : 32u * 1024;
 }
 
 template <int IPT>
@@ -242,9 +244,7 @@ extern "C" int em_merge_keep(const em_side_t* A, const em_side_t* B, const uint3
     launch_merge<2>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);
   else if (ipt <= 4)
     launch_merge<4>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);
-  else if (ipt <= 8)
-    launch_merge<8>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);
   else
-    launch_merge<16>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);
+    launch_merge<8>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);
   return check_launch();
 }

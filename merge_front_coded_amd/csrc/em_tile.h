@@ -45,10 +45,10 @@ __device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, 
   return tomb ? 1u : 1u + eg0_len(vlen) + 8u * vlen;
 }
 
-// Merges this thread's slice of the partition.  Keys are read through
-// (base, position - lo + at) per side: the LDS copy when staged, the arenas
-// otherwise.  Returns the kept count; refs[] get the merged references with
-// kDrop on a replaced A.
+// Merges this thread's slice of the partition exactly.  Keys are read
+// through (base, position - lo + at) per side: the LDS copy when staged, the
+// arenas otherwise.  Returns the kept count; refs[] get the merged references
+// with kDrop on a replaced A.
 //
 // Most comparisons are settled by the 8-byte prefixes and the lengths.  The
 // rest (equal prefixes, both keys longer than 8 bytes: above all an A key and
@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, 
 // are then done together, so a wave pays about one suffix comparison per
 // lane instead of one per step at which any of its lanes ties.
 template <int IPT>
-__device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
+__device__ __forceinline__ uint32_t merge_slice_exact(const uint32_t* a_off, const uint32_t* b_off,
                                                 const uint64_t* a_pfx, const uint64_t* b_pfx,
                                                 const uint8_t* abase, uint32_t a_adj,
                                                 const uint8_t* bbase, uint32_t b_adj, uint32_t k,
@@ -184,6 +184,119 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
     }
   }
   return n - static_cast<uint32_t>(__builtin_popcount(dmask));
+}
+
+// The same merge with a fixed-step search and no suffix reads on the way.
+// A comparison the prefixes and lengths leave open between two keys of equal
+// length is taken as "equal" and the pair is noted; once the slice is merged
+// every noted pair is compared in full (the whole wave at once).  If all of
+// them are equal, every comparison the merge made was exact and so is its
+// result; otherwise, or when a pair of different lengths is left open, `bad`
+// is set and the caller redoes the partition with merge_slice_exact.
+template <int IPT>
+__device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, const uint32_t* b_off,
+                                                     const uint64_t* a_pfx, const uint64_t* b_pfx,
+                                                     const uint8_t* abase, uint32_t a_adj,
+                                                     const uint8_t* bbase, uint32_t b_adj, uint32_t k,
+                                                     uint32_t len, uint32_t nA_t, uint32_t nB_t,
+                                                     bool has_next_b, uint32_t i0, uint32_t nA_all,
+                                                     uint32_t j0, uint32_t (&refs)[IPT], bool& bad) {
+  constexpr int kNotes = 4;
+  uint32_t note[kNotes];  // noted pairs, A index | B index << 16
+#pragma unroll
+  for (int q = 0; q < kNotes; ++q) note[q] = 0;
+  uint32_t nnote = 0;
+  bool open_pair = false;
+  // c: -1, 0 or 1; a pair left open counts as 0 and is noted when `use`
+  // (written with selects only: the search runs every step in every lane)
+  auto cmp = [&](uint32_t a, uint32_t b, bool use) -> int {
+    const uint64_t pa = a_pfx[a], pb = b_pfx[b];
+    const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
+    const bool peq = pa == pb;
+    const int cp = pa < pb ? -1 : 1;
+    const int cl = (la > lb) - (la < lb);
+    const bool open = use & peq & (la > 8u) & (lb > 8u);
+    open_pair |= open & (la != lb);
+    const uint32_t v = a | (b << 16);
+#pragma unroll
+    for (int q = 0; q < kNotes; ++q) note[q] = (open & (nnote == static_cast<uint32_t>(q))) ? v : note[q];
+    nnote += open ? 1u : 0u;
+    return open ? 0 : (peq ? cl : cp);
+  };
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
+  bad = false;
+  if (k >= len) return 0;
+
+  // co-rank of diagonal k: the largest a in [lo, hi] with A[a-1] <= B[k-a],
+  // by binary lifting over the same number of steps in every lane
+  const uint32_t lo = k > nB_t ? k - nB_t : 0;
+  const uint32_t hi = k < nA_t ? k : nA_t;
+  uint32_t a = lo;
+  for (uint32_t step = 1u << (31 - __builtin_clz(len)); step; step >>= 1) {
+    const uint32_t m = a + step;
+    const uint32_t j = k - m;
+    const bool in = m <= hi;                  // then m <= k, so j did not wrap
+    const bool probe = in && j < nB_t;        // B exhausted: A[m-1] is not too large
+    const int c = cmp(probe ? m - 1 : 0u, probe ? j : 0u, probe);
+    a = (in && !(probe && c > 0)) ? m : a;
+  }
+
+  uint32_t b = k - a;
+  uint32_t kept = 0;
+#pragma unroll
+  for (int s = 0; s < IPT; ++s) {
+    const bool live = k + s < len;
+    const bool both = a < nA_t && b < nB_t;
+    // B exhausted inside the partition: only the partition's last A can equal
+    // the next partition's first B
+    const bool edge = !both && a < nA_t && a + 1 == nA_t && has_next_b;
+    const bool use = live && (both || edge);
+    const int e = cmp(use ? a : 0u, both ? b : (use ? nB_t : 0u), use);
+    const int c = both ? e : a < nA_t ? ((edge && e == 0) ? 0 : -1) : 1;
+    if (live) {
+      refs[s] = c <= 0 ? ((i0 + a) | (c == 0 ? kDrop : 0u)) : nA_all + j0 + b;
+      kept += c != 0;
+    }
+    a += (live && c <= 0) ? 1u : 0u;
+    b += (live && c > 0) ? 1u : 0u;
+  }
+
+  // check the pairs taken as equal, the whole wave together
+  bool ok = !open_pair && nnote <= static_cast<uint32_t>(kNotes);
+  if (__ballot(nnote != 0) != 0) {
+#pragma unroll
+    for (int q = 0; q < kNotes; ++q) {
+      if (ok && static_cast<uint32_t>(q) < nnote) {
+        const uint32_t x = note[q] & 0xFFFFu, y = note[q] >> 16;
+        const uint32_t px = a_off[x], py = b_off[y];
+        ok = cmp_keys(abase, KeyRef{px - a_adj + 8, a_off[x + 1] - px - 8}, bbase,
+                      KeyRef{py - b_adj + 8, b_off[y + 1] - py - 8}) == 0;
+      }
+    }
+  }
+  bad = !ok;
+  return kept;
+}
+
+// The merge of a workgroup's partition: every thread calls it (threads past
+// the partition's end get kDrop refs and a zero count).  Exact whichever
+// branch runs.
+template <int IPT>
+__device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
+                                                const uint64_t* a_pfx, const uint64_t* b_pfx,
+                                                const uint8_t* abase, uint32_t a_adj,
+                                                const uint8_t* bbase, uint32_t b_adj, uint32_t k,
+                                                uint32_t len, uint32_t nA_t, uint32_t nB_t,
+                                                bool has_next_b, uint32_t i0, uint32_t nA_all,
+                                                uint32_t j0, uint32_t (&refs)[IPT]) {
+  bool bad;
+  uint32_t kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len,
+                                        nA_t, nB_t, has_next_b, i0, nA_all, j0, refs, bad);
+  if (__syncthreads_or(bad))
+    kept = merge_slice_exact<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
+                                  nB_t, has_next_b, i0, nA_all, j0, refs);
+  return kept;
 }
 
 // Appends bits MSB-first at consecutive output positions inside the current

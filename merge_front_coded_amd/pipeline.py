@@ -16,8 +16,8 @@ import torch
 from . import binding as em
 
 
-# LDS bytes for a partition's keys in the merge kernel, by outputs per thread
-_KEY_CAP = {1: 13 * 1024, 2: 26 * 1024, 4: 44 * 1024, 8: 60 * 1024, 16: 60 * 1024}
+# staged key bytes of one merge partition, by partition size (em_merge_keep.hip)
+_KEY_CAP = {256: 26 * 1024, 512: 26 * 1024, 1024: 48 * 1024, 2048: 60 * 1024, 4096: 32 * 1024}
 
 
 def choose_items_per_part(A: em.DeviceSide, B: em.DeviceSide) -> int:
@@ -27,7 +27,7 @@ def choose_items_per_part(A: em.DeviceSide, B: em.DeviceSide) -> int:
     mean = (A.key_bytes + B.key_bytes) / n if n else 0.0
     best = 256
     for items in (256, 512, 1024, 2048, 4096):
-        if items * (mean * 1.1 + 4) <= _KEY_CAP[items // 256]:
+        if items * (mean * 1.1 + 4) <= _KEY_CAP[items]:
             best = items
     return best
 
