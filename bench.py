@@ -4,8 +4,9 @@ MI355X, on the 8M+8M base64-key workload (or another named workload).
 
 One step is one pass of the whole hot path over inputs already resident in
 HBM.  Paths:
-  fused (default)  em_partition (coarse) + em_merge_fc: co-rank, merge,
-                   keep-newer, lengths, bit offsets and emission in one kernel
+  fused (default)  em_partition, em_merge_lengths (co-rank, merge, keep-newer,
+                   LCPs, lengths, bit offsets), em_emit_merged (emission); no
+                   host read inside a step
   merge            em_partition, em_merge_keep, host read of S, em_fc_lengths,
                    em_scan, host read of T, em_emit
   collision        em_collision_rank in place of partition + merge_keep
@@ -34,13 +35,20 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "merged records/s and pipeline GB/s (% of HBM peak) at 8M+8M string keys, 1 GPU"
 
 
+# the kernel each timed call launches (em_merge_lengths also runs a one-workgroup
+# scan of partition totals, about 1% of its time)
+KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em_fc_lengths": "k_fc_lengths",
+             "em_scan": "k_scan", "em_emit": "k_emit", "em_collision_rank": "k_collision (5 kernels)",
+             "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
-    ap.add_argument("--path", choices=("fused", "merge", "collision"), default="merge")
+    ap.add_argument("--path", choices=("fused", "merge", "collision"), default="fused")
     ap.add_argument("--items", type=int, default=0,
                     help="outputs per merge partition (0: chosen from the mean key length)")
     ap.add_argument("--coarse-parts", type=int, default=0,
@@ -80,6 +88,7 @@ def algorithmic_bytes(Ah, Bh, pl, path):
     value_bytes = int(np.sum(vlen))
     payload = 4 * ((T + 31) // 32)
     per_rec_meta = 4 + 8 + 4 + 8 + 8 + 1  # final, off, lcp, key_off pair, val_off pair, tomb
+    vmeta = 4 * (Ah.n + 1 + Bh.n + 1) + int(Ah.tomb.size + Bh.tomb.size)  # value offsets, tombstones
     out = {
         # merge: every key byte, both offset arrays; writes refs and both ordinal arrays
         "em_merge_keep": keys + offs + 4 * S + 4 * N,
@@ -91,6 +100,12 @@ def algorithmic_bytes(Ah, Bh, pl, path):
         "em_collision_rank": keys + offs + 4 * S + 4 * N,
         # the whole path: every input byte once, the payload once
         "em_merge_fc": side_bytes(Ah) + side_bytes(Bh) + payload,
+        # merge, keep, LCPs, lengths: every key byte, key and value offsets,
+        # tombstones; writes refs, LCPs and partition-form offsets
+        "em_merge_lengths": keys + offs + vmeta + 16 * S,
+        # emission: refs, LCPs, offsets (16 B), key_off and val_off pairs,
+        # tombstone, key suffixes, values; writes the payload
+        "em_emit_merged": S * (16 + 8 + 8 + 1) + suffix_bytes + value_bytes + payload,
     }
     return out
 
@@ -148,7 +163,7 @@ def main():
     stream = torch.cuda.current_stream()
     calls = {"merge": ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"],
              "collision": ["em_collision_rank", "em_fc_lengths", "em_scan", "em_emit"],
-             "fused": ["em_partition", "em_merge_fc"]}[args.path]
+             "fused": ["em_partition", "em_merge_lengths", "em_emit_merged"]}[args.path]
     ev = {c: [] for c in calls}
     orig = {c: getattr(em.pipeline.em, c) for c in calls}
 
@@ -223,7 +238,8 @@ def main():
         "survivors_per_s": pl.S / (ms_per_step * 1e-3),
         "wall_s_timed": wall,
         "per_call_ms": per_call_ms,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dominant], "call": dominant, "achieved": ach,
+                     "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_ms": per_call_ms[dominant]},

@@ -179,21 +179,46 @@ int em_emit(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs,
             uint64_t payload_words, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The whole path in one pass (Everett, "GPU construction experiment": merge
+ * First half of the whole path (Everett, "GPU construction experiment": merge
  * by diagonal partitions, keep-newer, exact lengths, one global scan of bit
- * offsets, word-owned MSB-first emission).  One workgroup per partition of
- * items_per_part (1..256) merged outputs finds its co-ranks inside the coarse
- * partition given by coarse_splits (em_partition's output for
- * coarse_items, a multiple of items_per_part), merges, keeps the newer
- * record, computes LCPs and exact lengths, takes its survivor and bit bases
- * from two decoupled look-backs, and stores its payload words once (a word
- * belongs to the partition holding its last bit).  Writes:
- *   payload[ceil(T/32)]  same bits as em_emit; payload_words is the capacity
- *                        and must cover em_payload_bound_bits;
- *   d_S[0] (u32), d_T[0] (u64)  survivor count and payload bits (device);
- *   final_refs, ord_A, ord_B, len_bits, lcp_bits, off: optional (nullable),
- *                        the same arrays the separate calls produce.
- * Nothing has to be read by the host between steps.
+ * offsets).  One workgroup per partition of items_per_part (1..2048) merged
+ * outputs finds its co-ranks inside the coarse partition given by
+ * coarse_splits (em_partition's output for coarse_items, a multiple of
+ * items_per_part; read directly when coarse_items == items_per_part),
+ * merges, keeps the newer record, and computes LCPs, exact lengths and
+ * partition-local bit offsets, taking its survivor base from a decoupled
+ * look-back; one workgroup then scans the partitions' bit totals.  Writes
+ * d_S[0] (u32) and d_T[0] (u64), the optional (nullable) per-record arrays
+ * final_refs, ord_A, ord_B, len_bits, lcp_bits of the separate calls, and,
+ * in the workspace, what em_emit_merged reads (record offsets in partition
+ * form, partition bit bases; final_refs and lcp_bits when those are NULL).
+ * The workspace (em_merge_fc_workspace_bytes, 256-byte aligned) is about 16
+ * bytes per record.
+ */
+int em_merge_lengths(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_splits,
+                     uint32_t coarse_items, uint32_t items_per_part, uint32_t *d_S, uint64_t *d_T,
+                     uint32_t *final_refs, uint32_t *ord_A, uint32_t *ord_B, uint32_t *len_bits,
+                     uint32_t *lcp_bits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Second half: word-owned emission (as em_emit) after em_merge_lengths on the
+ * same stream, with the same A, B, items_per_part, workspace, final_refs and
+ * lcp_bits (NULL where em_merge_lengths got NULL).  Reads S and T from d_S and
+ * d_T; a fixed grid of resident workgroups walks the records.  Writes
+ * payload[ceil(T/32)] (payload_words is the capacity and must cover
+ * em_payload_bound_bits; 16-byte aligned) and, when off is not NULL, the S+1
+ * bit offsets of em_scan.  Nothing has to be read by the host in between.
+ */
+int em_emit_merged(const em_side_t *A, const em_side_t *B, uint32_t items_per_part, uint32_t *payload,
+                   uint64_t payload_words, const uint32_t *d_S, const uint64_t *d_T,
+                   const uint32_t *final_refs, const uint32_t *lcp_bits, uint64_t *off, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * The whole path in one call: em_merge_lengths then em_emit_merged, with the
+ * same arguments (every argument is checked before anything is enqueued).
+ * Writes the payload, d_S, d_T and the optional (nullable) per-record arrays
+ * final_refs, ord_A, ord_B, len_bits, lcp_bits, off of the separate calls.
  */
 size_t em_merge_fc_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t items_per_part);
 int em_merge_fc(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_splits,

@@ -145,14 +145,51 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
   }
 }
 
-__global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
-                                                     const uint32_t* __restrict__ final_refs,
-                                                     const uint32_t* __restrict__ lcp_in, uint32_t S,
-                                                     const uint64_t* __restrict__ off, uint64_t T,
-                                                     uint32_t* __restrict__ payload, uint32_t rpb) {
-  __shared__ EmitShared sh;
+// Record offsets: off[r] directly (kTiled = false), or a partition number
+// above bit kTiledShift plus a partition-local offset, to which the
+// partition's bit base tbase[] is added (kTiled = true; off_out, when given,
+// then receives the offsets of the owned records and T).
+
+// The first loads of a thread's record: its reference, the offsets of its
+// start and end, its LCP.  A workgroup that walks several chunks loads these
+// for its next chunk while it works on the current one.
+struct RecPre {
+  uint32_t ref, lcp;
+  uint64_t o0, o1;
+  uint32_t pref;  // thread 0: the reference of the record before the chunk
+};
+
+template <bool kTiled, bool kLcp>
+__device__ __forceinline__ RecPre load_rec_pre(const uint32_t* __restrict__ final_refs,
+                                               const uint32_t* __restrict__ lcp_in,
+                                               const uint64_t* __restrict__ off, uint32_t S, uint32_t R0,
+                                               uint32_t rpb) {
+  RecPre p{0, 0, 0, 0, 0};
+  const uint32_t j = threadIdx.x;
+  if (j == 0 && R0 > 0 && R0 < S) p.pref = final_refs[R0 - 1];
+  const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
+  if (R0 < S && j < cnt) {
+    const uint32_t r = R0 + j;
+    p.ref = final_refs[r];
+    p.o0 = off[r];
+    p.o1 = (kTiled && r + 1 == S) ? p.o0 : off[r + 1];
+    p.lcp = kLcp ? lcp_in[r] : 0u;
+  }
+  return p;
+}
+
+// One workgroup's records [R0, R0 + rpb) (and up to kEmitExtra after them).
+// kLcp: LCPs come from lcp_in (else they are recomputed from the keys).
+template <bool kTiled, bool kLcp>
+__device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, const em_side_t& B,
+                                           const uint32_t* __restrict__ final_refs,
+                                           const uint32_t* __restrict__ lcp_in, uint32_t S,
+                                           const uint64_t* __restrict__ off,
+                                           const uint64_t* __restrict__ tbase,
+                                           uint64_t* __restrict__ off_out, uint64_t T,
+                                           uint32_t* __restrict__ payload, uint32_t R0, uint32_t rpb,
+                                           const RecPre& pre) {
   const uint32_t tid = threadIdx.x;
-  const uint32_t R0 = blockIdx.x * rpb;
   const uint32_t nown = (S - R0) < rpb ? S - R0 : rpb;
   const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
   if (tid < 4) {
@@ -169,26 +206,42 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
   uint64_t rec_off = 0, rec_end = 0;
   if (active) {
     const uint32_t r = R0 + j;
-    const uint32_t ref = final_refs[r];
-    rec_off = off[r];
-    rec_end = off[r + 1];
-    const uint32_t lin = lcp_in ? lcp_in[r] : 0u;
+    const bool last = r + 1 == S;
+    const uint32_t ref = pre.ref;
+    // every load of this record's fields is issued before any is used
+    uint64_t b0 = 0, b1 = 0;
+    if (kTiled) {
+      b0 = tbase[pre.o0 >> kTiledShift];
+      b1 = tbase[pre.o1 >> kTiledShift];
+    }
     uint32_t idx;
     const SideView s = pick(A, B, ref, idx);
     const KeyRef x = key_of(s, idx);
-    if (lcp_in) {
-      l = min(lin, 8u * x.len);  // a stale array must not send reads past the key
+    bool t;
+    value_bits(s, idx, vlen, t, &vpos);
+    if (j == 0) {
+      // the key length of the record before the chunk (for c of its first record)
+      uint32_t kp = 0;
+      if (R0 > 0) {
+        uint32_t pidx;
+        const SideView ps = pick(A, B, pre.pref, pidx);
+        kp = 8u * (ps.key_off[pidx + 1] - ps.key_off[pidx]);
+      }
+      sh.kprev0 = kp;
+    }
+    if (kLcp) {
+      l = min(pre.lcp, 8u * x.len);  // a stale array must not send reads past the key
     } else if (r > 0) {
       uint32_t pidx;
       const SideView ps = pick(A, B, final_refs[r - 1], pidx);
       l = lcp_bits(ps.keys, key_of(ps, pidx), s.keys, x);
     }
-    bool t;
-    value_bits(s, idx, vlen, t);
+    constexpr uint64_t kLocal = (1ull << kTiledShift) - 1;
+    rec_off = kTiled ? b0 + (pre.o0 & kLocal) : pre.o0;
+    rec_end = kTiled ? (last ? T : b1 + (pre.o1 & kLocal)) : pre.o1;
     tomb = t;
     kpos = x.pos;
     klen = x.len;
-    vpos = tomb ? 0u : s.val_off[idx];
     isB = s.isB;
     sh.kbits[j] = 8u * x.len;
     const uint32_t q = isB ? 1u : 0u;
@@ -204,15 +257,10 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
     if (j == 0) sh.bit_lo = rec_off;
     if (j == nown - 1) sh.bit_hi = rec_end;
     if (j == cnt - 1) sh.bit_ext = rec_end;
-  }
-  if (tid == 0) {
-    uint32_t kp = 0;
-    if (R0 > 0) {
-      uint32_t pidx;
-      const SideView ps = pick(A, B, final_refs[R0 - 1], pidx);
-      kp = 8u * (ps.key_off[pidx + 1] - ps.key_off[pidx]);
+    if (kTiled && off_out && j < nown) {
+      off_out[r] = rec_off;
+      if (r + 1 == S) off_out[S] = T;
     }
-    sh.kprev0 = kp;
   }
   __syncthreads();
   if (tid == 0) {
@@ -288,6 +336,56 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
   }
 }
 
+// Records per workgroup: the expected output bits and staged source bytes of
+// one workgroup fill about 90% of the window and the stage (a workgroup above
+// that takes its window in slices or reads its sources in place).  Staged
+// spans also hold the keys of replaced records and 16-byte margins, so the
+// source estimate is all input bytes per survivor plus 4.
+__host__ __device__ inline uint32_t emit_rpb(uint32_t S, uint64_t T, uint64_t src_bytes) {
+  const double mean_bits = static_cast<double>(T) / S;
+  const double mean_src = static_cast<double>(src_bytes) / S + 4.0;
+  const double r1 = 0.9 * kEmitWindow * 32.0 / mean_bits;
+  const double r2 = 0.9 * kEmitStage / mean_src;
+  const double r = r1 < r2 ? r1 : r2;
+  return r >= kEmitMaxRecs ? kEmitMaxRecs : (r < 16.0 ? 16u : static_cast<uint32_t>(r));
+}
+
+// One workgroup per `rpb` records (kDev = false: S, T and rpb come from the
+// host), or a grid of workgroups that are all resident at once and take
+// every gridDim-th chunk of `rpb` records (kDev = true: S and T are read from
+// device memory, where earlier kernels left them, and rpb follows from them).
+// (A shared atomic chunk counter was slower: every chunk then waits on the
+// same contended address.)
+template <bool kDev, bool kTiled, bool kLcp>
+__global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
+                                                     const uint32_t* __restrict__ final_refs,
+                                                     const uint32_t* __restrict__ lcp_in, uint32_t S_arg,
+                                                     const uint64_t* __restrict__ off,
+                                                     const uint64_t* __restrict__ tbase,
+                                                     uint64_t* __restrict__ off_out, uint64_t T_arg,
+                                                     uint32_t* __restrict__ payload, uint32_t rpb_arg,
+                                                     const uint32_t* __restrict__ d_S,
+                                                     const uint64_t* __restrict__ d_T, uint64_t src_bytes) {
+  __shared__ EmitShared sh;
+  const uint32_t S = kDev ? d_S[0] : S_arg;
+  const uint64_t T = kDev ? d_T[0] : T_arg;
+  if (S == 0) return;
+  const uint32_t rpb = kDev ? emit_rpb(S, T, src_bytes) : rpb_arg;
+  uint32_t chunk = blockIdx.x;
+  RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, chunk * rpb, rpb);
+  while (static_cast<uint64_t>(chunk) * rpb < S) {
+    const RecPre cur = pre;
+    const uint32_t nxt = chunk + gridDim.x;
+    if (kDev && static_cast<uint64_t>(nxt) * rpb < S)
+      pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, nxt * rpb, rpb);
+    emit_chunk<kTiled, kLcp>(sh, A, B, final_refs, lcp_in, S, off, tbase, off_out, T, payload, chunk * rpb,
+                             rpb, cur);
+    if (!kDev) break;
+    __syncthreads();
+    chunk = nxt;
+  }
+}
+
 }  // namespace em
 
 using namespace em;
@@ -321,20 +419,54 @@ extern "C" int em_emit(const em_side_t* A, const em_side_t* B, const uint32_t* f
   if (S == 0) return EM_OK;
   if (!final_refs || !off || !payload) return EM_EINVAL;
   if (payload_words < (T + 31) / 32) return EM_ENOSPC;
-  // records per workgroup: the expected output bits and staged source bytes
-  // of one workgroup fill about 90% of the window and the stage (a workgroup
-  // above that takes its window in slices or reads its sources in place).
-  // Staged spans also hold the keys of replaced records and 16-byte margins,
-  // so the source estimate is all input bytes per survivor plus 4.
-  const double mean_bits = static_cast<double>(T) / S;
-  const double mean_src =
-      static_cast<double>(A->key_bytes + B->key_bytes + A->val_bytes + B->val_bytes) / S + 4.0;
-  double r1 = 0.9 * kEmitWindow * 32.0 / mean_bits;
-  double r2 = 0.9 * kEmitStage / mean_src;
-  double r = r1 < r2 ? r1 : r2;
-  uint32_t rpb = r >= kEmitMaxRecs ? kEmitMaxRecs : (r < 16.0 ? 16u : static_cast<uint32_t>(r));
+  const uint64_t src = A->key_bytes + B->key_bytes + A->val_bytes + B->val_bytes;
+  const uint32_t rpb = emit_rpb(S, T, src);
   const uint32_t blocks = (S + rpb - 1) / rpb;
-  hipLaunchKernelGGL(k_emit, dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream), *A, *B,
-                     final_refs, lcp_bits, S, off, T, payload, rpb);
+  if (lcp_bits)
+    hipLaunchKernelGGL((k_emit<false, false, true>), dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream), *A,
+                       *B, final_refs, lcp_bits, S, off, nullptr, nullptr, T, payload, rpb, nullptr, nullptr,
+                       src);
+  else
+    hipLaunchKernelGGL((k_emit<false, false, false>), dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream),
+                       *A, *B, final_refs, nullptr, S, off, nullptr, nullptr, T, payload, rpb, nullptr,
+                       nullptr, src);
   return check_launch();
 }
+
+namespace em {
+
+// Workgroups of k_emit<true, true, true> that one device holds at once.
+int emit_resident_grid(int dev, int* grid) {
+  static int cache[64] = {0};
+  if (dev < 0 || dev >= 64) return set_hip_error(hipErrorInvalidDevice);
+  if (cache[dev] == 0) {
+    int cus = 0, per = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return set_hip_error(e);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k_emit<true, true, true>, kEmitBlock, 0);
+    if (e != hipSuccess) return set_hip_error(e);
+    cache[dev] = (cus > 0 ? cus : 1) * (per > 0 ? per : 1);
+  }
+  *grid = cache[dev];
+  return EM_OK;
+}
+
+// The emitter after kernels that left S and T in device memory and record
+// offsets as partition number + local offset (tbase: partition bit bases):
+// exactly as many workgroups as the device holds at once (a workgroup that
+// had to wait for another to finish would add its whole run to the tail).
+int emit_launch_dev(const em_side_t& A, const em_side_t& B, const uint32_t* final_refs,
+                    const uint32_t* lcp_bits, const uint64_t* toff, const uint64_t* tbase,
+                    uint64_t* off_out, uint32_t* payload, const uint32_t* d_S, const uint64_t* d_T,
+                    hipStream_t st) {
+  int dev = 0, grid = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_hip_error(hipErrorInvalidDevice);
+  const int rc = emit_resident_grid(dev, &grid);
+  if (rc) return rc;
+  const uint64_t src = A.key_bytes + B.key_bytes + A.val_bytes + B.val_bytes;
+  hipLaunchKernelGGL((k_emit<true, true, true>), dim3(grid), dim3(kEmitBlock), 0, st, A, B, final_refs,
+                     lcp_bits, 0u, toff, tbase, off_out, 0ull, payload, 0u, d_S, d_T, src);
+  return check_launch();
+}
+
+}  // namespace em

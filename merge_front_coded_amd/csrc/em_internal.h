@@ -15,8 +15,8 @@ constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
 // Byte-arena access.  Arena bases are 16-byte aligned and padded by
-// EM_ARENA_PAD readable bytes, so the aligned dwords around any byte position
-// inside an arena (or up to 16 bytes past its end) are always readable.
+// EM_ARENA_PAD (32) readable bytes, so the aligned dwords around any byte
+// position inside an arena, up to 20 bytes past it, are always readable.
 
 // 8 bytes starting at byte `pos`, as a big-endian u64 (first byte most
 // significant): numeric order of these words is bytewise order of the bytes.
@@ -39,14 +39,53 @@ struct KeyRef {
   uint32_t len;  // bytes
 };
 
+// 16 bytes starting at byte `pos` as two big-endian u64s (reads the five
+// aligned dwords around them).
+__device__ __forceinline__ void load_be16(const uint8_t* base, uint32_t pos, uint64_t& hi, uint64_t& lo) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(base + (pos & ~3u));
+  const uint32_t s = pos & 3u;
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
+  const uint32_t d0 = __builtin_amdgcn_alignbyte(w1, w0, s);
+  const uint32_t d1 = __builtin_amdgcn_alignbyte(w2, w1, s);
+  const uint32_t d2 = __builtin_amdgcn_alignbyte(w3, w2, s);
+  const uint32_t d3 = __builtin_amdgcn_alignbyte(w4, w3, s);
+  hi = (static_cast<uint64_t>(__builtin_bswap32(d0)) << 32) | __builtin_bswap32(d1);
+  lo = (static_cast<uint64_t>(__builtin_bswap32(d2)) << 32) | __builtin_bswap32(d3);
+}
+
+// The next up-to-32 common bytes of two keys, as four big-endian u64s each,
+// bytes past `r` (the common bytes left) zeroed.  Both halves are loaded
+// before either is used, so one memory round trip covers 32 bytes.
+struct Chunk32 {
+  uint64_t v[4];
+};
+__device__ __forceinline__ void load_pair32(const uint8_t* ka, uint32_t pa, const uint8_t* kb, uint32_t pb,
+                                            uint32_t r, Chunk32& a, Chunk32& b) {
+  load_be16(ka, pa, a.v[0], a.v[1]);
+  load_be16(kb, pb, b.v[0], b.v[1]);
+  a.v[2] = a.v[3] = b.v[2] = b.v[3] = 0;
+  if (r > 16) {
+    load_be16(ka, pa + 16, a.v[2], a.v[3]);
+    load_be16(kb, pb + 16, b.v[2], b.v[3]);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t rq = r > 8u * q ? r - 8u * q : 0u;
+    const uint64_t m = be_mask(rq);
+    a.v[q] &= m;
+    b.v[q] &= m;
+  }
+}
+
 // Unsigned bytewise comparison with a proper prefix first: <0, 0, >0.
 __device__ __forceinline__ int cmp_keys(const uint8_t* ka, KeyRef a, const uint8_t* kb, KeyRef b) {
   const uint32_t m = a.len < b.len ? a.len : b.len;
-  for (uint32_t t = 0; t < m; t += 8) {
-    const uint64_t mask = be_mask(m - t);
-    const uint64_t va = load_be8(ka, a.pos + t) & mask;
-    const uint64_t vb = load_be8(kb, b.pos + t) & mask;
-    if (va != vb) return va < vb ? -1 : 1;
+  for (uint32_t t = 0; t < m; t += 32) {
+    Chunk32 x, y;
+    load_pair32(ka, a.pos + t, kb, b.pos + t, m - t, x, y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (x.v[q] != y.v[q]) return x.v[q] < y.v[q] ? -1 : 1;
   }
   return (a.len > b.len) - (a.len < b.len);
 }
@@ -54,10 +93,14 @@ __device__ __forceinline__ int cmp_keys(const uint8_t* ka, KeyRef a, const uint8
 // Exact bit LCP (MSB first within bytes), clamped to the shorter key.
 __device__ __forceinline__ uint32_t lcp_bits(const uint8_t* ka, KeyRef a, const uint8_t* kb, KeyRef b) {
   const uint32_t m = a.len < b.len ? a.len : b.len;
-  for (uint32_t t = 0; t < m; t += 8) {
-    const uint64_t mask = be_mask(m - t);
-    const uint64_t x = (load_be8(ka, a.pos + t) ^ load_be8(kb, b.pos + t)) & mask;
-    if (x) return 8 * t + static_cast<uint32_t>(__builtin_clzll(x));
+  for (uint32_t t = 0; t < m; t += 32) {
+    Chunk32 x, y;
+    load_pair32(ka, a.pos + t, kb, b.pos + t, m - t, x, y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t d = x.v[q] ^ y.v[q];
+      if (d) return 8 * t + 64u * q + static_cast<uint32_t>(__builtin_clzll(d));
+    }
   }
   return 8 * m;
 }
@@ -233,5 +276,17 @@ void clear_u64(uint64_t* p, size_t n, hipStream_t st);
 template <class OutT>
 int scan_launch(const uint32_t* in, uint32_t n, OutT* out, void* ws, size_t ws_bytes, hipStream_t st);
 void clear_u32(uint32_t* p, size_t n, hipStream_t st);
+
+// A record offset in partition form: partition number (< 2^24) above this
+// bit, the offset inside the partition's bits below it.
+constexpr int kTiledShift = 40;
+
+// The payload emitter reading S and T from device memory and record offsets
+// as partition number << 40 | partition-local offset plus partition bit
+// bases (em_fc.hip); off_out (nullable) receives the S+1 offsets.
+int emit_launch_dev(const em_side_t& A, const em_side_t& B, const uint32_t* final_refs,
+                    const uint32_t* lcp_bits, const uint64_t* toff, const uint64_t* tbase,
+                    uint64_t* off_out, uint32_t* payload, const uint32_t* d_S, const uint64_t* d_T,
+                    hipStream_t st);
 
 }  // namespace em

@@ -9,45 +9,40 @@
 // exactly as many steps as its slice is long.
 //
 // gfx950 design (one 512-thread workgroup = one partition of `items_per_part`
-// outputs; eight waves per partition keep the merge's dependent LDS steps
-// overlapped):
-//  * the partition's A and B key offsets are staged in LDS once;
-//  * each thread finds its slice's co-rank inside the partition by bisection
-//    on the staged offsets and merges IPT outputs; the comparison that decides
-//    each step also tells whether an A record equals its B neighbour, so the
-//    keep flag needs no second pass (an equal pair split by the partition
-//    boundary is caught by comparing the partition's last A with the next
-//    partition's first B);
+// outputs):
+//  * the partition's A and B key offsets and each key's first 8 bytes (the
+//    prefix cache) go to LDS; the key bytes stay in HBM, so a partition needs
+//    about 24 bytes of LDS per output and several partitions share a compute
+//    unit, which hides the latency of their loads and look-backs;
+//  * each thread finds its slice's co-rank inside the partition by a
+//    fixed-step search on the prefix cache and merges IPT outputs
+//    (merge_slice); the comparison that decides each step also tells whether
+//    an A record equals its B neighbour, so the keep flag needs no second pass
+//    (an equal pair split by the partition boundary is caught by comparing the
+//    partition's last A with the next partition's first B);
 //  * a block scan of keep flags gives partition-local ordinals, and a
 //    decoupled look-back over partitions (dynamic tickets) gives the global
 //    survivor base in the same pass;
-//  * survivors, ord_A and ord_B are staged in LDS and written with
-//    consecutive lanes on consecutive words.
+//  * survivors, ord_A and ord_B are staged in LDS (over the dead prefix
+//    cache) and written with consecutive lanes on consecutive words.
 #include "em_tile.h"
 
 namespace em {
 
 constexpr int kMergeBlock = 512;
 
-// LDS for a partition's key bytes; the compaction arrays reuse it after the merge.
-// (a multiple of 1 KB: LDS-DMA fills it 64 chunks of 16 bytes at a time)
-template <int IPT>
-constexpr uint32_t merge_key_cap() {
-  return IPT <= 1 ? 26u * 1024 : IPT == 2 ? 48u * 1024 : IPT == 4 ? 60u * 1024 : 32u * 1024;
-}
-
 template <int IPT>
 struct MergeShared {
   static constexpr int kTile = kMergeBlock * IPT;
-  static constexpr uint32_t kKeyCap = merge_key_cap<IPT>();
-  static_assert(kKeyCap >= 8u * kTile, "compaction arrays reuse the key buffer");
   uint32_t a_off[kTile + 2];
   uint32_t b_off[kTile + 2];
-  // prefix cache: each key's first 8 bytes, big-endian, zero padded
-  uint64_t a_pfx[kTile + 2];
-  uint64_t b_pfx[kTile + 2];
+  // prefix cache: each key's first 8 bytes, big-endian, zero padded; the
+  // compaction arrays reuse it after the merge
   union {
-    uint4 keys[kKeyCap / 16];
+    struct {
+      uint64_t a_pfx[kTile + 2];
+      uint64_t b_pfx[kTile + 2];
+    } m;
     struct {
       uint32_t out[kTile];
       uint32_t ords[kTile];
@@ -105,41 +100,18 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   }
   __syncthreads();
 
-  // ---- stage the partition's key bytes (A span, then B span) in LDS ----
-  // A compare reads 8-byte chunks through aligned dwords, up to 11 bytes past
-  // a key's last byte, so each span is staged with a 16-byte margin.
-  const uint32_t a_lo = sh.a_off[0] & ~15u;
-  const uint32_t a_bytes = len ? ((sh.a_off[nA_t] + 16u + 15u) & ~15u) - a_lo : 0u;
-  const uint32_t b_lo = sh.b_off[0] & ~15u;
-  const uint32_t b_bytes = len ? ((sh.b_off[nb_off - 1] + 16u + 15u) & ~15u) - b_lo : 0u;
-  const bool staged = a_bytes + b_bytes <= Sh::kKeyCap;
-  if (staged) {
-    // global -> LDS without registers: each wave moves 64 consecutive 16-byte
-    // chunks, lane i's chunk landing 16 i bytes after the wave's base
-    const uint32_t na16 = a_bytes / 16, total16 = (a_bytes + b_bytes) / 16;
-    const uint32_t lane = tid & (kWave - 1);
-    for (uint32_t c0 = (tid / kWave) * kWave; c0 < total16; c0 += kMergeBlock) {
-      const uint32_t c = c0 + lane;
-      if (c < total16) {
-        const uint8_t* src = c < na16 ? A.keys + a_lo + 16u * c : B.keys + b_lo + 16u * (c - na16);
-        lds_dma16(src, sh.u.keys + c0);
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();
-  const uint32_t a_adj = staged ? a_lo : 0u, b_adj = staged ? b_lo - a_bytes : 0u;
+  // ---- prefix cache (the keys themselves stay in HBM: comparisons the
+  // prefixes leave open read them in place, and the small LDS footprint
+  // keeps more partitions resident) ----
   {
     const uint32_t nb_keys = nb_off - 1;
     for (uint32_t x = tid; x < nA_t; x += kMergeBlock) {
       const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
-      sh.a_pfx[x] = (staged ? load_be8(reinterpret_cast<const uint8_t*>(sh.u.keys), p0 - a_adj)
-                            : load_be8(A.keys, p0)) & be_mask(ln < 8 ? ln : 8);
+      sh.u.m.a_pfx[x] = load_be8(A.keys, p0) & be_mask(ln < 8 ? ln : 8);
     }
     for (uint32_t y = tid; y < nb_keys; y += kMergeBlock) {
       const uint32_t p0 = sh.b_off[y], ln = sh.b_off[y + 1] - p0;
-      sh.b_pfx[y] = (staged ? load_be8(reinterpret_cast<const uint8_t*>(sh.u.keys), p0 - b_adj)
-                            : load_be8(B.keys, p0)) & be_mask(ln < 8 ? ln : 8);
+      sh.u.m.b_pfx[y] = load_be8(B.keys, p0) & be_mask(ln < 8 ? ln : 8);
     }
   }
   __syncthreads();
@@ -147,18 +119,11 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   // ---- merge this thread's slice ----
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
-  uint32_t kept;
-  if (staged) {
-    const uint8_t* st = reinterpret_cast<const uint8_t*>(sh.u.keys);
-    kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.a_pfx, sh.b_pfx, st, a_adj, st, b_adj, k, len, nA_t,
-                            nB_t, has_next_b, i0, A.n, j0, refs);
-  } else {
-    kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.a_pfx, sh.b_pfx, A.keys, 0u, B.keys, 0u, k, len,
-                            nA_t, nB_t, has_next_b, i0, A.n, j0, refs);
-  }
-  __syncthreads();  // the key buffer becomes the compaction arrays
+  const uint32_t kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.u.m.a_pfx, sh.u.m.b_pfx, A.keys, 0u, B.keys,
+                                         0u, k, len, nA_t, nB_t, has_next_b, i0, A.n, j0, refs);
 
-  // ---- keep scan inside the partition (the key buffer is free from here) ----
+  // ---- keep scan inside the partition (its barriers end every read of the
+  // prefix cache, which the compaction arrays then reuse) ----
   uint32_t total;
   uint32_t ord = block_exclusive_scan<uint32_t, kMergeBlock>(kept, sh.scan, total);
 #pragma unroll

@@ -38,10 +38,17 @@ __device__ __forceinline__ KeyRef key_of(const SideView& s, uint32_t r) {
   return KeyRef{p, s.key_off[r + 1] - p};
 }
 
+// The value's bit count in the record grammar; also its byte length (0 for a
+// tombstone) and start.  All loads are issued before any is used.
 __device__ __forceinline__ uint32_t value_bits(const SideView& s, uint32_t idx, uint32_t& vlen,
-                                               bool& tomb) {
-  tomb = s.tomb != nullptr && s.tomb[idx] != 0;
-  vlen = tomb ? 0u : s.val_off[idx + 1] - s.val_off[idx];
+                                               bool& tomb, uint32_t* vpos = nullptr) {
+  const uint32_t v0 = s.val_off[idx], v1 = s.val_off[idx + 1];
+  // (a side without tombstone flags reads a byte it then ignores, so that the
+  // load needs no branch)
+  const uint8_t tv = *(s.tomb ? s.tomb + idx : reinterpret_cast<const uint8_t*>(s.val_off + idx));
+  tomb = s.tomb != nullptr && tv != 0;
+  vlen = tomb ? 0u : v1 - v0;
+  if (vpos) *vpos = tomb ? 0u : v0;
   return tomb ? 1u : 1u + eg0_len(vlen) + 8u * vlen;
 }
 
@@ -439,6 +446,27 @@ __device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t
     }
   }
   return lo;
+}
+
+// Co-rank of diagonal d given coarse co-ranks around it: csplits[c] is the
+// co-rank of diagonal c * coarse (em_partition's output for `coarse`
+// outputs per partition, Pc partitions).  Read directly at a coarse
+// boundary, searched by corank16 inside the coarse partition otherwise (a
+// group of 16 lanes: t is the lane in the group, gshift its first lane).
+__device__ __forceinline__ uint32_t fine_corank(const em_side_t& A, const em_side_t& B,
+                                                const uint32_t* csplits, uint32_t coarse, uint32_t Pc,
+                                                uint32_t d, uint32_t t, uint32_t gshift) {
+  const uint32_t N = A.n + B.n;
+  if (d >= N) return csplits[Pc];
+  const uint32_t c = d / coarse;
+  if (d == c * coarse) return csplits[c];
+  const uint32_t Dc = c * coarse, Dn = min(Dc + coarse, N);
+  const uint32_t Ic = csplits[c], In = csplits[c + 1];
+  const uint32_t Jc = Dc - Ic, Jn = Dn - In;
+  uint32_t lo = max(max(Ic, d > Jn ? d - Jn : 0u), d > B.n ? d - B.n : 0u);
+  uint32_t hi = min(min(In, d - min(Jc, d)), min(d, A.n));
+  if (hi < lo) hi = lo;  // only for coarse splits that do not come from em_partition
+  return corank16(A, B, d, lo, hi, t, gshift);
 }
 
 }  // namespace em

@@ -4,8 +4,9 @@ Paths:
   merge      partition -> merge_keep -> [host reads S] -> fc_lengths -> scan
              -> [host reads T] -> emit  (the six-call C ABI)
   collision  collision_rank instead of partition + merge_keep
-  fused      coarse partition -> merge_fc (the whole path in one kernel; S and
-             T stay on the device)
+  fused      partition -> merge_lengths (merge, keep, LCPs, lengths, bit
+             offsets) -> emit_merged (the emitter); S and T stay on the
+             device.  one_call=True runs the same work as em_merge_fc.
 All buffers are allocated once up front (sized from em_workspace_bytes and
 em_payload_bound_bits) and reused by every run.
 """
@@ -16,43 +17,31 @@ import torch
 from . import binding as em
 
 
-# staged key bytes of one merge partition, by partition size (em_merge_keep.hip)
-_KEY_CAP = {256: 26 * 1024, 512: 26 * 1024, 1024: 48 * 1024, 2048: 60 * 1024, 4096: 32 * 1024}
-
-
 def choose_items_per_part(A: em.DeviceSide, B: em.DeviceSide) -> int:
-    """Largest partition (256..4096 outputs) whose keys are expected to fit the
-    merge kernel's LDS key buffer, so the partition's comparisons read LDS."""
+    """Partition size of the merge: 2048 outputs (LDS holds offsets and 8-byte
+    prefixes only, so two or three partitions share a compute unit), smaller
+    for small inputs so that every compute unit still gets partitions."""
     n = A.n + B.n
-    mean = (A.key_bytes + B.key_bytes) / n if n else 0.0
-    best = 256
-    for items in (256, 512, 1024, 2048, 4096):
-        if items * (mean * 1.1 + 4) <= _KEY_CAP[items]:
-            best = items
-    return best
+    for items in (2048, 1024, 512):
+        if n >= items * 512:
+            return items
+    return 256
 
 
-# staged key and value bytes of one partition in the fused kernel
-_FUSE_KEY_CAP, _FUSE_VAL_CAP, _FUSE_MAX_ITEMS, _FUSE_COARSE_PARTS = 14 * 1024, 12 * 1024, 256, 16
+_FUSE_COARSE_PARTS = 1
 
 
 def choose_fused_items(A: em.DeviceSide, B: em.DeviceSide) -> int:
-    """Largest partition (32..256 outputs) whose key and value bytes are expected
-    to fit the fused kernel's LDS staging buffers."""
-    n = A.n + B.n
-    mk = (A.key_bytes + B.key_bytes) / n if n else 0.0
-    mv = (A.val_bytes + B.val_bytes) / n if n else 0.0
-    best = 32
-    for items in (32, 64, 128, 256):
-        if (items + 3) * (mk * 1.1) + 64 <= _FUSE_KEY_CAP and items * (mv * 1.1) + 64 <= _FUSE_VAL_CAP:
-            best = items
-    return best
+    """Partition size of em_merge_fc's first kernel (at most 2048 outputs; the
+    same choice as the merge path)."""
+    return choose_items_per_part(A, B)
 
 
 class Pipeline:
     def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int | None = None,
                  path: str = "merge", keep_ordinals: bool = True, keep_lcp: bool = True,
-                 keep_all: bool = True, coarse_parts: int = _FUSE_COARSE_PARTS, device="cuda"):
+                 keep_all: bool = True, coarse_parts: int = _FUSE_COARSE_PARTS, one_call: bool = False,
+                 device="cuda"):
         if path not in ("merge", "collision", "fused"):
             raise ValueError("path is 'merge', 'collision' or 'fused'")
         self.A, self.B = A, B
@@ -64,6 +53,7 @@ class Pipeline:
             self.coarse = 0
         self.path = path
         self.keep_all = keep_all
+        self.one_call = one_call
         N = A.n + B.n
         self.N = N
         P = (N + (self.coarse or self.items) - 1) // (self.coarse or self.items)
@@ -96,11 +86,18 @@ class Pipeline:
         if self.path == "fused":
             em.em_partition(A, B, self.coarse, self.splits, self.ws, stream)
             k = self.keep_all
-            em.em_merge_fc(A, B, self.splits, self.coarse, self.items, self.payload, self.d_S, self.d_T,
-                           self.ws, final_refs=self.final if k else None,
-                           ord_A=self.ord_A if k else None, ord_B=self.ord_B if k else None,
-                           len_bits=self.len_bits if k else None, lcp_bits=self.lcp if k else None,
-                           off=self.off if k else None, stream=stream)
+            outs = dict(final_refs=self.final if k else None, ord_A=self.ord_A if k else None,
+                        ord_B=self.ord_B if k else None, len_bits=self.len_bits if k else None,
+                        lcp_bits=self.lcp if k else None)
+            if self.one_call:
+                em.em_merge_fc(A, B, self.splits, self.coarse, self.items, self.payload, self.d_S, self.d_T,
+                               self.ws, off=self.off if k else None, stream=stream, **outs)
+            else:
+                em.em_merge_lengths(A, B, self.splits, self.coarse, self.items, self.d_S, self.d_T, self.ws,
+                                    stream=stream, **outs)
+                em.em_emit_merged(A, B, self.items, self.payload, self.d_S, self.d_T, self.ws,
+                                  final_refs=outs["final_refs"], lcp_bits=outs["lcp_bits"],
+                                  off=self.off if k else None, stream=stream)
             if read_counts:
                 self.read_counts()
             return self.S, self.T

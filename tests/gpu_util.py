@@ -76,8 +76,8 @@ def compare(pl, ref, Ah, Bh, check_splits=True, label=""):
 
 
 def check_path(Ah, Bh, items=2048, path="merge", keep_lcp=True, label="", **kw):
-    if path == "fused" and items and items > 256:
-        items = 256
+    if path == "fused" and items and items > 2048:
+        items = 2048
     ref = oracle.run(Ah, Bh, items_per_part=items or 256)
     pl = run_gpu(Ah, Bh, items=items, path=path, keep_lcp=keep_lcp, **kw)
     compare(pl, ref, Ah, Bh, label=label or f"{path}/items={items}")

@@ -79,13 +79,22 @@ def test_argument_errors_before_any_launch(lib):
     # null splits, zero or oversized partition sizes
     assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 16, None, None, 0, None) == -1
     assert lib.em_partition(ctypes.byref(A), ctypes.byref(B), 0, buf, None, 0, None) == -1
-    # merge tiles hold at most EM_MAX_ITEMS_PER_PART outputs; the fused kernel 256
+    # merge tiles hold at most EM_MAX_ITEMS_PER_PART outputs; em_merge_fc's 2048
     assert lib.em_merge_keep(ctypes.byref(A), ctypes.byref(B), buf, 4097, buf, None, None, buf,
                              ctypes.c_void_p(0x100000), 1 << 20, None) == -1
-    for items, coarse in ((0, 256), (257, 514), (64, 100), (64, 0)):
+    for items, coarse in ((0, 256), (2049, 4098), (64, 100), (64, 0)):
         assert lib.em_merge_fc(ctypes.byref(A), ctypes.byref(B), buf, coarse, items, buf, 1 << 20, buf,
                                buf, None, None, None, None, None, None, ctypes.c_void_p(0x100000),
                                1 << 20, None) == -1
+    # the two halves of em_merge_fc check the same way
+    assert lib.em_merge_lengths(ctypes.byref(A), ctypes.byref(B), buf, 64, 0, buf, buf, None, None, None, None,
+                                None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    assert lib.em_merge_lengths(ctypes.byref(A), ctypes.byref(B), None, 64, 64, buf, buf, None, None, None,
+                                None, None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    assert lib.em_emit_merged(ctypes.byref(A), ctypes.byref(B), 64, ctypes.c_void_p(0x100008), 1 << 20, buf,
+                              buf, None, None, None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    assert lib.em_emit_merged(ctypes.byref(A), ctypes.byref(B), 64, buf, 1 << 20, buf, buf, None, None, None,
+                              ctypes.c_void_p(0x100000), 0, None) == -3
     # misaligned arena
     bad = _side(ptr=0x1001)
     assert lib.em_partition(ctypes.byref(bad), ctypes.byref(B), 16, buf, None, 0, None) == -1

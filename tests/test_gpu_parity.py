@@ -60,11 +60,20 @@ def test_uniform_workload_full_10k():
 
 
 @pytest.mark.parametrize("items,coarse_parts", [(1, 1), (1, 16), (3, 5), (17, 16), (64, 2), (100, 3),
-                                                (255, 16), (256, 1), (256, 16)])
+                                                (255, 16), (256, 1), (256, 16), (513, 2), (1000, 1),
+                                                (1024, 1), (1024, 4)])
 def test_fused_every_partition_size(items, coarse_parts):
     A, B = workload(1, 0.3)
     print(f"fused uniform-az 3000+3000 items={items} coarse={coarse_parts}", flush=True)
     check_path(A, B, items=items, path="fused", coarse_parts=coarse_parts)
+
+
+@pytest.mark.parametrize("items", [64, 1024, 2048])
+def test_fused_one_call_matches_oracle(items):
+    """em_merge_fc (both halves in one call) gives the same outputs."""
+    A, B = workload(2, 0.01)
+    print(f"fused one call zipf-paths 10k+10k items={items}", flush=True)
+    check_path(A, B, items=items, path="fused", one_call=True)
 
 
 def test_empty_sides():
