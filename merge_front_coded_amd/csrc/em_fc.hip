@@ -151,8 +151,7 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
 // then receives the offsets of the owned records and T).
 
 // The first loads of a thread's record: its reference, the offsets of its
-// start and end, its LCP.  A workgroup that walks several chunks loads these
-// for its next chunk while it works on the current one.
+// start and end, its LCP (and, for thread 0, the record before the chunk).
 struct RecPre {
   uint32_t ref, lcp;
   uint64_t o0, o1;
@@ -356,8 +355,10 @@ __host__ __device__ inline uint32_t emit_rpb(uint32_t S, uint64_t T, uint64_t sr
 // device memory, where earlier kernels left them, and rpb follows from them).
 // (A shared atomic chunk counter was slower: every chunk then waits on the
 // same contended address.)
+// (Six waves per SIMD: the register budget this asks for costs a few spilled
+// registers and is still faster than five.)
 template <bool kDev, bool kTiled, bool kLcp>
-__global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
+__global__ __launch_bounds__(kEmitBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_emit(em_side_t A, em_side_t B,
                                                      const uint32_t* __restrict__ final_refs,
                                                      const uint32_t* __restrict__ lcp_in, uint32_t S_arg,
                                                      const uint64_t* __restrict__ off,
@@ -371,18 +372,12 @@ __global__ __launch_bounds__(kEmitBlock) void k_emit(em_side_t A, em_side_t B,
   const uint64_t T = kDev ? d_T[0] : T_arg;
   if (S == 0) return;
   const uint32_t rpb = kDev ? emit_rpb(S, T, src_bytes) : rpb_arg;
-  uint32_t chunk = blockIdx.x;
-  RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, chunk * rpb, rpb);
-  while (static_cast<uint64_t>(chunk) * rpb < S) {
-    const RecPre cur = pre;
-    const uint32_t nxt = chunk + gridDim.x;
-    if (kDev && static_cast<uint64_t>(nxt) * rpb < S)
-      pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, nxt * rpb, rpb);
+  for (uint32_t chunk = blockIdx.x; static_cast<uint64_t>(chunk) * rpb < S; chunk += gridDim.x) {
+    const RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, chunk * rpb, rpb);
     emit_chunk<kTiled, kLcp>(sh, A, B, final_refs, lcp_in, S, off, tbase, off_out, T, payload, chunk * rpb,
-                             rpb, cur);
+                             rpb, pre);
     if (!kDev) break;
     __syncthreads();
-    chunk = nxt;
   }
 }
 
