@@ -42,6 +42,28 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
              "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit"}
 
 
+# Scaled HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes on
+# the 8M+8M base64 workload (profiles/traffic_fused_base64_8M+8M.md: FETCH_SIZE
+# x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
+# only while the kernel sources hash to the fingerprint it was taken with.
+TRAFFIC = {
+    "em_emit_merged": (2544459729, ("em_fc.hip", "em_tile.h", "em_internal.h"), "68a2445dd3d28850"),
+    "em_merge_lengths": (1330084572, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "dd1f7daa8736e43a"),
+}
+
+
+def measured_traffic(call, workload):
+    import hashlib
+    if workload != 3 or call not in TRAFFIC:
+        return None
+    nbytes, files, want = TRAFFIC[call]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "merge_front_coded_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return nbytes if h.hexdigest()[:16] == want else None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,7 +262,8 @@ def main():
         "per_call_ms": per_call_ms,
         "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dominant], "call": dominant, "achieved": ach,
                      "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(dominant, args.workload),
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_ms": per_call_ms[dominant]},
     }
