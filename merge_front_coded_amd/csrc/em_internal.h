@@ -165,6 +165,38 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T* smem, T& total) {
   return r;
 }
 
+// Exclusive scan of R values per thread where value u of thread t is element
+// u * NT + t of the sequence (rounds of a strided layout), with two barriers.
+// `smem` holds R * NT/64 + 1 values.
+template <class T, int NT, int R>
+__device__ __forceinline__ void block_exclusive_scan_rounds(const T (&v)[R], T* smem, T (&out)[R],
+                                                            T& total) {
+  constexpr int NW = NT / kWave;
+  const uint32_t lane = lane_id();
+  const uint32_t wid = threadIdx.x / kWave;
+  T inc[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    inc[u] = wave_inclusive_scan(v[u]);
+    if (lane == kWave - 1) smem[u * NW + wid] = inc[u];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    T acc = 0;
+    for (int w = 0; w < R * NW; ++w) {
+      T t = smem[w];
+      smem[w] = acc;
+      acc += t;
+    }
+    smem[R * NW] = acc;
+  }
+  __syncthreads();
+  total = smem[R * NW];
+#pragma unroll
+  for (int u = 0; u < R; ++u) out[u] = smem[u * NW + wid] + inc[u] - v[u];
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Decoupled look-back over per-tile descriptors (single-pass scan).  A
 // descriptor packs a 2-bit status and a 62-bit value in one u64 so that one

@@ -53,7 +53,7 @@ struct MlShared {
       uint32_t ords[kTile];  // per input record: survivor ordinal in the partition, or EM_NONE
     } c;
   } u;
-  uint64_t scan64[kMlWaves + 1];
+  uint64_t scan64[IPT * kMlWaves + 1];
   uint32_t scan32[kMlWaves + 1];
   uint32_t tile, i0, i1, g0;
 };
@@ -91,8 +91,10 @@ __device__ __forceinline__ int cmp_from_prefix(uint64_t p, uint64_t q, const uin
   return cmp_keys(pb, KeyRef{pk.pos + 8, pk.len - 8}, qb, KeyRef{qk.pos + 8, qk.len - 8});
 }
 
+// (Six waves per SIMD: three 512-thread partitions per compute unit, which
+// their LDS allows.)
 template <int IPT>
-__global__ __launch_bounds__(kMlBlock) void k_merge_len(em_side_t A, em_side_t B,
+__global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_merge_len(em_side_t A, em_side_t B,
                                                         const uint32_t* __restrict__ csplits,
                                                         uint32_t coarse, uint32_t items, uint32_t P,
                                                         MlOut out, uint32_t* __restrict__ ticket,
@@ -152,14 +154,30 @@ __global__ __launch_bounds__(kMlBlock) void k_merge_len(em_side_t A, em_side_t B
   }
   __syncthreads();
 
-  // ---- 3. prefix cache of every key whose offsets are in LDS ----
-  for (uint32_t x = tid; x + 1 < na_off; x += kMlBlock) {
-    const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
-    sh.u.m.a_pfx[x] = load_be8(A.keys, p0) & be_mask(ln < 8 ? ln : 8);
-  }
-  for (uint32_t y = tid; y + 1 < nb_off; y += kMlBlock) {
-    const uint32_t p0 = sh.b_off[y], ln = sh.b_off[y + 1] - p0;
-    sh.u.m.b_pfx[y] = load_be8(B.keys, p0) & be_mask(ln < 8 ? ln : 8);
+  // ---- 3. prefix cache of every key whose offsets are in LDS (all loads,
+  // then all stores) ----
+  {
+    constexpr int kPer = IPT + 1;  // ceil((kTile + 3) / kMlBlock)
+    uint64_t pa[kPer], pb[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t x = tid + u * kMlBlock;
+      pa[u] = pb[u] = 0;
+      if (x + 1 < na_off) {
+        const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
+        pa[u] = load_be8(A.keys, p0) & be_mask(ln < 8 ? ln : 8);
+      }
+      if (x + 1 < nb_off) {
+        const uint32_t p0 = sh.b_off[x], ln = sh.b_off[x + 1] - p0;
+        pb[u] = load_be8(B.keys, p0) & be_mask(ln < 8 ? ln : 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t x = tid + u * kMlBlock;
+      if (x + 1 < na_off) sh.u.m.a_pfx[x] = pa[u];
+      if (x + 1 < nb_off) sh.u.m.b_pfx[x] = pb[u];
+    }
   }
   __syncthreads();
 
@@ -216,21 +234,32 @@ __global__ __launch_bounds__(kMlBlock) void k_merge_len(em_side_t A, em_side_t B
   };
   uint32_t klen[IPT], l[IPT], kprev[IPT], vlen[IPT], sref[IPT];
   bool tomb[IPT];
+  // value lengths and tombstone flags from HBM, all issued before the LCPs
+  uint32_t v0[IPT], v1[IPT];
+  uint8_t tv[IPT];
 #pragma unroll
   for (int u = 0; u < IPT; ++u) {
     const uint32_t x = tid + u * kMlBlock;
-    klen[u] = l[u] = kprev[u] = vlen[u] = sref[u] = 0;
-    tomb[u] = false;
-    if (x >= n_kept) continue;
-    const uint32_t ref = sh.u.c.surv[x];
+    const uint32_t ref = x < n_kept ? sh.u.c.surv[x] : 0u;
     sref[u] = ref;
     const bool isB = ref >= A.n;
-    // value length and tombstone from HBM (consumed after the LCP)
     const uint32_t idx = isB ? ref - A.n : ref;
     const uint32_t* vo = isB ? B.val_off : A.val_off;
     const uint8_t* tb = isB ? B.tomb : A.tomb;
-    const uint32_t v0 = vo[idx], v1 = vo[idx + 1];
-    const bool t = tb != nullptr && tb[idx] != 0;
+    v0[u] = vo[idx];
+    v1[u] = vo[idx + 1];
+    // (a side without tombstone flags reads a byte it then ignores)
+    tv[u] = *(tb ? tb + idx : reinterpret_cast<const uint8_t*>(vo + idx));
+  }
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const uint32_t x = tid + u * kMlBlock;
+    klen[u] = l[u] = kprev[u] = vlen[u] = 0;
+    tomb[u] = false;
+    if (x >= n_kept) continue;
+    const uint32_t ref = sref[u];
+    const bool isB = ref >= A.n;
+    const bool t = (isB ? B.tomb : A.tomb) != nullptr && tv[u] != 0;
     const uint8_t* xb = isB ? B.keys : A.keys;
     const KeyRef xk = key_at(ref);
     const uint64_t xp = sh.u.c.spfx[x];
@@ -272,7 +301,7 @@ __global__ __launch_bounds__(kMlBlock) void k_merge_len(em_side_t A, em_side_t B
     }
     klen[u] = xk.len;
     tomb[u] = t;
-    vlen[u] = t ? 0u : v1 - v0;
+    vlen[u] = t ? 0u : v1[u] - v0[u];
   }
 
   // ---- 6. survivor base (look-back) ----
@@ -295,15 +324,11 @@ __global__ __launch_bounds__(kMlBlock) void k_merge_len(em_side_t A, em_side_t B
     rlen[u] = eg0_len(c) + eg0_len(kb - l[u]) + (kb - l[u]) +
               (tomb[u] ? 1u : 1u + eg0_len(vlen[u]) + 8u * vlen[u]);
   }
-  // survivors tid, tid + 512, ... : one block scan per round
-  uint64_t tile_bits = 0;
-  uint64_t sb[IPT];
+  // survivors tid, tid + 512, ...: one scan over the rounds
+  uint64_t tile_bits, sb[IPT], rl[IPT];
 #pragma unroll
-  for (int u = 0; u < IPT; ++u) {
-    uint64_t round_total;
-    sb[u] = tile_bits + block_exclusive_scan<uint64_t, kMlBlock>(rlen[u], sh.scan64, round_total);
-    tile_bits += round_total;
-  }
+  for (int u = 0; u < IPT; ++u) rl[u] = rlen[u];
+  block_exclusive_scan_rounds<uint64_t, kMlBlock, IPT>(rl, sh.scan64, sb, tile_bits);
 
   // ---- 8. outputs ----
   const uint64_t tag = static_cast<uint64_t>(tile) << kTiledShift;
