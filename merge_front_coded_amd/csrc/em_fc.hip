@@ -80,6 +80,7 @@ struct EmitShared {
   uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
   uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
   uint32_t kprev0;
+  uint32_t next;  // the workgroup's next chunk ticket
   uint64_t bit_lo, bit_hi, bit_ext;
 };
 
@@ -96,14 +97,18 @@ struct EmitRecord {
 };
 
 // Steps 2 and 3 for the workgroup: the records' bits go into the LDS window
-// slice by slice, and each slice's owned words are copied out.
+// slice by slice, and each slice's owned words are copied out.  Thread 0
+// publishes `ticket` in sh.next before the first copy-out (it waits for the
+// ticket's atomic there, after the window is built).
 __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r, const uint32_t* kbase,
-                                            const uint32_t* vbase, uint64_t T, uint32_t* payload) {
+                                            const uint32_t* vbase, uint64_t T, uint32_t* payload,
+                                            uint32_t ticket) {
   const uint32_t tid = threadIdx.x;
   const uint64_t wb = (sh.bit_lo >> 5) << 5;           // first bit of window word 0
   const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
   const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
-  const uint64_t ext = sh.bit_ext;
+  // bits past the last owned word are not needed
+  const uint64_t ext = min(sh.bit_ext, 32ull * w_hi);
   for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
     const uint64_t s1 = min(s0 + 32ull * kEmitWindow, ext);
     const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
@@ -131,6 +136,7 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
       span(vbase, r.vbit, r.b4, r.b5);
       ap.finish();
     }
+    if (s0 == wb && tid == 0) sh.next = ticket;
     __syncthreads();
     // owned words of this slice: 16-byte stores between a scalar head and tail
     const uint64_t o_lo = max(w_lo, s0 >> 5), o_hi = min(w_hi, (s1 + 31) >> 5);
@@ -141,6 +147,10 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
     for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock)
       *reinterpret_cast<uint4*>(payload + w) = uint4{win(w), win(w + 1), win(w + 2), win(w + 3)};
     for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
+    __syncthreads();
+  }
+  if (!(wb < ext && (wb >> 5) < w_hi)) {  // no slice (offsets that leave the chunk no bits)
+    if (tid == 0) sh.next = ticket;
     __syncthreads();
   }
 }
@@ -171,7 +181,10 @@ __device__ __forceinline__ RecPre load_rec_pre(const uint32_t* __restrict__ fina
     const uint32_t r = R0 + j;
     p.ref = final_refs[r];
     p.o0 = off[r];
-    p.o1 = (kTiled && r + 1 == S) ? p.o0 : off[r + 1];
+    // partition-form offsets have no entry S: the last record reads entry
+    // S-1 again (both loads are issued before either is waited for)
+    const uint64_t o1 = off[kTiled && r + 1 == S ? r : r + 1];
+    p.o1 = o1;
     p.lcp = kLcp ? lcp_in[r] : 0u;
   }
   return p;
@@ -187,7 +200,7 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
                                            const uint64_t* __restrict__ tbase,
                                            uint64_t* __restrict__ off_out, uint64_t T,
                                            uint32_t* __restrict__ payload, uint32_t R0, uint32_t rpb,
-                                           const RecPre& pre) {
+                                           const RecPre& pre, uint32_t* ctr) {
   const uint32_t tid = threadIdx.x;
   const uint32_t nown = (S - R0) < rpb ? S - R0 : rpb;
   const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
@@ -308,6 +321,14 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     }
     __builtin_amdgcn_s_waitcnt(0);
   }
+  // The next chunk's ticket: taken here, after the last global load of the
+  // chunk, so that its round trip overlaps the LDS work below (a later wait
+  // for a load would also wait for it).
+  // (an increment-with-wrap at 2^32 - 1 is an add of one here; unlike an add,
+  // the compiler does not rewrite it into a wave-combined form whose result
+  // it must wait for at once)
+  uint32_t ticket = 0;
+  if (ctr && tid == 0) ticket = __builtin_amdgcn_atomic_inc32(ctr, 0xFFFFFFFFu, __ATOMIC_RELAXED, "agent");
   // source bit positions of this record's key suffix and value bytes
   const uint32_t k = 8u * klen;
   const uint32_t e1 = eg0_len(c), e2 = eg0_len(k - l), ev = eg0_len(vlen);
@@ -326,12 +347,12 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     rec.kbit = 8ull * (kpos + (l >> 3) - sh.span_lo[qk] + sh.stage_at[qk]) + (l & 7u);
     rec.vbit = 8ull * (vpos - sh.span_lo[qv] + sh.stage_at[qv]);
     const uint32_t* st = reinterpret_cast<const uint32_t*>(sh.stage);
-    emit_slices(sh, rec, st, st, T, payload);
+    emit_slices(sh, rec, st, st, T, payload, ticket);
   } else {
     rec.kbit = 8ull * kpos + l;
     rec.vbit = 8ull * vpos;
     emit_slices(sh, rec, reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys),
-                reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals), T, payload);
+                reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals), T, payload, ticket);
   }
 }
 
@@ -350,13 +371,19 @@ __host__ __device__ inline uint32_t emit_rpb(uint32_t S, uint64_t T, uint64_t sr
 }
 
 // One workgroup per `rpb` records (kDev = false: S, T and rpb come from the
-// host), or a grid of workgroups that are all resident at once and take
-// every gridDim-th chunk of `rpb` records (kDev = true: S and T are read from
-// device memory, where earlier kernels left them, and rpb follows from them).
-// (A shared atomic chunk counter was slower: every chunk then waits on the
-// same contended address.)
-// (Six waves per SIMD: the register budget this asks for costs a few spilled
-// registers and is still faster than five.)
+// host), or a grid of workgroups that are all resident at once (kDev = true:
+// S and T are read from device memory, where earlier kernels left them, and
+// rpb follows from them).  A resident workgroup starts with chunk
+// blockIdx.x and then takes chunks from one of kEmitCtrs ticket counters
+// (workgroup b uses counter b mod kEmitCtrs, whose tickets name the chunks
+// congruent to it beyond those the workgroups start with), so that
+// workgroups that drew short chunks take more; spreading the tickets over
+// several counters keeps any one address cool.  Counter x hands out exactly
+// as many tickets as there are chunks congruent to x (one per chunk taken
+// from it, one that ends the loop for each workgroup that ran a chunk), so
+// the workgroup that draws the last one sets it back to zero for the next
+// launch.  (Six waves per SIMD: the register budget this asks for is still
+// faster than five.)
 template <bool kDev, bool kTiled, bool kLcp>
 __global__ __launch_bounds__(kEmitBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_emit(em_side_t A, em_side_t B,
                                                      const uint32_t* __restrict__ final_refs,
@@ -366,18 +393,38 @@ __global__ __launch_bounds__(kEmitBlock) __attribute__((amdgpu_waves_per_eu(6)))
                                                      uint64_t* __restrict__ off_out, uint64_t T_arg,
                                                      uint32_t* __restrict__ payload, uint32_t rpb_arg,
                                                      const uint32_t* __restrict__ d_S,
-                                                     const uint64_t* __restrict__ d_T, uint64_t src_bytes) {
+                                                     const uint64_t* __restrict__ d_T, uint64_t src_bytes,
+                                                     uint32_t* __restrict__ ctr) {
   __shared__ EmitShared sh;
   const uint32_t S = kDev ? d_S[0] : S_arg;
   const uint64_t T = kDev ? d_T[0] : T_arg;
   if (S == 0) return;
   const uint32_t rpb = kDev ? emit_rpb(S, T, src_bytes) : rpb_arg;
-  for (uint32_t chunk = blockIdx.x; static_cast<uint64_t>(chunk) * rpb < S; chunk += gridDim.x) {
-    const RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, chunk * rpb, rpb);
-    emit_chunk<kTiled, kLcp>(sh, A, B, final_refs, lcp_in, S, off, tbase, off_out, T, payload, chunk * rpb,
-                             rpb, pre);
-    if (!kDev) break;
-    __syncthreads();
+  if (!kDev) {
+    const uint32_t R0 = blockIdx.x * rpb;
+    if (R0 >= S) return;
+    const RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, R0, rpb);
+    emit_chunk<kTiled, kLcp>(sh, A, B, final_refs, lcp_in, S, off, tbase, off_out, T, payload, R0, rpb, pre,
+                             nullptr);
+    return;
+  }
+  const uint32_t nchunks = (S - 1) / rpb + 1;
+  const uint32_t G = gridDim.x, R = G < kEmitCtrs ? G : kEmitCtrs;
+  const uint32_t x = blockIdx.x % R;
+  const uint32_t nb = (G - x + R - 1) / R;                            // workgroups on counter x
+  const uint32_t nx = x < nchunks ? (nchunks - 1 - x) / R + 1 : 0;  // chunks congruent to x
+  uint32_t* const my_ctr = ctr + x * kEmitCtrStride;
+  uint64_t chunk = blockIdx.x;  // 64 bits: a ticket near 2^32 must end the loop, not wrap
+  while (chunk < nchunks) {
+    const uint32_t R0 = static_cast<uint32_t>(chunk * rpb);  // < S
+    const RecPre pre = load_rec_pre<kTiled, kLcp>(final_refs, lcp_in, off, S, R0, rpb);
+    emit_chunk<kTiled, kLcp>(sh, A, B, final_refs, lcp_in, S, off, tbase, off_out, T, payload, R0, rpb, pre,
+                             my_ctr);
+    // (sh.next is rewritten only after the next chunk's first barriers)
+    const uint32_t t = sh.next;
+    chunk = static_cast<uint64_t>(R) * (static_cast<uint64_t>(t) + nb) + x;
+    if (chunk >= nchunks && threadIdx.x == 0 && t == nx - 1)
+      __hip_atomic_store(my_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -420,11 +467,11 @@ extern "C" int em_emit(const em_side_t* A, const em_side_t* B, const uint32_t* f
   if (lcp_bits)
     hipLaunchKernelGGL((k_emit<false, false, true>), dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream), *A,
                        *B, final_refs, lcp_bits, S, off, nullptr, nullptr, T, payload, rpb, nullptr, nullptr,
-                       src);
+                       src, nullptr);
   else
     hipLaunchKernelGGL((k_emit<false, false, false>), dim3(blocks), dim3(kEmitBlock), 0, as_stream(stream),
                        *A, *B, final_refs, nullptr, S, off, nullptr, nullptr, T, payload, rpb, nullptr,
-                       nullptr, src);
+                       nullptr, src, nullptr);
   return check_launch();
 }
 
@@ -453,14 +500,14 @@ int emit_resident_grid(int dev, int* grid) {
 int emit_launch_dev(const em_side_t& A, const em_side_t& B, const uint32_t* final_refs,
                     const uint32_t* lcp_bits, const uint64_t* toff, const uint64_t* tbase,
                     uint64_t* off_out, uint32_t* payload, const uint32_t* d_S, const uint64_t* d_T,
-                    hipStream_t st) {
+                    uint32_t* ctr, hipStream_t st) {
   int dev = 0, grid = 0;
   if (hipGetDevice(&dev) != hipSuccess) return set_hip_error(hipErrorInvalidDevice);
   const int rc = emit_resident_grid(dev, &grid);
   if (rc) return rc;
   const uint64_t src = A.key_bytes + B.key_bytes + A.val_bytes + B.val_bytes;
   hipLaunchKernelGGL((k_emit<true, true, true>), dim3(grid), dim3(kEmitBlock), 0, st, A, B, final_refs,
-                     lcp_bits, 0u, toff, tbase, off_out, 0ull, payload, 0u, d_S, d_T, src);
+                     lcp_bits, 0u, toff, tbase, off_out, 0ull, payload, 0u, d_S, d_T, src, ctr);
   return check_launch();
 }
 

@@ -313,12 +313,20 @@ void clear_u32(uint32_t* p, size_t n, hipStream_t st);
 // bit, the offset inside the partition's bits below it.
 constexpr int kTiledShift = 40;
 
+// Chunk ticket counters of the resident emitter: kEmitCtrs counters,
+// kEmitCtrStride u32 apart (one 128-byte line each).  They must be zero
+// before the first launch; each launch leaves them zero.
+constexpr uint32_t kEmitCtrs = 8;
+constexpr uint32_t kEmitCtrStride = 32;
+constexpr uint32_t kEmitCtrWords = kEmitCtrs * kEmitCtrStride;
+
 // The payload emitter reading S and T from device memory and record offsets
 // as partition number << 40 | partition-local offset plus partition bit
-// bases (em_fc.hip); off_out (nullable) receives the S+1 offsets.
+// bases (em_fc.hip); off_out (nullable) receives the S+1 offsets; ctr holds
+// kEmitCtrWords u32 of ticket counters.
 int emit_launch_dev(const em_side_t& A, const em_side_t& B, const uint32_t* final_refs,
                     const uint32_t* lcp_bits, const uint64_t* toff, const uint64_t* tbase,
                     uint64_t* off_out, uint32_t* payload, const uint32_t* d_S, const uint64_t* d_T,
-                    hipStream_t st);
+                    uint32_t* ctr, hipStream_t st);
 
 }  // namespace em

@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kTsBlock) void k_tile_scan(const uint64_t* __restri
 }
 
 struct MlLayout {
-  uint32_t* ticket;
+  uint32_t* ticket;  // [0]: partition ticket of k_merge_len; from [kEmitCtrStride]: the emitter's counters
   uint64_t* desc_s;
   uint64_t* tile_bits;
   uint64_t* tbase;
@@ -390,7 +390,7 @@ MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
   const size_t P = items ? (static_cast<size_t>(N) + items - 1) / items : 0;
   WsCursor cur{static_cast<uint8_t*>(ws), 0};
   MlLayout L;
-  L.ticket = cur.take<uint32_t>(64);
+  L.ticket = cur.take<uint32_t>(kEmitCtrStride + kEmitCtrWords);
   L.desc_s = cur.take<uint64_t>(P ? P : 1);
   L.tile_bits = cur.take<uint64_t>(P ? P : 1);
   L.tbase = cur.take<uint64_t>(P ? P : 1);
@@ -403,7 +403,7 @@ MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
 size_t ml_ws_bytes(uint32_t N, uint32_t items) {
   const size_t P = items ? (static_cast<size_t>(N) + items - 1) / items : 0;
   const size_t p = P ? P : 1, n = N ? N : 1;
-  return align_up(64 * 4, 256) + 3 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) + align_up(n * 8, 256);
+  return align_up((kEmitCtrStride + kEmitCtrWords) * 4, 256) + 3 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) + align_up(n * 8, 256);
 }
 
 template <int IPT>
@@ -452,7 +452,7 @@ extern "C" int em_merge_lengths(const em_side_t* A, const em_side_t* B, const ui
   }
   const uint32_t P = (N + items_per_part - 1) / items_per_part;
   const MlLayout L = ml_layout(ws, N, items_per_part);
-  clear_u32(L.ticket, 1, st);
+  clear_u32(L.ticket, kEmitCtrStride + kEmitCtrWords, st);
   clear_u64(L.desc_s, P, st);
   MlOut o{d_S, final_refs ? final_refs : L.refs, lcp_bits ? lcp_bits : L.lcp, L.toff, L.tile_bits,
           ord_A, ord_B, len_bits};
@@ -486,7 +486,7 @@ extern "C" int em_emit_merged(const em_side_t* A, const em_side_t* B, uint32_t i
   }
   const MlLayout L = ml_layout(ws, N, items_per_part);
   return emit_launch_dev(*A, *B, final_refs ? final_refs : L.refs, lcp_bits ? lcp_bits : L.lcp, L.toff,
-                         L.tbase, off, payload, d_S, d_T, st);
+                         L.tbase, off, payload, d_S, d_T, L.ticket + kEmitCtrStride, st);
 }
 
 extern "C" int em_merge_fc(const em_side_t* A, const em_side_t* B, const uint32_t* coarse_splits,

@@ -366,55 +366,62 @@ __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp)
   return sh ? __builtin_amdgcn_alignbit(hi, lo, 32u - sh) : hi;
 }
 
-// Appends source bits [bp, bp + n) of a dword array.  After the first word
-// the output fill level stays fixed, so each further output word is one new
-// source dword and two funnel shifts.
+// Appends source bits [bp, bp + n) of a dword array.  The output word being
+// filled (fill f) is completed from the first source bits; every later
+// output word starts f bits before a 32-bit boundary of the remaining source,
+// so it is one funnel shift of two consecutive source dwords with a shift
+// that is the same for the whole span.  Reads reach at most one dword past
+// the one holding the span's last bit.
 __device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, uint64_t bp, uint32_t n) {
-  if (n >= 32 && ap.shared) {  // the shared first word goes through the general path
-    ap.put(bits32_at(base, bp), 32);
-    bp += 32;
-    n -= 32;
+  const uint32_t f = ap.fill;
+  if (f + n < 32u) {  // stays inside the word being filled
+    if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
+    return;
   }
-  if (n >= 32) {
-    const uint32_t* p = base + (bp >> 5);
-    const uint32_t sb = static_cast<uint32_t>(bp & 31u);
-    const uint32_t f = ap.fill;
-    uint32_t cur = __builtin_bswap32(p[0]);
-    uint32_t acc = ap.acc;
-    uint32_t* o = ap.out + ap.w;
-    const uint32_t full = n >> 5;
-    // source dword pair -> the 32 bits starting sb bits into the first one;
-    // v_alignbit takes its shift modulo 32, so sb = 0 selects the first dword
-    const uint32_t rs = 32u - sb;
-    auto src32 = [sb, rs](uint32_t a, uint32_t b) { return sb ? __builtin_amdgcn_alignbit(a, b, rs) : a; };
-    uint32_t t = 0;
-    for (; t + 4 <= full; t += 4) {  // four source dwords in flight per iteration
-      const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
-      const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
-      const uint32_t c0 = src32(cur, n1);
-      const uint32_t c1 = src32(n1, n2);
-      const uint32_t c2 = src32(n2, n3);
-      const uint32_t c3 = src32(n3, n4);
-      o[t] = acc | (c0 >> f);
-      o[t + 1] = __builtin_amdgcn_alignbit(c0, c1, f);
-      o[t + 2] = __builtin_amdgcn_alignbit(c1, c2, f);
-      o[t + 3] = __builtin_amdgcn_alignbit(c2, c3, f);
-      acc = __builtin_amdgcn_alignbit(c3, 0u, f);  // c3 << (32 - f), 0 when f = 0
-      cur = n4;
-    }
-    for (; t < full; ++t) {
-      const uint32_t nxt = __builtin_bswap32(p[t + 1]);
-      const uint32_t chunk = src32(cur, nxt);
-      o[t] = acc | (chunk >> f);
-      acc = __builtin_amdgcn_alignbit(chunk, 0u, f);
-      cur = nxt;
-    }
-    ap.acc = acc;
-    ap.w += full;
-    bp += 32ull * full;
-    n &= 31u;
+  const uint32_t W = (f + n) >> 5, f2 = (f + n) & 31u;  // completed words, fill afterwards
+  const uint32_t v0 = ap.acc | (bits32_at(base, bp) >> f);
+  if (ap.shared)
+    atomicOr(ap.out + ap.w, v0);
+  else
+    ap.out[ap.w] = v0;
+  // output word i >= 1 holds source bits [P, P + 32) with P = bp + 32 i - f
+  // (P >= 1): bits of dwords (P - 1) / 32 and the next, shifted right by -P
+  // mod 32 (a shift of 0 gives the second dword).
+  const uint32_t* p = base + ((bp + 31u - f) >> 5);
+  const uint32_t sh = (f - static_cast<uint32_t>(bp)) & 31u;
+  uint32_t* o = ap.out + ap.w + 1;
+  const uint32_t cnt = W - 1;  // words 1 .. W-1 go to o[0 .. cnt)
+  uint32_t cur = __builtin_bswap32(p[0]);
+  uint32_t t = 0;
+  for (; t + 4 <= cnt; t += 4) {  // four source dwords in flight per iteration
+    const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
+    const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
+    o[t] = __builtin_amdgcn_alignbit(cur, n1, sh);
+    o[t + 1] = __builtin_amdgcn_alignbit(n1, n2, sh);
+    o[t + 2] = __builtin_amdgcn_alignbit(n2, n3, sh);
+    o[t + 3] = __builtin_amdgcn_alignbit(n3, n4, sh);
+    cur = n4;
   }
-  if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
+  // up to three more words, then the partial word left in the accumulator
+  // (source dwords t+1 .. t+rem, and one more when f2 > 0; indices past the
+  // last one needed re-read it)
+  const uint32_t rem = cnt - t;
+  const uint32_t last = t + rem + (f2 ? 1u : 0u);
+  const uint32_t m1 = __builtin_bswap32(p[min(t + 1, last)]), m2 = __builtin_bswap32(p[min(t + 2, last)]);
+  const uint32_t m3 = __builtin_bswap32(p[min(t + 3, last)]), m4 = __builtin_bswap32(p[min(t + 4, last)]);
+  if (rem > 0) o[t] = __builtin_amdgcn_alignbit(cur, m1, sh);
+  if (rem > 1) o[t + 1] = __builtin_amdgcn_alignbit(m1, m2, sh);
+  if (rem > 2) o[t + 2] = __builtin_amdgcn_alignbit(m2, m3, sh);
+  uint32_t acc = 0;
+  if (f2) {
+    const uint32_t x = rem == 0 ? cur : rem == 1 ? m1 : rem == 2 ? m2 : m3;
+    const uint32_t y = rem == 0 ? m1 : rem == 1 ? m2 : rem == 2 ? m3 : m4;
+    acc = __builtin_amdgcn_alignbit(x, y, sh) & ~(0xFFFFFFFFu >> f2);
+  }
+  ap.w += W;
+  ap.fill = f2;
+  ap.acc = acc;
+  ap.shared = false;
 }
 
 // Co-rank of diagonal d (A records among the first d outputs of the stable

@@ -244,3 +244,20 @@ def test_repeated_runs_are_identical():
         pl.final.fill_(-1)
         pl.run()
         compare(pl, ref, A, B, label="rerun")
+
+
+def test_fused_emitter_reruns_with_chunk_tickets():
+    """More chunks than resident emitter workgroups, so that most chunks are
+    handed out by the ticket counters; emitting again from the same workspace
+    (the counters were left at zero) gives the same payload."""
+    import merge_front_coded_amd as em
+
+    A, B = workload(3, 0.03)
+    print(f"fused emitter reruns base64 {A.n}+{B.n}", flush=True)
+    pl, ref = check_path(A, B, items=2048, path="fused")
+    for i in range(2):
+        pl.payload.fill_(-1)
+        em.em_emit_merged(pl.A, pl.B, pl.items, pl.payload, pl.d_S, pl.d_T, pl.ws,
+                          final_refs=pl.final, lcp_bits=pl.lcp)
+        torch.cuda.synchronize()
+        assert pl.payload_bytes() == ref["payload"].tobytes(), f"emit rerun {i}"
