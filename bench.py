@@ -9,7 +9,8 @@ HBM.  Paths:
                    host read inside a step
   merge            em_partition, em_merge_keep, host read of S, em_fc_lengths,
                    em_scan, host read of T, em_emit
-  collision        em_collision_rank in place of partition + merge_keep
+  collision        em_collision_rank_mode (--collision-mode 512, 2048,
+                   512-tiled, 512-compact) in place of partition + merge_keep
 W untimed warm-up steps, then exactly K timed steps between two device
 synchronisations.  Prints one JSON line.
 
@@ -38,7 +39,8 @@ METRIC = "merged records/s and pipeline GB/s (% of HBM peak) at 8M+8M string key
 # the kernel each timed call launches (em_merge_lengths also runs a one-workgroup
 # scan of partition totals, about 1% of its time)
 KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em_fc_lengths": "k_fc_lengths",
-             "em_scan": "k_scan", "em_emit": "k_emit", "em_collision_rank": "k_collision (5 kernels)",
+             "em_scan": "k_scan", "em_emit": "k_emit",
+             "em_collision_rank_mode": "k_mark, rank build, scatter or compact + merge",
              "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit"}
 
 
@@ -73,6 +75,8 @@ def parse():
     ap.add_argument("--path", choices=("fused", "merge", "collision"), default="fused")
     ap.add_argument("--items", type=int, default=0,
                     help="outputs per merge partition (0: chosen from the mean key length)")
+    ap.add_argument("--collision-mode", choices=("512", "2048", "512-tiled", "512-compact"),
+                    default="512-tiled", help="collision path: rank layout and A placement")
     ap.add_argument("--coarse-parts", type=int, default=0,
                     help="fused path: partitions per coarse partition (0: library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -119,7 +123,7 @@ def algorithmic_bytes(Ah, Bh, pl, path):
         "em_scan": 4 * S + 8 * (S + 1),
         "em_emit": S * per_rec_meta + suffix_bytes + value_bytes + payload,
         "em_partition": 0,
-        "em_collision_rank": keys + offs + 4 * S + 4 * N,
+        "em_collision_rank_mode": keys + offs + 4 * S + 4 * N,
         # the whole path: every input byte once, the payload once
         "em_merge_fc": side_bytes(Ah) + side_bytes(Bh) + payload,
         # merge, keep, LCPs, lengths: every key byte, key and value offsets,
@@ -172,6 +176,8 @@ def main():
     B = em.DeviceSide.from_host(Bh)
     fused = args.path == "fused"
     extra = {"coarse_parts": args.coarse_parts} if (fused and args.coarse_parts) else {}
+    if args.path == "collision":
+        extra["collision_mode"] = args.collision_mode
     pl = em.Pipeline(A, B, items_per_part=args.items or None, path=args.path, keep_all=not fused, **extra)
     torch.cuda.synchronize()
 
@@ -184,7 +190,7 @@ def main():
     # the binding passes to the library)
     stream = torch.cuda.current_stream()
     calls = {"merge": ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"],
-             "collision": ["em_collision_rank", "em_fc_lengths", "em_scan", "em_emit"],
+             "collision": ["em_collision_rank_mode", "em_fc_lengths", "em_scan", "em_emit"],
              "fused": ["em_partition", "em_merge_lengths", "em_emit_merged"]}[args.path]
     ev = {c: [] for c in calls}
     orig = {c: getattr(em.pipeline.em, c) for c in calls}
@@ -251,7 +257,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "nA": Ah.n, "nB": Bh.n, "items_per_part": pl.items,
                    "path": args.path, "parallelism": "single-gpu",
-                   **({"coarse_items": pl.coarse} if fused else {})},
+                   **({"coarse_items": pl.coarse} if fused else {}),
+                   **({"collision_mode": args.collision_mode} if args.path == "collision" else {})},
         "survivors": pl.S,
         "payload_bits": pl.T,
         "B_io_bytes": b_io,

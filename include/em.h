@@ -140,6 +140,33 @@ int em_collision_rank(const em_side_t *A, const em_side_t *B, uint32_t *final_re
                       uint32_t *ord_B, uint32_t *d_S, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The collision variants side by side (same page: "The three experimental
+ * paths" and the suggested modes collision512, collision2048,
+ * collision512-tiled and collision512-compact).  Every mode marks collisions
+ * and saves B's lower bounds as em_collision_rank does, and gives the same
+ * outputs; they differ in the rank directory and in how A is placed:
+ *   EM_COLLISION_512          rank512; each surviving A_i binary-searches B's
+ *                             keys for lower_bound(B, A_i);
+ *   EM_COLLISION_2048         the same with the rank2048 directory (one 8-byte
+ *                             entry per 2048 bits: 32-bit absolute prefix and
+ *                             the populations before its 512-bit runs 1..3);
+ *   EM_COLLISION_512_TILED    rank512; A in tiles of 32 (em_collision_rank);
+ *   EM_COLLISION_512_COMPACT  rank512; surviving A references are compacted
+ *                             to i - R(i), then merged with B by Merge Path
+ *                             (their key sets are disjoint).
+ * ws: em_collision_workspace_bytes(|A|, |B|, mode), 256-byte aligned (the
+ * compact mode adds 4|A| bytes).  An unknown mode is EM_EINVAL.
+ */
+#define EM_COLLISION_512 0u
+#define EM_COLLISION_2048 1u
+#define EM_COLLISION_512_TILED 2u
+#define EM_COLLISION_512_COMPACT 3u
+size_t em_collision_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t mode);
+int em_collision_rank_mode(const em_side_t *A, const em_side_t *B, uint32_t mode, uint32_t *final_refs,
+                           uint32_t *ord_A, uint32_t *ord_B, uint32_t *d_S, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
  * Exact record lengths (Everett, "GPU construction experiment": the c_i
  * control equation and the record grammar paragraph).  For survivor i with
  * key length k_i bits and exact bit LCP l_i with survivor i-1 (l_0 = 0,
@@ -241,6 +268,17 @@ int em_rank512_probe(const uint32_t *bitmap, uint32_t nbits, const uint32_t *pos
 
 /* Workspace bytes em_rank512_probe needs for nbits bits (host only). */
 size_t em_rank512_workspace_bytes(uint32_t nbits);
+
+/*
+ * The same probe for the rank2048 directory of EM_COLLISION_2048 (same page,
+ * "Temporary rank layouts": an 8-byte directory entry per 2048 bits with the
+ * populations of its 512-bit runs; queries read up to eight bitmap words).
+ * Arguments, limits and errors as em_rank512_probe; workspace
+ * em_rank2048_workspace_bytes(nbits).
+ */
+int em_rank2048_probe(const uint32_t *bitmap, uint32_t nbits, const uint32_t *positions, uint32_t npos,
+                      uint32_t *out, void *ws, size_t ws_bytes, void *stream);
+size_t em_rank2048_workspace_bytes(uint32_t nbits);
 
 /* Text for an EM_* code (static string). */
 const char *em_strerror(int code);

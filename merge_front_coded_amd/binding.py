@@ -54,6 +54,10 @@ def load_library(path: str = LIB_PATH):
         "em_partition": (i32, [S, S, u32, P, P, sz, P]),
         "em_merge_keep": (i32, [S, S, P, u32, P, P, P, P, P, sz, P]),
         "em_collision_rank": (i32, [S, S, P, P, P, P, P, sz, P]),
+        "em_collision_rank_mode": (i32, [S, S, u32, P, P, P, P, P, sz, P]),
+        "em_collision_workspace_bytes": (sz, [u32, u32, u32]),
+        "em_rank2048_probe": (i32, [P, u32, P, u32, P, P, sz, P]),
+        "em_rank2048_workspace_bytes": (sz, [u32]),
         "em_fc_lengths": (i32, [S, S, P, u32, P, P, P, sz, P]),
         "em_scan": (i32, [P, u32, P, P, sz, P]),
         "em_emit": (i32, [S, S, P, P, u32, P, u64, P, u64, P, sz, P]),
@@ -150,6 +154,20 @@ def em_rank512_workspace_bytes(nbits: int) -> int:
     return int(lib().em_rank512_workspace_bytes(nbits))
 
 
+def em_rank2048_workspace_bytes(nbits: int) -> int:
+    return int(lib().em_rank2048_workspace_bytes(nbits))
+
+
+# collision modes (include/em.h)
+EM_COLLISION_512, EM_COLLISION_2048, EM_COLLISION_512_TILED, EM_COLLISION_512_COMPACT = 0, 1, 2, 3
+COLLISION_MODES = {"512": EM_COLLISION_512, "2048": EM_COLLISION_2048, "512-tiled": EM_COLLISION_512_TILED,
+                   "512-compact": EM_COLLISION_512_COMPACT}
+
+
+def em_collision_workspace_bytes(nA: int, nB: int, mode: int) -> int:
+    return int(lib().em_collision_workspace_bytes(nA, nB, mode))
+
+
 def em_payload_bound_bits(A: DeviceSide, B: DeviceSide) -> int:
     out = ctypes.c_uint64()
     _check(lib().em_payload_bound_bits(ctypes.byref(A.struct), ctypes.byref(B.struct),
@@ -188,6 +206,17 @@ def em_emit(A, B, final_refs, lcp_bits, S, off, T, payload, ws, stream=None):
     _check(lib().em_emit(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), _p(lcp_bits),
                          S, _p(off), T, _p(payload), payload.numel(), _p(ws), ws.numel(),
                          _stream(stream)), "em_emit")
+
+
+def em_collision_rank_mode(A, B, mode, final_refs, ord_A, ord_B, d_S, ws, stream=None):
+    _check(lib().em_collision_rank_mode(ctypes.byref(A.struct), ctypes.byref(B.struct), mode, _p(final_refs),
+                                        _p(ord_A), _p(ord_B), _p(d_S), _p(ws), ws.numel(), _stream(stream)),
+           "em_collision_rank_mode")
+
+
+def em_rank2048_probe(bitmap, nbits, positions, out, ws, stream=None):
+    _check(lib().em_rank2048_probe(_p(bitmap), nbits, _p(positions), positions.numel(), _p(out), _p(ws),
+                                   ws.numel(), _stream(stream)), "em_rank2048_probe")
 
 
 def em_rank512_probe(bitmap, nbits, positions, out, ws, stream=None):

@@ -1,5 +1,5 @@
-// Collision-bitmap variant of the keep step, with the temporary rank512
-// directory.
+// Collision-bitmap variants of the keep step, with the temporary rank512 and
+// rank2048 directories.
 //
 // Everett, "Collision bitmap and rank experiment":
 //  * "Corrected record ordinals": for each B_j find lb_j = lower_bound(A, B_j)
@@ -7,51 +7,86 @@
 //    bitmap word); the bitmap is cleared on the GPU first and bits past |A|
 //    stay zero.  With R(i) = sum_{t<i} C_t, B_j lands at j + lb_j - R(lb_j)
 //    and a surviving A_i at i + lower_bound(B, A_i) - R(i).
-//  * "Temporary rank layouts": each 512-bit block has a 32-bit absolute prefix
-//    and seven 9-bit prefixes for its 64-bit pairs, built by count -> global
-//    scan -> finish; a query reads the directory and one masked 64-bit word.
-//  * "The three experimental paths": B keeps independent searches (it is the
-//    sparse side in the skewed workload); A is handled by tiles of 32
-//    consecutive records, one search per tile and a monotone cursor.
+//  * "Temporary rank layouts": rank512 gives each 512-bit block a 32-bit
+//    absolute prefix and seven 9-bit prefixes for its 64-bit pairs; a query
+//    reads the directory and one masked 64-bit word.  rank2048 gives each
+//    2048-bit block one 8-byte entry: a 32-bit absolute prefix and the
+//    populations before its second, third and fourth 512-bit runs, packed
+//    (10, 11 and 11 bits); a query adds the popcounts of up to seven whole
+//    64-bit words of its run and one masked word.  Both are built by count ->
+//    global scan -> finish.
+//  * "The three experimental paths", and the suggested modes collision512,
+//    collision2048, collision512-tiled and collision512-compact:
+//      - independent lower bounds (EM_COLLISION_512, EM_COLLISION_2048): each
+//        surviving A_i searches B's keys for lower_bound(B, A_i);
+//      - tiled (EM_COLLISION_512_TILED): A in tiles of 32 consecutive records,
+//        one search per tile and a monotone cursor; B keeps independent
+//        searches (it is the sparse side in the skewed workload);
+//      - compact A then Merge Path (EM_COLLISION_512_COMPACT): the surviving
+//        A references go to i - R(i) of a compact list, which is then merged
+//        with B (disjoint key sets now) by merge-path partitions.
 //
-// The A tile's search and cursor run over the saved lower bounds lb_j, not
+// The tiled A search and cursor run over the saved lower bounds lb_j, not
 // over B's keys: for a surviving A_i, B_j < A_i exactly when lb_j <= i (a
 // B_j with lb_j = i and an equal key would have collided and removed A_i), so
 // lower_bound(B, A_i) = #{j : lb_j <= i}, and lb is non-decreasing in j.  The
-// A side therefore reads no key bytes at all.
+// tiled A side therefore reads no key bytes at all.
 #include "em_internal.h"
 
 namespace em {
 
 constexpr int kColBlock = 256;
-constexpr uint32_t kRankBlockBits = 512;
 constexpr uint32_t kTileA = 32;
+constexpr uint32_t kSuperBits = 2048;  // rank2048 block; the bitmap is kept in whole ones
 
-struct RankView {
-  const uint32_t* bits;  // bitmap words (whole 512-bit blocks + 2 pad words)
-  const uint32_t* dir;   // 3 u32 per block, nblk + 1 blocks
+struct Rank512View {
+  const uint32_t* bits;  // bitmap words (whole 2048-bit blocks + 16 pad words)
+  const uint32_t* dir;   // 3 u32 per 512-bit block, nblk + 1 blocks
+  // Exclusive rank: set bits at positions < p (p <= nbits).
+  __device__ __forceinline__ uint32_t rank(uint32_t p) const {
+    const uint32_t b = p >> 9;
+    uint32_t r = dir[3 * b];
+    const uint32_t q = (p >> 6) & 7u;
+    if (q) {
+      const uint64_t packed = dir[3 * b + 1] | (static_cast<uint64_t>(dir[3 * b + 2]) << 32);
+      r += static_cast<uint32_t>((packed >> (9 * (q - 1))) & 511u);
+    }
+    const uint32_t m = p & 63u;
+    if (m) {
+      const uint32_t w = p >> 6;
+      const uint64_t word = bits[2 * w] | (static_cast<uint64_t>(bits[2 * w + 1]) << 32);
+      r += static_cast<uint32_t>(__builtin_popcountll(word & ((1ull << m) - 1)));
+    }
+    return r;
+  }
 };
 
-// Exclusive rank: set bits at positions < p (p <= nbits).
-__device__ __forceinline__ uint32_t rank512(RankView rv, uint32_t p) {
-  const uint32_t b = p >> 9;
-  uint32_t r = rv.dir[3 * b];
-  const uint32_t q = (p >> 6) & 7u;
-  if (q) {
-    const uint64_t packed = rv.dir[3 * b + 1] | (static_cast<uint64_t>(rv.dir[3 * b + 2]) << 32);
-    r += static_cast<uint32_t>((packed >> (9 * (q - 1))) & 511u);
+// rank2048 entry: bits 0..31 the set bits before the block, bits 32..41 /
+// 42..52 / 53..63 those inside it before its runs 1 / 2 / 3.  (The 32-bit
+// absolute field would restart at each 2^32-bit epoch; positions here are
+// below 2^25, so all of them are in the first epoch, whose base is 0.)
+struct Rank2048View {
+  const uint32_t* bits;
+  const uint64_t* dir;  // nsb + 1 entries
+  __device__ __forceinline__ uint32_t rank(uint32_t p) const {
+    const uint64_t e = dir[p >> 11];
+    uint32_t r = static_cast<uint32_t>(e);
+    const uint32_t run = (p >> 9) & 3u;
+    if (run == 1) r += static_cast<uint32_t>(e >> 32) & 0x3FFu;
+    if (run == 2) r += static_cast<uint32_t>(e >> 42) & 0x7FFu;
+    if (run == 3) r += static_cast<uint32_t>(e >> 53) & 0x7FFu;
+    // whole 64-bit words of the run before p, then the masked word
+    const uint64_t* w64 = reinterpret_cast<const uint64_t*>(bits);
+    const uint32_t w0 = (p >> 9) << 3, w1 = p >> 6;
+    for (uint32_t w = w0; w < w1; ++w) r += static_cast<uint32_t>(__builtin_popcountll(w64[w]));
+    const uint32_t m = p & 63u;
+    if (m) r += static_cast<uint32_t>(__builtin_popcountll(w64[w1] & ((1ull << m) - 1)));
+    return r;
   }
-  const uint32_t m = p & 63u;
-  if (m) {
-    const uint32_t w = p >> 6;
-    const uint64_t word = rv.bits[2 * w] | (static_cast<uint64_t>(rv.bits[2 * w + 1]) << 32);
-    r += static_cast<uint32_t>(__builtin_popcountll(word & ((1ull << m) - 1)));
-  }
-  return r;
-}
+};
 
-// count: population of each 512-bit block; entry nblk is 0 so that the scan
-// leaves the total there.
+// rank512 count: population of each 512-bit block; entry nblk is 0 so that
+// the scan leaves the total there.
 __global__ __launch_bounds__(kColBlock) void k_rank_count(const uint32_t* __restrict__ bits,
                                                           uint32_t nblk, uint32_t* __restrict__ cnt) {
   const uint32_t b = blockIdx.x * kColBlock + threadIdx.x;
@@ -69,7 +104,7 @@ __global__ __launch_bounds__(kColBlock) void k_rank_count(const uint32_t* __rest
   cnt[b] = c;
 }
 
-// finish: directory entry of every block from the scanned block prefixes.
+// rank512 finish: directory entry of every block from the scanned block prefixes.
 __global__ __launch_bounds__(kColBlock) void k_rank_finish(const uint32_t* __restrict__ bits,
                                                            uint32_t nblk,
                                                            const uint32_t* __restrict__ prefix,
@@ -87,6 +122,41 @@ __global__ __launch_bounds__(kColBlock) void k_rank_finish(const uint32_t* __res
   dir[3 * b] = prefix[b];
   dir[3 * b + 1] = static_cast<uint32_t>(packed);
   dir[3 * b + 2] = static_cast<uint32_t>(packed >> 32);
+}
+
+// rank2048 count: population of each 2048-bit block (entry nsb is 0).
+__global__ __launch_bounds__(kColBlock) void k_rank2048_count(const uint32_t* __restrict__ bits,
+                                                              uint32_t nsb, uint32_t* __restrict__ cnt) {
+  const uint32_t b = blockIdx.x * kColBlock + threadIdx.x;
+  if (b > nsb) return;
+  uint32_t c = 0;
+  if (b < nsb) {
+    const uint4* p = reinterpret_cast<const uint4*>(bits + 64 * b);
+    for (int q = 0; q < 16; ++q) {
+      const uint4 t = p[q];
+      c += __builtin_popcount(t.x) + __builtin_popcount(t.y) + __builtin_popcount(t.z) +
+           __builtin_popcount(t.w);
+    }
+  }
+  cnt[b] = c;
+}
+
+// rank2048 finish: the block's absolute prefix and its runs' populations.
+__global__ __launch_bounds__(kColBlock) void k_rank2048_finish(const uint32_t* __restrict__ bits,
+                                                               uint32_t nsb,
+                                                               const uint32_t* __restrict__ prefix,
+                                                               uint64_t* __restrict__ dir) {
+  const uint32_t b = blockIdx.x * kColBlock + threadIdx.x;
+  if (b > nsb) return;
+  uint64_t e = prefix[b];
+  if (b < nsb) {
+    uint32_t before = 0;
+    for (uint32_t run = 0; run < 3; ++run) {
+      for (uint32_t w = 0; w < 16; ++w) before += __builtin_popcount(bits[64 * b + 16 * run + w]);
+      e |= static_cast<uint64_t>(before) << (run == 0 ? 32 : run == 1 ? 42 : 53);
+    }
+  }
+  dir[b] = e;
 }
 
 // mark: lower bound of every B key in A, collision bit on an equal key.
@@ -108,22 +178,48 @@ __global__ __launch_bounds__(kColBlock) void k_mark(em_side_t A, em_side_t B, ui
   lb_out[j] = lo;
 }
 
-__global__ __launch_bounds__(kColBlock) void k_scatter_B(uint32_t nA, uint32_t nB, RankView rv,
+template <class View>
+__global__ __launch_bounds__(kColBlock) void k_scatter_B(uint32_t nA, uint32_t nB, View rv,
                                                          const uint32_t* __restrict__ lb,
                                                          uint32_t* __restrict__ final_refs,
                                                          uint32_t* __restrict__ ord_B) {
   const uint32_t j = blockIdx.x * kColBlock + threadIdx.x;
   if (j >= nB) return;
   const uint32_t i = lb[j];
-  const uint32_t o = j + i - rank512(rv, i);
+  const uint32_t o = j + i - rv.rank(i);
   final_refs[o] = nA + j;
   if (ord_B) ord_B[j] = o;
+}
+
+// Independent lower bounds: each surviving A_i searches B's keys.
+template <class View>
+__global__ __launch_bounds__(kColBlock) void k_scatter_A_search(em_side_t A, em_side_t B, View rv,
+                                                                uint32_t* __restrict__ final_refs,
+                                                                uint32_t* __restrict__ ord_A) {
+  const uint32_t i = blockIdx.x * kColBlock + threadIdx.x;
+  if (i >= A.n) return;
+  if ((rv.bits[i >> 5] >> (i & 31u)) & 1u) {
+    if (ord_A) ord_A[i] = EM_NONE;
+    return;
+  }
+  const KeyRef ka = key_of(A, i);
+  uint32_t lo = 0, hi = B.n;
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (cmp_keys(B.keys, key_of(B, mid), A.keys, ka) < 0)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  const uint32_t o = i + lo - rv.rank(i);
+  final_refs[o] = i;
+  if (ord_A) ord_A[i] = o;
 }
 
 // A in tiles of kTileA consecutive records: one search in the saved lower
 // bounds, then a monotone cursor; the rank is queried once per tile and then
 // advanced by the tile's own collision bits.
-__global__ __launch_bounds__(kColBlock) void k_scatter_A(uint32_t nA, uint32_t nB, RankView rv,
+__global__ __launch_bounds__(kColBlock) void k_scatter_A(uint32_t nA, uint32_t nB, Rank512View rv,
                                                          const uint32_t* __restrict__ lb,
                                                          uint32_t* __restrict__ final_refs,
                                                          uint32_t* __restrict__ ord_A) {
@@ -141,7 +237,7 @@ __global__ __launch_bounds__(kColBlock) void k_scatter_A(uint32_t nA, uint32_t n
       hi = mid;
   }
   uint32_t cur = lo;
-  uint32_t r = rank512(rv, i0);
+  uint32_t r = rv.rank(i0);
   const uint32_t cbits = rv.bits[i0 >> 5];  // kTileA == 32: the tile is one bitmap word
   for (uint32_t i = i0; i < i1; ++i) {
     const uint32_t c = (cbits >> (i - i0)) & 1u;
@@ -157,11 +253,94 @@ __global__ __launch_bounds__(kColBlock) void k_scatter_A(uint32_t nA, uint32_t n
   }
 }
 
-__global__ void k_collision_total(uint32_t nA, uint32_t nB, RankView rv, uint32_t* d_S) {
-  *d_S = nA + nB - rank512(rv, nA);
+// Compact A: surviving A_i goes to slot i - R(i) of cA (one bitmap word per
+// thread; the rank is queried once per word).  A replaced A_i gets EM_NONE.
+__global__ __launch_bounds__(kColBlock) void k_compact_A(uint32_t nA, Rank512View rv,
+                                                         uint32_t* __restrict__ cA,
+                                                         uint32_t* __restrict__ ord_A) {
+  const uint32_t t = blockIdx.x * kColBlock + threadIdx.x;
+  const uint32_t i0 = t * 32u;
+  if (i0 >= nA) return;
+  const uint32_t i1 = i0 + 32u < nA ? i0 + 32u : nA;
+  uint32_t r = rv.rank(i0);
+  const uint32_t cbits = rv.bits[i0 >> 5];
+  for (uint32_t i = i0; i < i1; ++i) {
+    if ((cbits >> (i - i0)) & 1u) {
+      ++r;
+      if (ord_A) ord_A[i] = EM_NONE;
+    } else {
+      cA[i - r] = i;
+    }
+  }
 }
 
-// Copy a caller bitmap into whole 512-bit blocks, clearing bits >= nbits.
+// Merge Path over the compact A list (A'_x = A[cA[x]]) and B, whose key sets
+// are disjoint: a workgroup takes kMcItems consecutive outputs, finds the
+// co-ranks of its two diagonals (threads 0 and 1), then each thread finds
+// the co-rank of its own diagonal inside that range and merges kMcIPT
+// outputs.  The co-rank of diagonal d is the number of A' among the first d
+// outputs: the smallest x with A'_x > B_{d-1-x} (or x = min(d, |A'|)).
+constexpr uint32_t kMcIPT = 4;
+constexpr uint32_t kMcItems = kColBlock * kMcIPT;
+
+__device__ __forceinline__ uint32_t corank_compact(const em_side_t& A, const em_side_t& B,
+                                                   const uint32_t* cA, uint32_t d, uint32_t lo,
+                                                   uint32_t hi) {
+  while (lo < hi) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);  // mid < min(d, |A'|), d - 1 - mid < |B|
+    if (cmp_keys(A.keys, key_of(A, cA[mid]), B.keys, key_of(B, d - 1 - mid)) <= 0)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kColBlock) void k_merge_compact(em_side_t A, em_side_t B, Rank512View rv,
+                                                             const uint32_t* __restrict__ cA,
+                                                             uint32_t* __restrict__ final_refs,
+                                                             uint32_t* __restrict__ ord_A,
+                                                             uint32_t* __restrict__ ord_B) {
+  __shared__ uint32_t s_i[2];
+  const uint32_t nAc = A.n - rv.rank(A.n);
+  const uint32_t N = nAc + B.n;
+  const uint32_t d0 = blockIdx.x * kMcItems;
+  if (d0 >= N) return;
+  const uint32_t d1 = min(d0 + kMcItems, N);
+  if (threadIdx.x < 2) {
+    const uint32_t d = threadIdx.x ? d1 : d0;
+    s_i[threadIdx.x] = corank_compact(A, B, cA, d, d > B.n ? d - B.n : 0u, min(d, nAc));
+  }
+  __syncthreads();
+  const uint32_t i0 = s_i[0], i1 = s_i[1];
+  const uint32_t j0 = d0 - i0, j1 = d1 - i1;
+  const uint32_t dt = d0 + threadIdx.x * kMcIPT;
+  if (dt >= d1) return;
+  // this thread's diagonal: i in [max(i0, dt - j1), min(i1, dt - j0)]
+  const uint32_t lo = max(i0, dt > j1 ? dt - j1 : 0u), hi = min(i1, dt - j0);
+  uint32_t i = corank_compact(A, B, cA, dt, lo, hi < lo ? lo : hi);
+  uint32_t j = dt - i;
+  const uint32_t dend = min(dt + kMcIPT, d1);
+  for (uint32_t d = dt; d < dend; ++d) {
+    const bool takeA = j >= j1 || (i < i1 && cmp_keys(A.keys, key_of(A, cA[i]), B.keys, key_of(B, j)) <= 0);
+    if (takeA) {
+      const uint32_t r = cA[i++];
+      final_refs[d] = r;
+      if (ord_A) ord_A[r] = d;
+    } else {
+      final_refs[d] = A.n + j;
+      if (ord_B) ord_B[j] = d;
+      ++j;
+    }
+  }
+}
+
+template <class View>
+__global__ void k_collision_total(uint32_t nA, uint32_t nB, View rv, uint32_t* d_S) {
+  *d_S = nA + nB - rv.rank(nA);
+}
+
+// Copy a caller bitmap into whole blocks, clearing bits >= nbits.
 __global__ __launch_bounds__(kColBlock) void k_copy_bits(const uint32_t* __restrict__ src, uint32_t nbits,
                                                          uint32_t* __restrict__ dst, uint32_t nwords) {
   const uint32_t w = blockIdx.x * kColBlock + threadIdx.x;
@@ -176,21 +355,24 @@ __global__ __launch_bounds__(kColBlock) void k_copy_bits(const uint32_t* __restr
   dst[w] = v;
 }
 
-__global__ __launch_bounds__(kColBlock) void k_rank_probe(RankView rv, const uint32_t* __restrict__ pos,
+template <class View>
+__global__ __launch_bounds__(kColBlock) void k_rank_probe(View rv, const uint32_t* __restrict__ pos,
                                                           uint32_t npos, uint32_t nbits,
                                                           uint32_t* __restrict__ out) {
   const uint32_t t = blockIdx.x * kColBlock + threadIdx.x;
   if (t >= npos) return;
   const uint32_t p = pos[t];
-  out[t] = p <= nbits ? rank512(rv, p) : EM_NONE;
+  out[t] = p <= nbits ? rv.rank(p) : EM_NONE;
 }
 
-// ---- workspace layout shared by the collision path and the probe ----
+// ---- workspace layout shared by the collision path and the probes ----
 
 struct RankLayout {
-  uint32_t nblk;
-  uint32_t* bits;    // 16 * nblk + 16 words
-  uint32_t* dir;     // 3 * (nblk + 1)
+  uint32_t nblk;     // 512-bit blocks
+  uint32_t nsb;      // 2048-bit blocks
+  uint32_t* bits;    // 64 * nsb + 16 words
+  uint32_t* dir;     // rank512: 3 * (nblk + 1)
+  uint64_t* dir2048; // rank2048: nsb + 1
   uint32_t* cnt;     // nblk + 1
   uint32_t* prefix;  // nblk + 2
   uint8_t* scan_ws;
@@ -200,10 +382,12 @@ struct RankLayout {
 
 static RankLayout rank_layout(void* ws, uint32_t nbits) {
   RankLayout L{};
-  L.nblk = (nbits + kRankBlockBits - 1) / kRankBlockBits;
+  L.nblk = (nbits + 511u) / 512u;
+  L.nsb = (nbits + kSuperBits - 1) / kSuperBits;
   WsCursor cur{static_cast<uint8_t*>(ws), 0};
-  L.bits = cur.take<uint32_t>(16 * static_cast<size_t>(L.nblk) + 16);
+  L.bits = cur.take<uint32_t>(64 * static_cast<size_t>(L.nsb) + 16);
   L.dir = cur.take<uint32_t>(3 * (static_cast<size_t>(L.nblk) + 1));
+  L.dir2048 = cur.take<uint64_t>(static_cast<size_t>(L.nsb) + 1);
   L.cnt = cur.take<uint32_t>(static_cast<size_t>(L.nblk) + 1);
   L.prefix = cur.take<uint32_t>(static_cast<size_t>(L.nblk) + 2);
   L.scan_bytes = scan_ws(L.nblk + 1);
@@ -214,16 +398,31 @@ static RankLayout rank_layout(void* ws, uint32_t nbits) {
 
 size_t rank_ws(uint32_t nbits) { return align_up(rank_layout(nullptr, nbits).used, 256); }
 
-size_t collision_ws(uint32_t nA, uint32_t nB) {
-  return align_up(rank_ws(nA) + 256 + static_cast<size_t>(nB) * sizeof(uint32_t), 256);
+// Collision workspace of one mode: the rank layout, the saved B lower bounds
+// and (compact mode) the compact A list.
+static size_t collision_mode_ws(uint32_t nA, uint32_t nB, uint32_t mode) {
+  size_t b = rank_ws(nA) + align_up(static_cast<size_t>(nB) * sizeof(uint32_t) + 4, 256);
+  if (mode == EM_COLLISION_512_COMPACT) b += align_up(static_cast<size_t>(nA) * sizeof(uint32_t) + 4, 256);
+  return b;
 }
+
+size_t collision_ws(uint32_t nA, uint32_t nB) { return collision_mode_ws(nA, nB, EM_COLLISION_512_COMPACT); }
 
 static inline uint32_t blocks_for(uint64_t n) {
   return static_cast<uint32_t>((n + kColBlock - 1) / kColBlock);
 }
 
 // count -> scan -> finish over a bitmap already in L.bits
-static int rank_build(RankLayout& L, hipStream_t st) {
+static int rank_build(RankLayout& L, bool r2048, hipStream_t st) {
+  if (r2048) {
+    hipLaunchKernelGGL(k_rank2048_count, dim3(blocks_for(L.nsb + 1)), dim3(kColBlock), 0, st, L.bits, L.nsb,
+                       L.cnt);
+    int rc = scan_launch<uint32_t>(L.cnt, L.nsb + 1, L.prefix, L.scan_ws, L.scan_bytes, st);
+    if (rc) return rc;
+    hipLaunchKernelGGL(k_rank2048_finish, dim3(blocks_for(L.nsb + 1)), dim3(kColBlock), 0, st, L.bits,
+                       L.nsb, L.prefix, L.dir2048);
+    return check_launch();
+  }
   hipLaunchKernelGGL(k_rank_count, dim3(blocks_for(L.nblk + 1)), dim3(kColBlock), 0, st, L.bits, L.nblk,
                      L.cnt);
   int rc = scan_launch<uint32_t>(L.cnt, L.nblk + 1, L.prefix, L.scan_ws, L.scan_bytes, st);
@@ -233,58 +432,119 @@ static int rank_build(RankLayout& L, hipStream_t st) {
   return check_launch();
 }
 
-}  // namespace em
-
-using namespace em;
-
-extern "C" size_t em_rank512_workspace_bytes(uint32_t nbits) { return rank_ws(nbits); }
-
-extern "C" int em_collision_rank(const em_side_t* A, const em_side_t* B, uint32_t* final_refs,
-                                 uint32_t* ord_A, uint32_t* ord_B, uint32_t* d_S, void* ws,
-                                 size_t ws_bytes, void* stream) {
-  int rc = check_pair(A, B);
+static int collision_run(const em_side_t& A, const em_side_t& B, uint32_t mode, uint32_t* final_refs,
+                         uint32_t* ord_A, uint32_t* ord_B, uint32_t* d_S, void* ws, hipStream_t st) {
+  RankLayout L = rank_layout(ws, A.n);
+  uint8_t* after = static_cast<uint8_t*>(ws) + align_up(L.used, 256);
+  uint32_t* lb = reinterpret_cast<uint32_t*>(after);
+  uint32_t* cA = reinterpret_cast<uint32_t*>(after + align_up(static_cast<size_t>(B.n) * 4 + 4, 256));
+  clear_u32(L.bits, 64 * static_cast<size_t>(L.nsb) + 16, st);
+  if (B.n) hipLaunchKernelGGL(k_mark, dim3(blocks_for(B.n)), dim3(kColBlock), 0, st, A, B, L.bits, lb);
+  int rc = check_launch();
   if (rc) return rc;
-  if (!final_refs || !d_S || !ws) return EM_EINVAL;
-  if (reinterpret_cast<uintptr_t>(ws) & 255) return EM_EINVAL;
-  if (ws_bytes < collision_ws(A->n, B->n)) return EM_ENOSPC;
-  hipStream_t st = as_stream(stream);
-  RankLayout L = rank_layout(ws, A->n);
-  uint32_t* lb = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + align_up(L.used, 256));
-  clear_u32(L.bits, 16 * static_cast<size_t>(L.nblk) + 16, st);
-  if (B->n)
-    hipLaunchKernelGGL(k_mark, dim3(blocks_for(B->n)), dim3(kColBlock), 0, st, *A, *B, L.bits, lb);
-  rc = check_launch();
+  const bool r2048 = mode == EM_COLLISION_2048;
+  rc = rank_build(L, r2048, st);
   if (rc) return rc;
-  rc = rank_build(L, st);
-  if (rc) return rc;
-  RankView rv{L.bits, L.dir};
-  if (B->n)
-    hipLaunchKernelGGL(k_scatter_B, dim3(blocks_for(B->n)), dim3(kColBlock), 0, st, A->n, B->n, rv, lb,
-                       final_refs, ord_B);
-  if (A->n)
-    hipLaunchKernelGGL(k_scatter_A, dim3(blocks_for((A->n + kTileA - 1) / kTileA)), dim3(kColBlock), 0,
-                       st, A->n, B->n, rv, lb, final_refs, ord_A);
-  hipLaunchKernelGGL(k_collision_total, dim3(1), dim3(1), 0, st, A->n, B->n, rv, d_S);
+  const Rank512View v512{L.bits, L.dir};
+  const Rank2048View v2048{L.bits, L.dir2048};
+  if (mode == EM_COLLISION_512_COMPACT) {
+    if (A.n)
+      hipLaunchKernelGGL(k_compact_A, dim3(blocks_for((A.n + 31) / 32)), dim3(kColBlock), 0, st, A.n, v512,
+                         cA, ord_A);
+    const uint64_t N = static_cast<uint64_t>(A.n) + B.n;  // a bound on the merged count
+    if (N)
+      hipLaunchKernelGGL(k_merge_compact, dim3(static_cast<uint32_t>((N + kMcItems - 1) / kMcItems)),
+                         dim3(kColBlock), 0, st, A, B, v512, cA, final_refs, ord_A, ord_B);
+    hipLaunchKernelGGL(k_collision_total<Rank512View>, dim3(1), dim3(1), 0, st, A.n, B.n, v512, d_S);
+    return check_launch();
+  }
+  if (r2048) {
+    if (B.n)
+      hipLaunchKernelGGL(k_scatter_B<Rank2048View>, dim3(blocks_for(B.n)), dim3(kColBlock), 0, st, A.n, B.n,
+                         v2048, lb, final_refs, ord_B);
+    if (A.n)
+      hipLaunchKernelGGL(k_scatter_A_search<Rank2048View>, dim3(blocks_for(A.n)), dim3(kColBlock), 0, st, A,
+                         B, v2048, final_refs, ord_A);
+    hipLaunchKernelGGL(k_collision_total<Rank2048View>, dim3(1), dim3(1), 0, st, A.n, B.n, v2048, d_S);
+    return check_launch();
+  }
+  if (B.n)
+    hipLaunchKernelGGL(k_scatter_B<Rank512View>, dim3(blocks_for(B.n)), dim3(kColBlock), 0, st, A.n, B.n,
+                       v512, lb, final_refs, ord_B);
+  if (A.n) {
+    if (mode == EM_COLLISION_512_TILED)
+      hipLaunchKernelGGL(k_scatter_A, dim3(blocks_for((A.n + kTileA - 1) / kTileA)), dim3(kColBlock), 0, st,
+                         A.n, B.n, v512, lb, final_refs, ord_A);
+    else
+      hipLaunchKernelGGL(k_scatter_A_search<Rank512View>, dim3(blocks_for(A.n)), dim3(kColBlock), 0, st, A,
+                         B, v512, final_refs, ord_A);
+  }
+  hipLaunchKernelGGL(k_collision_total<Rank512View>, dim3(1), dim3(1), 0, st, A.n, B.n, v512, d_S);
   return check_launch();
 }
 
-extern "C" int em_rank512_probe(const uint32_t* bitmap, uint32_t nbits, const uint32_t* positions,
-                                uint32_t npos, uint32_t* out, void* ws, size_t ws_bytes, void* stream) {
+static int rank_probe(const uint32_t* bitmap, uint32_t nbits, const uint32_t* positions, uint32_t npos,
+                      uint32_t* out, void* ws, size_t ws_bytes, void* stream, bool r2048) {
   if (!ws || (npos && (!positions || !out)) || (nbits && !bitmap)) return EM_EINVAL;
   if (reinterpret_cast<uintptr_t>(ws) & 255) return EM_EINVAL;
   if (nbits >= EM_MAX_RECORDS + (1u << 13)) return EM_ERANGE;
   if (ws_bytes < rank_ws(nbits)) return EM_ENOSPC;
   hipStream_t st = as_stream(stream);
   RankLayout L = rank_layout(ws, nbits);
-  const uint32_t nwords = 16 * L.nblk + 16;
+  const uint32_t nwords = 64 * L.nsb + 16;
   hipLaunchKernelGGL(k_copy_bits, dim3(blocks_for(nwords)), dim3(kColBlock), 0, st, bitmap, nbits, L.bits,
                      nwords);
   int rc = check_launch();
   if (rc) return rc;
-  rc = rank_build(L, st);
+  rc = rank_build(L, r2048, st);
   if (rc) return rc;
-  if (npos)
-    hipLaunchKernelGGL(k_rank_probe, dim3(blocks_for(npos)), dim3(kColBlock), 0, st,
-                       RankView{L.bits, L.dir}, positions, npos, nbits, out);
+  if (npos) {
+    if (r2048)
+      hipLaunchKernelGGL(k_rank_probe<Rank2048View>, dim3(blocks_for(npos)), dim3(kColBlock), 0, st,
+                         Rank2048View{L.bits, L.dir2048}, positions, npos, nbits, out);
+    else
+      hipLaunchKernelGGL(k_rank_probe<Rank512View>, dim3(blocks_for(npos)), dim3(kColBlock), 0, st,
+                         Rank512View{L.bits, L.dir}, positions, npos, nbits, out);
+  }
   return check_launch();
+}
+
+}  // namespace em
+
+using namespace em;
+
+extern "C" size_t em_rank512_workspace_bytes(uint32_t nbits) { return rank_ws(nbits); }
+extern "C" size_t em_rank2048_workspace_bytes(uint32_t nbits) { return rank_ws(nbits); }
+
+extern "C" size_t em_collision_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t mode) {
+  return collision_mode_ws(nA, nB, mode);
+}
+
+extern "C" int em_collision_rank_mode(const em_side_t* A, const em_side_t* B, uint32_t mode,
+                                      uint32_t* final_refs, uint32_t* ord_A, uint32_t* ord_B, uint32_t* d_S,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_pair(A, B);
+  if (rc) return rc;
+  if (mode > EM_COLLISION_512_COMPACT) return EM_EINVAL;
+  if (!final_refs || !d_S || !ws) return EM_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return EM_EINVAL;
+  if (ws_bytes < collision_mode_ws(A->n, B->n, mode)) return EM_ENOSPC;
+  return collision_run(*A, *B, mode, final_refs, ord_A, ord_B, d_S, ws, as_stream(stream));
+}
+
+extern "C" int em_collision_rank(const em_side_t* A, const em_side_t* B, uint32_t* final_refs,
+                                 uint32_t* ord_A, uint32_t* ord_B, uint32_t* d_S, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return em_collision_rank_mode(A, B, EM_COLLISION_512_TILED, final_refs, ord_A, ord_B, d_S, ws, ws_bytes,
+                                stream);
+}
+
+extern "C" int em_rank512_probe(const uint32_t* bitmap, uint32_t nbits, const uint32_t* positions,
+                                uint32_t npos, uint32_t* out, void* ws, size_t ws_bytes, void* stream) {
+  return rank_probe(bitmap, nbits, positions, npos, out, ws, ws_bytes, stream, false);
+}
+
+extern "C" int em_rank2048_probe(const uint32_t* bitmap, uint32_t nbits, const uint32_t* positions,
+                                 uint32_t npos, uint32_t* out, void* ws, size_t ws_bytes, void* stream) {
+  return rank_probe(bitmap, nbits, positions, npos, out, ws, ws_bytes, stream, true);
 }

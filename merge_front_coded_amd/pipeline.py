@@ -3,7 +3,8 @@
 Paths:
   merge      partition -> merge_keep -> [host reads S] -> fc_lengths -> scan
              -> [host reads T] -> emit  (the six-call C ABI)
-  collision  collision_rank instead of partition + merge_keep
+  collision  collision_rank_mode (collision_mode: "512", "2048", "512-tiled",
+             "512-compact") instead of partition + merge_keep
   fused      partition -> merge_lengths (merge, keep, LCPs, lengths, bit
              offsets) -> emit_merged (the emitter); S and T stay on the
              device.  one_call=True runs the same work as em_merge_fc.
@@ -41,7 +42,7 @@ class Pipeline:
     def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int | None = None,
                  path: str = "merge", keep_ordinals: bool = True, keep_lcp: bool = True,
                  keep_all: bool = True, coarse_parts: int = _FUSE_COARSE_PARTS, one_call: bool = False,
-                 device="cuda"):
+                 collision_mode: str = "512-tiled", device="cuda"):
         if path not in ("merge", "collision", "fused"):
             raise ValueError("path is 'merge', 'collision' or 'fused'")
         self.A, self.B = A, B
@@ -52,6 +53,9 @@ class Pipeline:
             self.items = int(items_per_part) if items_per_part else choose_items_per_part(A, B)
             self.coarse = 0
         self.path = path
+        if collision_mode not in em.COLLISION_MODES:
+            raise ValueError(f"collision_mode is one of {sorted(em.COLLISION_MODES)}")
+        self.collision_mode = em.COLLISION_MODES[collision_mode]
         self.keep_all = keep_all
         self.one_call = one_call
         N = A.n + B.n
@@ -72,6 +76,8 @@ class Pipeline:
         ws_bytes = em.em_workspace_bytes(A.n, B.n, min(self.items, 4096))
         if path == "fused":
             ws_bytes = max(ws_bytes, em.em_merge_fc_workspace_bytes(A.n, B.n, self.items))
+        if path == "collision":
+            ws_bytes = max(ws_bytes, em.em_collision_workspace_bytes(A.n, B.n, self.collision_mode))
         self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)
         self.S = 0
         self.T = 0
@@ -106,7 +112,8 @@ class Pipeline:
             em.em_merge_keep(A, B, self.splits, self.items, self.final, self.ord_A, self.ord_B,
                              self.d_S, self.ws, stream)
         else:
-            em.em_collision_rank(A, B, self.final, self.ord_A, self.ord_B, self.d_S, self.ws, stream)
+            em.em_collision_rank_mode(A, B, self.collision_mode, self.final, self.ord_A, self.ord_B, self.d_S,
+                                      self.ws, stream)
         S = int(self.d_S.item()) & 0xFFFFFFFF
         em.em_fc_lengths(A, B, self.final, S, self.len_bits, self.lcp, self.ws, stream)
         em.em_scan(self.len_bits, S, self.off, self.ws, stream)

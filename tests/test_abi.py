@@ -113,3 +113,13 @@ def test_argument_errors_before_any_launch(lib):
     assert lib.em_emit(ctypes.byref(A5), ctypes.byref(B), buf, None, 2, buf, 100, buf, 3, buf, 0,
                        None) == -3
     assert lib.em_rank512_probe(None, 5, None, 0, None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    assert lib.em_rank2048_probe(None, 5, None, 0, None, ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    assert lib.em_rank2048_probe(buf, 5, None, 0, None, ctypes.c_void_p(0x100000), 0, None) == -3
+    # collision modes: an unknown mode, and each mode's own workspace size
+    assert lib.em_collision_rank_mode(ctypes.byref(A5), ctypes.byref(B), 4, buf, None, None, buf,
+                                      ctypes.c_void_p(0x100000), 1 << 20, None) == -1
+    compact = lib.em_collision_workspace_bytes(1000, 10, 3)
+    assert compact >= lib.em_collision_workspace_bytes(1000, 10, 2) + 4000
+    assert lib.em_collision_rank_mode(ctypes.byref(A5), ctypes.byref(B), 3, buf, None, None, buf,
+                                      ctypes.c_void_p(0x100000), lib.em_collision_workspace_bytes(5, 0, 2),
+                                      None) == -3

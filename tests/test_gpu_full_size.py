@@ -43,9 +43,11 @@ def test_full_size_workload_matches_oracle(wid):
     A, B = gen.make(wid)
     assert _sha(A.keys, A.key_off, A.vals, A.val_off, A.tomb, B.keys, B.key_off, B.vals, B.val_off,
                 B.tomb) == ref["input"], "generator output drifted from the digested inputs"
-    for path in ("fused", "merge", "collision"):
-        print(f"  path {path}", flush=True)
-        pl = run_gpu(A, B, items=None, path=path)
+    runs = [("fused", {}), ("merge", {})] + [("collision", {"collision_mode": m})
+                                             for m in ("512-tiled", "512", "2048", "512-compact")]
+    for path, kw in runs:
+        print(f"  path {path} {kw}", flush=True)
+        pl = run_gpu(A, B, items=None, path=path, **kw)
         torch.cuda.synchronize()
         S = pl.S
         assert S == ref["S"], f"{path}: S {S} != {ref['S']}"

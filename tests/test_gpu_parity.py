@@ -177,11 +177,18 @@ def test_scan_random_lengths_many_tiles():
         assert np.array_equal(got, want), f"scan n={n}"
 
 
-def test_rank512_probe_boundaries():
+@pytest.mark.parametrize("layout", ["512", "2048"])
+def test_rank_probe_boundaries(layout):
+    """GPU rank queries of both temporary layouts against the oracle's prefix
+    counts, at every position of small maps and at block and run edges of
+    large ones, on all-zero, all-one, sparse and random maps."""
     import torch
     import merge_front_coded_amd as em
+    probe = em.em_rank512_probe if layout == "512" else em.em_rank2048_probe
+    ws_bytes = em.em_rank512_workspace_bytes if layout == "512" else em.em_rank2048_workspace_bytes
     rng = np.random.default_rng(7)
-    for nbits in (0, 1, 31, 32, 33, 63, 64, 65, 511, 512, 513, 2047, 2048, 2049, 100_003):
+    for nbits in (0, 1, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 1535, 1536, 1537, 2047, 2048,
+                  2049, 4095, 4096, 4097, 100_003):
         for fill in ("zero", "one", "sparse", "random"):
             bits = {"zero": np.zeros(nbits, np.uint8), "one": np.ones(nbits, np.uint8),
                     "sparse": (rng.random(nbits) < 0.01).astype(np.uint8),
@@ -195,16 +202,18 @@ def test_rank512_probe_boundaries():
             if nbits <= 4096:
                 pos = np.arange(nbits + 1, dtype=np.uint32)
             else:
-                pos = np.unique(np.concatenate([rng.integers(0, nbits + 1, 5000),
-                                                [0, 31, 32, 33, 511, 512, 513, nbits]])).astype(np.uint32)
+                edges = np.arange(0, nbits + 1, 512, dtype=np.int64)
+                pos = np.concatenate([rng.integers(0, nbits + 1, 5000), [0, 31, 32, 33, 63, 64, 65, nbits],
+                                      edges, edges - 1, edges + 1])
+                pos = np.unique(pos[(pos >= 0) & (pos <= nbits)]).astype(np.uint32)
             want = oracle.rank(_masked(words, nbits), pos)
             dev_words = torch.from_numpy(words.view(np.int32)).cuda()
             dev_pos = torch.from_numpy(pos.view(np.int32)).cuda()
             out = torch.empty(max(pos.size, 1), dtype=torch.int32, device="cuda")
-            ws = torch.empty(em.em_rank512_workspace_bytes(nbits), dtype=torch.uint8, device="cuda")
-            em.em_rank512_probe(dev_words, nbits, dev_pos, out, ws)
+            ws = torch.empty(ws_bytes(nbits), dtype=torch.uint8, device="cuda")
+            probe(dev_words, nbits, dev_pos, out, ws)
             got = out.cpu().numpy().view(np.uint32)[:pos.size]
-            assert np.array_equal(got, want), f"rank nbits={nbits} fill={fill}"
+            assert np.array_equal(got, want), f"rank{layout} nbits={nbits} fill={fill}"
 
 
 def _masked(words, nbits):
