@@ -10,7 +10,10 @@ names the passage of the pages its C function follows.
 
 Pinned by the ``-m "not gpu"`` tests against the pages' worked merge examples,
 brute-force set semantics, the closed-form record length, an independent
-decoder and hand-derived payloads.  No function here is "parity unpinned".
+decoder and hand-derived payloads; the navigation sections by hand-derived
+sections, an independent section reader (every entry selected back), the
+exact sparse threshold and value widths read back from decoded payloads.  No
+function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -66,6 +69,10 @@ def _load():
         lib.or_collision.argtypes = [S, S, P, P, P, P, P, P]
         lib.or_rank.restype = u32
         lib.or_rank.argtypes = [P, u32]
+        lib.or_common_width.restype = ctypes.c_uint64
+        lib.or_common_width.argtypes = [S, S, P, u32]
+        lib.or_ef_entries.argtypes = [P, u32, ctypes.c_uint64, ctypes.c_uint64, P]
+        lib.or_ef_encode.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -174,6 +181,55 @@ def rank(words: np.ndarray, positions) -> np.ndarray:
     w = np.ascontiguousarray(words, dtype=np.uint32)
     lib = _load()
     return np.asarray([lib.or_rank(_ptr(w), int(p)) for p in positions], dtype=np.uint32)
+
+
+class _EfInfo(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in ("n", "L", "width", "low_words", "high_bits", "high_words",
+                                               "groups", "exceptions")]
+
+
+def common_width(A, B, final: np.ndarray) -> int:
+    """The encoded value width all survivors share, else 0 (0 when S = 0)."""
+    f = np.ascontiguousarray(final, dtype=np.uint32)
+    return int(_load().or_common_width(ctypes.byref(_side(A)), ctypes.byref(_side(B)), _ptr(f), f.size))
+
+
+def ef_entries(off: np.ndarray, S: int, T: int, width: int) -> np.ndarray:
+    """Offsets at ordinals 0, 15, 30, ... and EOF, less width x ordinal."""
+    o = np.ascontiguousarray(off, dtype=np.uint64)
+    e = np.empty((S + 14) // 15 + 1, np.uint64)
+    _load().or_ef_entries(_ptr(o), S, T, width, _ptr(e))
+    return e
+
+
+def ef_encode(entries: np.ndarray, width: int = 0) -> dict:
+    """Elias-Fano sections of non-decreasing entries -> dict(lows, highs,
+    samples, exceptions, and the header fields n, L, width, low_words,
+    high_bits, high_words, groups, n_exceptions)."""
+    e = np.ascontiguousarray(entries, dtype=np.uint64)
+    n = int(e.size)
+    if n == 0:
+        raise ValueError("at least one entry (the EOF entry) is needed")
+    lows = np.zeros(n + 1, np.uint64)
+    highs = np.zeros((3 * n + 1 + 63) // 64 + 1, np.uint64)
+    groups = (n + 255) // 256
+    samples = np.zeros(2 * groups, np.uint64)
+    exc = np.zeros(n, np.uint64)
+    info = _EfInfo()
+    _load().or_ef_encode(_ptr(e), n, width, _ptr(lows), _ptr(highs), _ptr(samples), _ptr(exc),
+                         ctypes.byref(info))
+    out = {f: int(getattr(info, f)) for f, _ in _EfInfo._fields_}
+    out["n_exceptions"] = out.pop("exceptions")
+    out.update(lows=lows[:info.low_words].copy(), highs=highs[:info.high_words].copy(), samples=samples,
+               exceptions=exc[:info.exceptions].copy())
+    return out
+
+
+def ef_navigation(A, B, final: np.ndarray, off: np.ndarray, T: int) -> dict:
+    """The output navigation of a merged payload: common width, entries, EF sections."""
+    S = int(final.shape[0])
+    w = common_width(A, B, final)
+    return ef_encode(ef_entries(off, S, T, w), w)
 
 
 def run(A, B, items_per_part: int = 2048):

@@ -22,7 +22,9 @@
  *        fields, value framing, E(x) and the record length, MSB-first bits,
  *        no padding, word-owned payload with zero unused final bits) and the
  *        prefix-cache paragraph (proper-prefix order, LCP clamped to the
- *        shorter key).
+ *        shorter key); the KV03 and output-EF paragraphs for the output
+ *        navigation (sampled offsets, common value width, Elias-Fano lows
+ *        and highs, 256-entry groups, the 4096-bit sparse threshold).
  *  [CB]  Everett, "Collision bitmap and rank experiment": "Corrected record
  *        ordinals" (collision bits, exclusive rank R, ordinal formulas).
  *
@@ -278,4 +280,107 @@ uint32_t or_rank(const uint32_t *words, uint32_t p) {
   uint32_t c = 0;
   for (uint32_t q = 0; q < p; ++q) c += (words[q >> 5] >> (q & 31)) & 1u;
   return c;
+}
+
+/*
+ * [GC] Output navigation.  The KV03 paragraph: physical offsets are sampled
+ * at ordinals 0, 15, 30, ... plus EOF, and when every encoded value has the
+ * same width, that width times the sample's ordinal is subtracted from the
+ * offset.  The output-EF paragraph: each entry comes from the record-offset
+ * scan (the last from the payload extent); the entries are Elias-Fano coded
+ * into packed lows and high bits; every group of 256 entries whose positions
+ * in the high bits span at least 4096 bits is sparse, and a scan of the
+ * sparse groups' sizes assigns them ranges of explicit exception positions;
+ * each group has a sample pair.
+ *
+ * Readings (the section layouts are not printed on the pages):
+ *  - value width of record i: 1 for a tombstone, else 1 + E(len) + 8 len;
+ *    the common width w is that width when all S records share it, else 0
+ *    (and 0 when S = 0);
+ *  - entries: n = ceil(S/15) + 1; e_k = off[15k] - 15k w for 15k < S, and
+ *    the last entry e_{n-1} = T - S w;
+ *  - low width L = floor(log2(floor((e_{n-1} + 1) / n))), 0 when that
+ *    quotient is 0;
+ *  - lows: entry k's low L bits at bit k L of little-endian 64-bit words
+ *    (bit b is bit b mod 64 of word b/64); unused bits zero;
+ *  - high bits: bit (e_k >> L) + k set, n + (e_{n-1} >> L) bits long, same
+ *    word order;
+ *  - group g holds entries 256g .. min(256g + 256, n) - 1; its span is
+ *    p_last - p_first + 1 with p_k = (e_k >> L) + k; sparse when >= 4096;
+ *  - sample pair of group g: (p_first, number of exception entries of the
+ *    groups before g);
+ *  - exceptions: the p_k of every entry of a sparse group, in order.
+ */
+typedef struct {
+  uint64_t n, L, width, low_words, high_bits, high_words, groups, exceptions;
+} or_ef_info;
+
+/* Encoded value width of survivor i (record grammar: 0 for a tombstone;
+ * 1, EG0(byte length) and the bytes otherwise). */
+static uint64_t eg0_bits(uint64_t x) {
+  unsigned z = 0;
+  while ((x + 1) >> (z + 1)) ++z; /* z = floor(log2(x + 1)) */
+  return 2ull * z + 1;
+}
+
+uint64_t or_common_width(const or_side *A, const or_side *B, const uint32_t *final_refs, uint32_t S) {
+  uint64_t w = 0;
+  for (uint32_t i = 0; i < S; ++i) {
+    uint32_t r;
+    const or_side *s = ref_side(A, B, final_refs[i], &r);
+    uint64_t v = 1;
+    if (!is_tomb(s, r)) {
+      uint64_t len = s->val_off[r + 1] - s->val_off[r];
+      v = 1 + eg0_bits(len) + 8 * len;
+    }
+    if (i == 0)
+      w = v;
+    else if (v != w)
+      return 0;
+  }
+  return w;
+}
+
+/* The n = ceil(S/15) + 1 navigation entries. */
+void or_ef_entries(const uint64_t *off, uint32_t S, uint64_t T, uint64_t w, uint64_t *e) {
+  uint64_t k = 0;
+  for (uint64_t ord = 0; ord < S; ord += 15) e[k++] = off[ord] - ord * w;
+  e[k] = T - (uint64_t)S * w;
+}
+
+static void set_bit64(uint64_t *words, uint64_t b) { words[b >> 6] |= 1ull << (b & 63); }
+
+/* Elias-Fano sections of the non-decreasing entries e[0..n).  The output
+ * arrays must be zeroed and large enough (at most n low words, ceil((3n + 1)
+ * / 64) high words, 2 ceil(n / 256) sample words, n exception words). */
+void or_ef_encode(const uint64_t *e, uint64_t n, uint64_t width, uint64_t *lows, uint64_t *highs,
+                  uint64_t *samples, uint64_t *exc, or_ef_info *info) {
+  const uint64_t last = e[n - 1];
+  const uint64_t q = (last + 1) / n;
+  uint64_t L = 0;
+  while (q >> (L + 1)) ++L; /* floor(log2 q) for q >= 1; 0 for q = 0 */
+  for (uint64_t k = 0; k < n; ++k) {
+    for (uint64_t b = 0; b < L; ++b)
+      if ((e[k] >> b) & 1) set_bit64(lows, k * L + b);
+    set_bit64(highs, (e[k] >> L) + k);
+  }
+  const uint64_t high_bits = n + (last >> L);
+  const uint64_t groups = (n + 255) / 256;
+  uint64_t nexc = 0;
+  for (uint64_t g = 0; g < groups; ++g) {
+    const uint64_t k0 = 256 * g, k1 = (k0 + 256 < n ? k0 + 256 : n);
+    const uint64_t p0 = (e[k0] >> L) + k0, p1 = (e[k1 - 1] >> L) + (k1 - 1);
+    samples[2 * g] = p0;
+    samples[2 * g + 1] = nexc;
+    if (p1 - p0 + 1 >= 4096)
+      for (uint64_t k = k0; k < k1; ++k) exc[nexc++] = (e[k] >> L) + k;
+  }
+  info->n = n;
+  info->L = L;
+  info->width = width;
+  info->low_words = (n * L + 63) / 64;
+  info->high_bits = high_bits;
+  info->high_words = (high_bits + 63) / 64;
+  info->groups = groups;
+  info->exceptions = nexc;
 }

@@ -297,3 +297,93 @@ def test_key_order_proper_prefix_and_unsigned_bytes():
     assert oracle.key_cmp(A, 1, B, 2) < 0      # 0x61 < 0x62 regardless of later bytes
     assert oracle.key_cmp(A, 2, B, 2) > 0      # 0xff is large: unsigned bytes
     assert oracle.key_cmp(A, 0, A, 0) == 0
+
+
+# ---- output navigation: Elias-Fano sections of the sampled offsets ----
+
+def test_ef_hand_examples():
+    # e = 0, 5, 9, 20: (20 + 1) // 4 = 5 -> L = 2.  Lows 0, 1, 1, 0 at bits
+    # 0, 2, 4, 6 -> 0b00010100.  Highs: e >> 2 = 0, 1, 2, 5, plus k -> bits
+    # 0, 2, 4, 8 -> 0x115, 4 + 5 = 9 bits.  One group, span 9: dense.
+    r = oracle.ef_encode(np.array([0, 5, 9, 20], np.uint64))
+    assert (r["n"], r["L"], r["high_bits"], r["groups"], r["n_exceptions"]) == (4, 2, 9, 1, 0)
+    assert [int(x) for x in r["lows"]] == [0x14] and [int(x) for x in r["highs"]] == [0x115]
+    assert [int(x) for x in r["samples"]] == [0, 0]
+    # repeated entries 0, 0, 1, 3: (3 + 1) // 4 = 1 -> L = 0, no low words;
+    # highs at 0, 1, 3, 6 -> 0b1001011, 4 + 3 = 7 bits.
+    r = oracle.ef_encode(np.array([0, 0, 1, 3], np.uint64))
+    assert (r["L"], r["low_words"], r["high_bits"]) == (0, 0, 7)
+    assert [int(x) for x in r["highs"]] == [0x4B]
+    # a single entry (empty payload): L = 0, high bit 0
+    r = oracle.ef_encode(np.array([0], np.uint64))
+    assert (r["n"], r["L"], r["high_bits"], [int(x) for x in r["highs"]]) == (1, 0, 1, [1])
+
+
+@pytest.mark.parametrize("n", [1, 2, 255, 256, 257, 700, 3000])
+def test_ef_round_trip(n):
+    from efdecode import popcount, select_all
+    rng = np.random.default_rng(n)
+    for shape in ("uniform", "clustered", "repeats"):
+        if shape == "uniform":
+            gaps = rng.integers(0, 1000, n)
+        elif shape == "clustered":  # long quiet stretches, then bursts: sparse groups
+            gaps = np.where(rng.random(n) < 0.02, rng.integers(10 ** 5, 10 ** 6, n), rng.integers(0, 3, n))
+        else:
+            gaps = rng.integers(0, 2, n)
+        e = np.cumsum(gaps).astype(np.uint64)
+        r = oracle.ef_encode(e)
+        assert select_all(r) == [int(x) for x in e], f"n={n} {shape}"
+        assert popcount(r["highs"]) == n
+        # canonical padding: nothing set past the sections' lengths
+        assert r["high_bits"] == n + (int(e[-1]) >> r["L"])
+        if r["high_bits"] % 64:
+            assert int(r["highs"][-1]) >> (r["high_bits"] % 64) == 0
+        if (n * r["L"]) % 64:
+            assert int(r["lows"][-1]) >> ((n * r["L"]) % 64) == 0
+        # L = floor(log2((last + 1) // n)) from its definition
+        q = (int(e[-1]) + 1) // n
+        assert r["L"] == (q.bit_length() - 1 if q else 0)
+
+
+@pytest.mark.parametrize("top", [3839, 3840])
+def test_ef_sparse_threshold(top):
+    # 2048 entries, all at most 3840, so (3840 + 1) // 2048 = 1 and L = 0:
+    # position p_k = e_k + k.  Group 0 runs from e_0 = 0 to e_255 = top, so its
+    # span is top + 255 + 1: 4095 (dense) or 4096 (sparse).  The other groups
+    # sit on one value and span 256.
+    e = np.concatenate([np.linspace(0, top, 256).round(), np.full(2048 - 256, 3840)]).astype(np.uint64)
+    r = oracle.ef_encode(e)
+    assert r["L"] == 0
+    sparse = top + 256 >= 4096
+    assert r["n_exceptions"] == (256 if sparse else 0)
+    if sparse:
+        assert [int(x) for x in r["exceptions"]] == [int(e[k]) + k for k in range(256)]
+    assert [int(x) for x in r["samples"][1::2]] == [0] + [256 if sparse else 0] * 7
+    from efdecode import select_all
+    assert select_all(r) == [int(x) for x in e]
+
+
+def test_ef_navigation_of_merged_payloads():
+    # the hand-derived merge: widths 1 (tombstone), 1 + E(1) + 8 = 12 and
+    # 1 + E(0) = 2 differ, so w = 0: entries off[0] = 0 and T = 73
+    A = gen.side_from_records([(b"ab", b"1"), (b"b", b"")])
+    B = gen.side_from_records([(b"ab", None), (b"abc", b"Z")])
+    r = oracle.run(A, B)
+    nav = oracle.ef_navigation(A, B, r["final"], r["off"], r["T"])
+    assert nav["width"] == 0 and nav["n"] == 2
+    from efdecode import select_all
+    assert select_all(nav) == [0, 73]
+    # fixed-width values: every record's value is 1 + E(16) + 128 = 138 bits,
+    # read back from the payload by the independent decoder
+    keys = [b"k%04d" % i for i in range(40)]
+    A = gen.side_from_records([(k, bytes(16)) for k in keys[::2]])
+    B = gen.side_from_records([(k, bytes([i]) * 16) for i, k in enumerate(keys[1::2])])
+    r = oracle.run(A, B)
+    recs, info = decode(r["payload"].tobytes(), r["T"], r["S"])
+    widths = {i["length"] - eg0_length(i["c"]) - eg0_length(i["k"] - i["l"]) - (i["k"] - i["l"]) for i in info}
+    assert widths == {138}
+    nav = oracle.ef_navigation(A, B, r["final"], r["off"], r["T"])
+    assert nav["width"] == 138 and nav["n"] == (40 + 14) // 15 + 1
+    starts = [i["start"] for i in info]
+    want = [starts[o] - 138 * o for o in range(0, 40, 15)] + [r["T"] - 138 * 40]
+    assert select_all(nav) == want
