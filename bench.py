@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-scale", type=float, default=0.125,
                     help="fraction of the workload the CPU oracle is timed on")
+    ap.add_argument("--navigation", action="store_true",
+                    help="also time em_ef_navigation (the output navigation) on the step's outputs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -274,6 +276,34 @@ def main():
                      "algorithmic_bytes_per_launch": alg[dominant],
                      "avg_launch_ms": per_call_ms[dominant]},
     }
+    if args.navigation:
+        # the output navigation built from this step's outputs (the step after
+        # emit; not part of the timed step above)
+        if fused:
+            pn = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
+            pn.run()
+        else:
+            pn = pl
+        for _ in range(2):
+            pn.ef_navigation()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(args.steps):
+            pn.ef_navigation(stream)
+        e.record(stream)
+        torch.cuda.synchronize()
+        nav = pn.nav.host()
+        nav_ms = s.elapsed_time(e) / args.steps
+        # reads: final refs, value offset pairs and tombstones for the common
+        # width, the sampled offsets; writes: the sections
+        nav_bytes = pn.S * (4 + 8 + 1) + 8 * nav["n"] + 8 * (nav["low_words"] + nav["high_words"] +
+                                                             2 * nav["groups"] + nav["n_exceptions"])
+        result["navigation"] = {"call": "em_ef_navigation", "ms": nav_ms, "entries": nav["n"], "L": nav["L"],
+                                "width": nav["width"], "sparse_entries": nav["n_exceptions"],
+                                "algorithmic_bytes": nav_bytes, "GBps": nav_bytes / (nav_ms * 1e-3) / 1e9}
+        if pn is not pl:
+            del pn
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")

@@ -280,6 +280,51 @@ int em_rank2048_probe(const uint32_t *bitmap, uint32_t nbits, const uint32_t *po
                       uint32_t *out, void *ws, size_t ws_bytes, void *stream);
 size_t em_rank2048_workspace_bytes(uint32_t nbits);
 
+/*
+ * Output navigation (Everett, "GPU construction experiment": the KV03
+ * paragraph and the output-EF paragraph).  The record offsets are sampled at
+ * ordinals 0, 15, 30, ... and at EOF (n = em_ef_entry_count(S) =
+ * ceil(S/15) + 1 entries; the last is T); when every survivor's encoded value
+ * has the same width w (1 for a tombstone, else 1 + E(len) + 8 len), w times
+ * the ordinal is subtracted.  The entries are Elias-Fano coded:
+ *   L = floor(log2(floor((e_{n-1} + 1) / n))), 0 when that quotient is 0;
+ *   lows[]:       entry k's low L bits at bit k L (bit b is bit b mod 64 of
+ *                 u64 word b / 64);
+ *   highs[]:      bit (e_k >> L) + k set, n + (e_{n-1} >> L) bits;
+ *   samples[]:    per group of 256 entries the pair (position of its first
+ *                 high bit, exception entries of the groups before it);
+ *   exceptions[]: the high-bit position of every entry of each group whose
+ *                 positions span at least 4096 bits, in order.
+ * Unused bits of the last low and high words are zero; words past the
+ * lengths in *info are not written.  info (device memory) receives n, L, w
+ * and the section lengths (low_words, high_bits, high_words, groups,
+ * exceptions).  Each output's capacity in u64 words comes from
+ * em_ef_capacity(n) (at most n, ceil(3n/64), 2 ceil(n/256), n), and the
+ * workspace from em_ef_workspace_bytes(n) (256-byte aligned).  Capacities too
+ * small: EM_ENOSPC.
+ *
+ * em_ef_navigation: from the survivors (final_refs, S), their offsets
+ * off[0..S] and T, after em_scan / em_emit (or em_emit_merged with off).
+ * S = 0 needs T = 0 and gives the one entry 0.
+ * em_ef_encode: from n explicit non-decreasing entries (width is recorded
+ * in info only); n >= 1.
+ */
+typedef struct {
+  uint64_t n, L, width, low_words, high_bits, high_words, groups, exceptions;
+} em_ef_info_t;
+uint32_t em_ef_entry_count(uint32_t S);
+int em_ef_capacity(uint32_t n_entries, uint64_t *low_words, uint64_t *high_words, uint64_t *sample_words,
+                   uint64_t *exception_words);
+size_t em_ef_workspace_bytes(uint32_t n_entries);
+int em_ef_navigation(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs, uint32_t S,
+                     const uint64_t *off, uint64_t T, uint64_t *lows, uint64_t low_cap, uint64_t *highs,
+                     uint64_t high_cap, uint64_t *samples, uint64_t sample_cap, uint64_t *exceptions,
+                     uint64_t exception_cap, em_ef_info_t *info, void *ws, size_t ws_bytes, void *stream);
+int em_ef_encode(const uint64_t *entries, uint32_t n, uint64_t width, uint64_t *lows, uint64_t low_cap,
+                 uint64_t *highs, uint64_t high_cap, uint64_t *samples, uint64_t sample_cap,
+                 uint64_t *exceptions, uint64_t exception_cap, em_ef_info_t *info, void *ws, size_t ws_bytes,
+                 void *stream);
+
 /* Text for an EM_* code (static string). */
 const char *em_strerror(int code);
 

@@ -67,6 +67,12 @@ def load_library(path: str = LIB_PATH):
         "em_merge_lengths": (i32, [S, S, P, u32, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_emit_merged": (i32, [S, S, u32, P, u64, P, P, P, P, P, P, sz, P]),
         "em_rank512_workspace_bytes": (sz, [u32]),
+        "em_ef_entry_count": (u32, [u32]),
+        "em_ef_capacity": (i32, [u32, ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(u64),
+                                 ctypes.POINTER(u64)]),
+        "em_ef_workspace_bytes": (sz, [u32]),
+        "em_ef_navigation": (i32, [S, S, P, u32, P, u64, P, u64, P, u64, P, u64, P, u64, P, P, sz, P]),
+        "em_ef_encode": (i32, [P, u32, u64, P, u64, P, u64, P, u64, P, u64, P, P, sz, P]),
         "em_strerror": (ctypes.c_char_p, [i32]),
         "em_last_hip_error": (i32, []),
     }
@@ -251,3 +257,62 @@ def em_emit_merged(A, B, items_per_part, payload, d_S, d_T, ws, final_refs=None,
     _check(lib().em_emit_merged(ctypes.byref(A.struct), ctypes.byref(B.struct), items_per_part, _p(payload),
                                 payload.numel(), _p(d_S), _p(d_T), _p(final_refs), _p(lcp_bits), _p(off),
                                 _p(ws), ws.numel(), _stream(stream)), "em_emit_merged")
+
+
+# ---- output navigation (include/em.h: em_ef_*) ----
+
+EF_INFO_FIELDS = ("n", "L", "width", "low_words", "high_bits", "high_words", "groups", "exceptions")
+
+
+def em_ef_entry_count(S: int) -> int:
+    return int(lib().em_ef_entry_count(S))
+
+
+def em_ef_capacity(n_entries: int):
+    """u64 word capacities (lows, highs, samples, exceptions) for n entries."""
+    out = [ctypes.c_uint64() for _ in range(4)]
+    _check(lib().em_ef_capacity(n_entries, *[ctypes.byref(o) for o in out]), "em_ef_capacity")
+    return tuple(int(o.value) for o in out)
+
+
+def em_ef_workspace_bytes(n_entries: int) -> int:
+    return int(lib().em_ef_workspace_bytes(n_entries))
+
+
+class EfSections:
+    """Device buffers for the navigation sections of n entries (allocated once)."""
+
+    def __init__(self, n_entries: int, device="cuda"):
+        import torch
+        self.n_entries = n_entries
+        caps = em_ef_capacity(n_entries)
+        i64 = dict(dtype=torch.int64, device=device)
+        self.lows, self.highs, self.samples, self.exceptions = (torch.zeros(max(c, 1), **i64) for c in caps)
+        self.info = torch.zeros(len(EF_INFO_FIELDS), **i64)
+        self.ws = torch.empty(max(em_ef_workspace_bytes(n_entries), 256), dtype=torch.uint8, device=device)
+
+    def _args(self):
+        return (_p(self.lows), self.lows.numel(), _p(self.highs), self.highs.numel(), _p(self.samples),
+                self.samples.numel(), _p(self.exceptions), self.exceptions.numel(), _p(self.info), _p(self.ws),
+                self.ws.numel())
+
+    def host(self) -> dict:
+        """The sections and header as host arrays (synchronizes)."""
+        import numpy as np
+        info = dict(zip(EF_INFO_FIELDS, (int(x) for x in self.info.cpu().numpy().view(np.uint64))))
+        out = dict(info)
+        out["n_exceptions"] = out.pop("exceptions")
+        cut = {"lows": info["low_words"], "highs": info["high_words"], "samples": 2 * info["groups"],
+               "exceptions": info["exceptions"]}
+        for k, n in cut.items():
+            out[k] = getattr(self, k)[:n].cpu().numpy().view(np.uint64).copy()
+        return out
+
+
+def em_ef_navigation(A, B, final_refs, S, off, T, sec: EfSections, stream=None):
+    _check(lib().em_ef_navigation(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), S, _p(off), T,
+                                  *sec._args(), _stream(stream)), "em_ef_navigation")
+
+
+def em_ef_encode(entries, width, sec: EfSections, stream=None):
+    _check(lib().em_ef_encode(_p(entries), entries.numel(), width, *sec._args(), _stream(stream)), "em_ef_encode")

@@ -122,6 +122,20 @@ class Pipeline:
         self.S, self.T = S, T
         return S, T
 
+    def ef_navigation(self, stream=None):
+        """The output navigation sections of the last run (em_ef_navigation),
+        into buffers allocated on first use for the largest possible S.  Needs
+        the survivors' references and offsets: any path but the fused one with
+        keep_all=False."""
+        if self.path == "fused" and not self.keep_all:
+            raise ValueError("the fused path keeps final refs and offsets only with keep_all=True")
+        if getattr(self, "nav", None) is None:
+            self.nav = em.EfSections(em.em_ef_entry_count(self.N))
+        if self.path == "fused":
+            self.read_counts()
+        em.em_ef_navigation(self.A, self.B, self.final, self.S, self.off, self.T, self.nav, stream)
+        return self.nav
+
     def read_counts(self):
         self.S = int(self.d_S.item()) & 0xFFFFFFFF
         self.T = int(self.d_T.item())

@@ -36,6 +36,14 @@ def input_digest(A, B) -> str:
                B.tomb)
 
 
+def ef_digest(nav) -> str:
+    """The navigation header fields and sections, in a fixed order."""
+    import numpy as np
+    head = np.array([nav[k] for k in ("n", "L", "width", "low_words", "high_bits", "high_words", "groups",
+                                      "n_exceptions")], np.uint64)
+    return sha(head, nav["lows"], nav["highs"], nav["samples"], nav["exceptions"])
+
+
 def main(ids):
     data = {}
     if os.path.exists(OUT):
@@ -54,6 +62,7 @@ def main(ids):
             "final": sha(final), "ord_A": sha(ord_A), "ord_B": sha(ord_B),
             "len_bits": sha(len_bits), "lcp_bits": sha(lcp_bits), "off": sha(off),
             "payload": sha(payload), "payload_bytes": int(payload.size),
+            "ef": ef_digest(oracle.ef_navigation(A, B, final, off, T)),
         }
         print(f"workload {wid}: S={S} T={T} ({time.time() - t0:.1f}s)", flush=True)
         with open(OUT, "w") as f:

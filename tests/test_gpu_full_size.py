@@ -1,4 +1,5 @@
-"""Full-size parity: every output of the HIP path on the five full-size
+"""Full-size parity: every output of the HIP path (and the output navigation
+sections built from it) on the five full-size
 workloads, in the benchmark's launch configuration (the partition size the
 pipeline chooses from the mean key length), against SHA-256 digests of the CPU oracle's outputs written by
 tests/golden/make_full_size_digests.py (which calls only gen/ and oracle/).
@@ -61,6 +62,10 @@ def test_full_size_workload_matches_oracle(wid):
             "off": _sha(pl.host("off", S + 1)),
             "payload": _sha(np.frombuffer(pl.payload_bytes(), np.uint8)),
         }
+        nav = pl.ef_navigation().host()
+        head = np.array([nav[k] for k in ("n", "L", "width", "low_words", "high_bits", "high_words", "groups",
+                                          "n_exceptions")], np.uint64)
+        got["ef"] = _sha(head, nav["lows"], nav["highs"], nav["samples"], nav["exceptions"])
         want = dict(ref)
         if path == "merge":
             got["splits"] = _sha(pl.host("splits"))
