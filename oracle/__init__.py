@@ -12,8 +12,10 @@ Pinned by the ``-m "not gpu"`` tests against the pages' worked merge examples,
 brute-force set semantics, the closed-form record length, an independent
 decoder and hand-derived payloads; the navigation sections by hand-derived
 sections, an independent section reader (every entry selected back), the
-exact sparse threshold and value widths read back from decoded payloads.  No
-function here is "parity unpinned".
+exact sparse threshold and value widths read back from decoded payloads; the
+payload decoder by a hand-derived payload, malformed lengths, and round trips
+checked against the merged input records and the independent Python
+decoder.  No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -73,6 +75,8 @@ def _load():
         lib.or_common_width.argtypes = [S, S, P, u32]
         lib.or_ef_entries.argtypes = [P, u32, ctypes.c_uint64, ctypes.c_uint64, P]
         lib.or_ef_encode.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P, P, P, P, P]
+        lib.or_fc_decode.restype = ctypes.c_int
+        lib.or_fc_decode.argtypes = [P, ctypes.c_uint64, u32, P, ctypes.c_uint64, P, P, ctypes.c_uint64, P, P]
         _lib = lib
     return _lib
 
@@ -230,6 +234,26 @@ def ef_navigation(A, B, final: np.ndarray, off: np.ndarray, T: int) -> dict:
     S = int(final.shape[0])
     w = common_width(A, B, final)
     return ef_encode(ef_entries(off, S, T, w), w)
+
+
+def fc_decode(payload: np.ndarray, T: int, S: int, key_cap: int, val_cap: int):
+    """Decode a front-coded payload of S records -> a side (gen.HostSide).
+
+    key_cap / val_cap bound the arenas; raises ValueError on a malformed
+    payload or too small a capacity."""
+    import gen
+    p = np.ascontiguousarray(payload, dtype=np.uint8)
+    keys = np.zeros(max(key_cap, 1), np.uint8)
+    vals = np.zeros(max(val_cap, 1), np.uint8)
+    key_off = np.zeros(S + 1, np.uint32)
+    val_off = np.zeros(S + 1, np.uint32)
+    tomb = np.zeros(S, np.uint8)
+    rc = _load().or_fc_decode(_ptr(p), T, S, _ptr(keys), key_cap, _ptr(key_off), _ptr(vals), val_cap,
+                              _ptr(val_off), _ptr(tomb))
+    if rc:
+        raise ValueError("malformed payload or capacity too small")
+    return gen.HostSide(keys=keys[:key_off[S]].copy(), key_off=key_off, vals=vals[:val_off[S]].copy(),
+                        val_off=val_off, tomb=tomb)
 
 
 def run(A, B, items_per_part: int = 2048):

@@ -24,7 +24,8 @@
  *        prefix-cache paragraph (proper-prefix order, LCP clamped to the
  *        shorter key); the KV03 and output-EF paragraphs for the output
  *        navigation (sampled offsets, common value width, Elias-Fano lows
- *        and highs, 256-entry groups, the 4096-bit sparse threshold).
+ *        and highs, 256-entry groups, the 4096-bit sparse threshold); the
+ *        block-parse paragraph for decoding a payload back into arenas.
  *  [CB]  Everett, "Collision bitmap and rank experiment": "Corrected record
  *        ordinals" (collision bits, exclusive rank R, ordinal formulas).
  *
@@ -383,4 +384,95 @@ void or_ef_encode(const uint64_t *e, uint64_t n, uint64_t width, uint64_t *lows,
   info->high_words = (high_bits + 63) / 64;
   info->groups = groups;
   info->exceptions = nexc;
+}
+
+/*
+ * [GC] Compressed input: the block-parse paragraph (a block's first control
+ * gives its absolute retained length, later controls count back from the
+ * predecessor's key length; values are skipped by their own grammar) read
+ * with the record grammar, one record after the other.  Each key is its
+ * predecessor's first l_i bits followed by its own literal; this sequential
+ * definition is what the literal-owner formula resolves in parallel.
+ * Decodes S records of a payload of T bits into a key arena (key_off[S+1]),
+ * a value arena (val_off[S+1]) and tombstone flags.  Returns 0, or -1 when
+ * the payload is malformed (a field reaches past T, an inherited prefix is
+ * longer than the predecessor's key, a key is not whole bytes, bits remain
+ * after record S-1) or a capacity is too small.
+ */
+typedef struct {
+  const uint8_t *p;
+  uint64_t n, pos;
+  int bad;
+} bitr;
+
+static unsigned get_bit(bitr *r) {
+  if (r->pos >= r->n) {
+    r->bad = 1;
+    return 0;
+  }
+  unsigned b = (r->p[r->pos >> 3] >> (7 - (r->pos & 7))) & 1u;
+  r->pos++;
+  return b;
+}
+
+static uint64_t get_eg0(bitr *r) {
+  unsigned z = 0;
+  while (!r->bad && get_bit(r) == 0) {
+    if (++z > 63) {
+      r->bad = 1;
+      return 0;
+    }
+  }
+  uint64_t v = 1;
+  for (unsigned t = 0; t < z && !r->bad; ++t) v = (v << 1) | get_bit(r);
+  return v - 1;
+}
+
+int or_fc_decode(const uint8_t *payload, uint64_t T, uint32_t S, uint8_t *keys, uint64_t key_cap,
+                 uint32_t *key_off, uint8_t *vals, uint64_t val_cap, uint32_t *val_off, uint8_t *tomb) {
+  bitr r = {payload, T, 0, 0};
+  uint64_t kprev = 0, kat = 0, vat = 0, prev_at = 0;
+  for (uint32_t i = 0; i < S; ++i) {
+    const uint64_t c = get_eg0(&r), s = get_eg0(&r);
+    if (r.bad) return -1;
+    uint64_t l;
+    if (i % 15 == 0) {
+      if (c == 0) return -1;
+      l = c - 1;
+    } else {
+      if (c > kprev) return -1;
+      l = kprev - c;
+    }
+    if (l > kprev) return -1; /* (l_0 must be 0: kprev is 0 before the first record) */
+    const uint64_t k = l + s;
+    if (k % 8 || kat + k / 8 > key_cap || kat + k / 8 > 0xFFFFFFFFull) return -1;
+    key_off[i] = (uint32_t)kat;
+    uint8_t *x = keys + kat;
+    for (uint64_t b = 0; b < k / 8; ++b) x[b] = 0;
+    for (uint64_t b = 0; b < k; ++b) {
+      unsigned bit = b < l ? (keys[prev_at + (b >> 3)] >> (7 - (b & 7))) & 1u : get_bit(&r);
+      x[b >> 3] |= (uint8_t)(bit << (7 - (b & 7)));
+    }
+    prev_at = kat;
+    kat += k / 8;
+    kprev = k;
+    val_off[i] = (uint32_t)vat;
+    if (get_bit(&r)) {
+      tomb[i] = 0;
+      const uint64_t len = get_eg0(&r);
+      if (r.bad || vat + len > val_cap || vat + len > 0xFFFFFFFFull) return -1;
+      for (uint64_t b = 0; b < len; ++b) {
+        unsigned v = 0;
+        for (int t = 0; t < 8; ++t) v = (v << 1) | get_bit(&r);
+        vals[vat + b] = (uint8_t)v;
+      }
+      vat += len;
+    } else {
+      tomb[i] = 1;
+    }
+    if (r.bad) return -1;
+  }
+  key_off[S] = (uint32_t)kat;
+  val_off[S] = (uint32_t)vat;
+  return r.pos == T ? 0 : -1;
 }

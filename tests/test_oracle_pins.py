@@ -387,3 +387,49 @@ def test_ef_navigation_of_merged_payloads():
     starts = [i["start"] for i in info]
     want = [starts[o] - 138 * o for o in range(0, 40, 15)] + [r["T"] - 138 * 40]
     assert select_all(nav) == want
+
+
+# ---- compressed input: the payload decoded back into arenas ----
+
+def _merged_records(A, B, final):
+    nA = A.n
+    return [(A.key(r), A.value(r)) if r < nA else (B.key(r - nA), B.value(r - nA)) for r in final]
+
+
+def test_fc_decode_hand_example():
+    payload = np.frombuffer(bytes.fromhex("411616244b1d2d04dd800000"), np.uint8)
+    side = oracle.fc_decode(payload, 73, 3, 64, 64)
+    assert side.records() == [(b"ab", None), (b"abc", b"Z"), (b"b", b"")]
+    assert list(side.key_off) == [0, 2, 5, 6] and list(side.val_off) == [0, 0, 1, 1]
+    with pytest.raises(ValueError):  # one bit short
+        oracle.fc_decode(payload, 72, 3, 64, 64)
+    with pytest.raises(ValueError):  # a bit left over after the last record
+        oracle.fc_decode(payload, 74, 3, 64, 64)
+    with pytest.raises(ValueError):  # key arena too small
+        oracle.fc_decode(payload, 73, 3, 5, 64)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fc_decode_round_trip(seed):
+    rng = random.Random(seed)
+    alpha = [0x00, 0x01, 0x61, 0x7F, 0x80, 0xFF]
+    keys = sorted({bytes(rng.choice(alpha) for _ in range(rng.randrange(0, 9))) for _ in range(400)})
+    a, b = [], []
+    for k in keys:
+        u = rng.random()
+        val = (lambda: None if rng.random() < 0.15 else bytes(rng.randrange(256) for _ in range(rng.randrange(0, 7))))
+        if u < 0.3:
+            a.append((k, val()))
+            b.append((k, val()))
+        elif u < 0.65:
+            a.append((k, val()))
+        else:
+            b.append((k, val()))
+    A, B = gen.side_from_records(a), gen.side_from_records(b)
+    r = oracle.run(A, B)
+    want = _merged_records(A, B, r["final"])
+    side = oracle.fc_decode(r["payload"], r["T"], r["S"], 16 * len(want) + 16, 16 * len(want) + 16)
+    assert side.records() == want
+    # and the independent Python decoder reads the same records
+    recs, _ = decode(r["payload"].tobytes(), r["T"], r["S"])
+    assert recs == want
