@@ -84,6 +84,8 @@ def parse():
                     help="fraction of the workload the CPU oracle is timed on")
     ap.add_argument("--navigation", action="store_true",
                     help="also time em_ef_navigation (the output navigation) on the step's outputs")
+    ap.add_argument("--fcin", action="store_true",
+                    help="also time decoding the step's payload back into arenas (em_fcin_parse + _materialize)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -302,6 +304,49 @@ def main():
         result["navigation"] = {"call": "em_ef_navigation", "ms": nav_ms, "entries": nav["n"], "L": nav["L"],
                                 "width": nav["width"], "sparse_entries": nav["n_exceptions"],
                                 "algorithmic_bytes": nav_bytes, "GBps": nav_bytes / (nav_ms * 1e-3) / 1e9}
+        if pn is not pl:
+            del pn
+    if args.fcin:
+        # the payload decoded back into arenas (the front-coded input path),
+        # block starts from the record offsets; parse and materialize are
+        # timed separately (the host reads the arena sizes between them)
+        if fused:
+            pn = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
+            pn.run()
+        else:
+            pn = pl
+        torch.cuda.synchronize()
+        S, T = pn.S, pn.T
+        ws = torch.empty(max(em.em_fcin_workspace_bytes(S), 256), dtype=torch.uint8, device="cuda")
+        tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+        em.em_fcin_parse(pn.payload, T, S, tot, ws, off=pn.off)
+        kb, vb, err = (int(x) for x in tot.cpu())
+        assert err == 0, f"front-coded input: error bits {err}"
+        keys = torch.zeros(kb + 64, dtype=torch.uint8, device="cuda")
+        vals = torch.zeros(vb + 64, dtype=torch.uint8, device="cuda")
+        key_off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+        val_off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+        tomb = torch.empty(max(S, 1), dtype=torch.uint8, device="cuda")
+        ev_p, ev_m = [], []
+        for it in range(args.steps + 1):
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            em.em_fcin_parse(pn.payload, T, S, tot, ws, off=pn.off, stream=stream)
+            b.record(stream)
+            em.em_fcin_materialize(pn.payload, S, keys, key_off, vals, val_off, tomb, tot, ws, stream=stream)
+            c.record(stream)
+            if it:  # the first pass warms up
+                ev_p.append((a, b))
+                ev_m.append((b, c))
+        torch.cuda.synchronize()
+        assert int(tot[2].item()) == 0
+        parse_ms = sum(x.elapsed_time(y) for x, y in ev_p) / len(ev_p)
+        mat_ms = sum(x.elapsed_time(y) for x, y in ev_m) / len(ev_m)
+        fcin_bytes = (T + 7) // 8 + kb + vb + 8 * (S + 1) + S
+        result["front_coded_input"] = {"calls": ["em_fcin_parse", "em_fcin_materialize"], "parse_ms": parse_ms,
+                                       "materialize_ms": mat_ms, "key_bytes": kb, "value_bytes": vb,
+                                       "algorithmic_bytes": fcin_bytes,
+                                       "GBps": fcin_bytes / ((parse_ms + mat_ms) * 1e-3) / 1e9}
         if pn is not pl:
             del pn
     if args.copy_calibration:

@@ -325,6 +325,44 @@ int em_ef_encode(const uint64_t *entries, uint32_t n, uint64_t width, uint64_t *
                  uint64_t *exceptions, uint64_t exception_cap, em_ef_info_t *info, void *ws, size_t ws_bytes,
                  void *stream);
 
+/*
+ * Front-coded input (Everett, "GPU construction experiment": the block-parse
+ * paragraph, the literal-owner paragraph j = max{t <= i : r_t <= p} with its
+ * minimum tree, and full-key materialization as a consumer of the parsed
+ * descriptors).  Decodes a payload of S records and T bits -- as em_emit or
+ * em_emit_merged wrote it -- back into the arenas of a side, so that it can
+ * be merged again.  Two calls, because the arena sizes are known only after
+ * the parse:
+ *   em_fcin_parse: block starts from the record offsets off[0..S] when off
+ *     is not NULL, else by select on the navigation sections of
+ *     em_ef_navigation (nav_info and the four arrays, device memory); one
+ *     thread parses each block of at most 15 records (retained length r_i,
+ *     key bytes, literal and value positions, tombstone flag); the key and
+ *     value arena offsets are scanned and a minimum tree over r_i is built.
+ *     Writes d_totals[0] = key arena bytes, d_totals[1] = value arena bytes
+ *     and d_totals[2] = error bits (0: none; 1: a field past T or a bad
+ *     EG0 code, 2: an inherited prefix longer than the predecessor's key,
+ *     4: a key that is not whole bytes, 8: a block not ending where the next
+ *     starts, 16: an arena of 2^32 bytes or more, 32: an output arena too
+ *     small).  d_totals is u64[3] in device memory.
+ *   em_fcin_materialize: after the host read d_totals (no errors): writes
+ *     keys (key_cap bytes), key_off[S+1], vals (val_cap bytes), val_off[S+1]
+ *     and tomb[S]; every inherited key bit comes from its owner's literal.
+ *     Arenas smaller than the totals set error bit 32 and leave the
+ *     records that do not fit unwritten.
+ * payload: u32 words in stream byte order, payload_words >= ceil(T/32).  The
+ * same workspace (em_fcin_workspace_bytes(S), 256-byte aligned) must reach
+ * both calls unchanged.
+ */
+size_t em_fcin_workspace_bytes(uint32_t S);
+int em_fcin_parse(const uint32_t *payload, uint64_t payload_words, uint64_t T, uint32_t S, const uint64_t *off,
+                  const em_ef_info_t *nav_info, const uint64_t *nav_lows, const uint64_t *nav_highs,
+                  const uint64_t *nav_samples, const uint64_t *nav_exceptions, uint64_t *d_totals, void *ws,
+                  size_t ws_bytes, void *stream);
+int em_fcin_materialize(const uint32_t *payload, uint64_t payload_words, uint32_t S, uint8_t *keys,
+                        uint64_t key_cap, uint32_t *key_off, uint8_t *vals, uint64_t val_cap, uint32_t *val_off,
+                        uint8_t *tomb, uint64_t *d_totals, void *ws, size_t ws_bytes, void *stream);
+
 /* Text for an EM_* code (static string). */
 const char *em_strerror(int code);
 

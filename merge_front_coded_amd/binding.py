@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH):
         "em_ef_workspace_bytes": (sz, [u32]),
         "em_ef_navigation": (i32, [S, S, P, u32, P, u64, P, u64, P, u64, P, u64, P, u64, P, P, sz, P]),
         "em_ef_encode": (i32, [P, u32, u64, P, u64, P, u64, P, u64, P, u64, P, P, sz, P]),
+        "em_fcin_workspace_bytes": (sz, [u32]),
+        "em_fcin_parse": (i32, [P, u64, u64, u32, P, P, P, P, P, P, P, P, sz, P]),
+        "em_fcin_materialize": (i32, [P, u64, u32, P, u64, P, P, u64, P, P, P, P, sz, P]),
         "em_strerror": (ctypes.c_char_p, [i32]),
         "em_last_hip_error": (i32, []),
     }
@@ -316,3 +319,49 @@ def em_ef_navigation(A, B, final_refs, S, off, T, sec: EfSections, stream=None):
 
 def em_ef_encode(entries, width, sec: EfSections, stream=None):
     _check(lib().em_ef_encode(_p(entries), entries.numel(), width, *sec._args(), _stream(stream)), "em_ef_encode")
+
+
+# ---- front-coded input (include/em.h: em_fcin_*) ----
+
+FCIN_ERRORS = {1: "field past T or bad EG0 code", 2: "inherited prefix longer than the predecessor's key",
+               4: "key not whole bytes", 8: "block does not end where the next starts",
+               16: "arena of 2^32 bytes or more", 32: "output arena too small"}
+
+
+def em_fcin_workspace_bytes(S: int) -> int:
+    return int(lib().em_fcin_workspace_bytes(S))
+
+
+def em_fcin_parse(payload, T, S, d_totals, ws, off=None, nav: "EfSections | None" = None, stream=None):
+    n = (None,) * 5 if nav is None else (nav.info, nav.lows, nav.highs, nav.samples, nav.exceptions)
+    _check(lib().em_fcin_parse(_p(payload), payload.numel(), T, S, _p(off), *[_p(t) for t in n], _p(d_totals),
+                               _p(ws), ws.numel(), _stream(stream)), "em_fcin_parse")
+
+
+def em_fcin_materialize(payload, S, keys, key_off, vals, val_off, tomb, d_totals, ws, stream=None):
+    _check(lib().em_fcin_materialize(_p(payload), payload.numel(), S, _p(keys), keys.numel(), _p(key_off),
+                                     _p(vals), vals.numel(), _p(val_off), _p(tomb), _p(d_totals), _p(ws),
+                                     ws.numel(), _stream(stream)), "em_fcin_materialize")
+
+
+def fcin_decode(payload, T: int, S: int, off=None, nav: "EfSections | None" = None, device="cuda") -> DeviceSide:
+    """Decode a front-coded payload of S records into a DeviceSide (parse,
+    read the arena sizes, materialize).  Block starts come from off (u64 record
+    offsets) or from the navigation sections."""
+    ws = torch.empty(max(em_fcin_workspace_bytes(S), 256), dtype=torch.uint8, device=device)
+    d_totals = torch.zeros(3, dtype=torch.int64, device=device)
+    em_fcin_parse(payload, T, S, d_totals, ws, off=off, nav=nav)
+    kb, vb, err = (int(x) & 0xFFFFFFFFFFFFFFFF for x in d_totals.cpu())
+    if err:
+        raise EmError(EM_EINVAL, "em_fcin_parse: " + ", ".join(m for b, m in FCIN_ERRORS.items() if err & b), lib())
+    keys = torch.zeros(((kb + 15) // 16) * 16 + EM_ARENA_PAD, dtype=torch.uint8, device=device)
+    vals = torch.zeros(((vb + 15) // 16) * 16 + EM_ARENA_PAD, dtype=torch.uint8, device=device)
+    key_off = torch.empty(S + 1, dtype=torch.int32, device=device)
+    val_off = torch.empty(S + 1, dtype=torch.int32, device=device)
+    tomb = torch.zeros(max(S, 16), dtype=torch.uint8, device=device)
+    em_fcin_materialize(payload, S, keys, key_off, vals, val_off, tomb, d_totals, ws)
+    err = int(d_totals[2].item())
+    if err:
+        raise EmError(EM_EINVAL, "em_fcin_materialize: " + ", ".join(m for b, m in FCIN_ERRORS.items() if err & b),
+                      lib())
+    return DeviceSide(keys, key_off, vals, val_off, tomb, S, kb, vb)

@@ -1,0 +1,533 @@
+// Front-coded input: a payload (with its navigation or its record offsets)
+// decoded back into key and value arenas, so that a compressed side can enter
+// the merge.
+//
+// Everett, "GPU construction experiment":
+//  * block parse: GPU select gives each block's physical offset (with the
+//    common-value-width correction); one invocation parses a block's at most
+//    fifteen records: its first control gives the absolute retained length,
+//    later controls count back from the predecessor's key length, values are
+//    skipped by their own grammar and their bit spans recorded;
+//  * literal owners: with r_i record i's retained key length, bit p of key i
+//    belongs to the literal of j = max{t <= i : r_t <= p}; a minimum tree over
+//    the retained lengths answers that query in O(log n): from the record's
+//    leaf, climb until a left sibling has minimum <= p, then descend
+//    right-first through children with minimum <= p; unused leaves hold an
+//    infinite sentinel.  A byte resolved from its highest bit backward can
+//    combine several literal fragments;
+//  * full-key materialization as a consumer of the same descriptors (the
+//    paragraph that names it as the alternative to owner searches during
+//    comparison): every key is written out whole, then the ordinary merge
+//    runs on the arenas.
+//
+// Following the owners from the top bit of key i down, the fragments are
+// contiguous: the owner j of bit r_i - 1 owns all of [r_j, r_i) (every record
+// after j up to i retains more than r_i - 1 bits), then the owner of bit
+// r_j - 1 takes over, and so on down to a record with r = 0.
+#include "em_internal.h"
+
+namespace em {
+
+constexpr int kFiBlock = 256;
+constexpr uint32_t kFiRecs = 15;  // records per block (the W15 period)
+constexpr uint32_t kFiInf = 0xFFFFFFFFu;
+
+enum : uint64_t {
+  kFiErrRange = 1,    // a field reaches past T, or an EG0 code is malformed
+  kFiErrPrefix = 2,   // an inherited prefix longer than the predecessor's key
+  kFiErrBytes = 4,    // a key that is not whole bytes
+  kFiErrBlock = 8,    // a block does not end where the next one starts
+  kFiErrTotal = 16,   // an arena of 2^32 bytes or more
+  kFiErrCap = 32,     // an output arena smaller than the decoded bytes
+};
+
+struct FiLayout {
+  uint32_t S, nb, P2;
+  uint64_t* starts;   // nb block start bits
+  uint32_t* r;        // S retained key bits
+  uint32_t* kbytes;   // S + 1 key bytes (scan input; entry S is 0)
+  uint32_t* vbytes;   // S + 1 value bytes
+  uint64_t* lit;      // S payload bit of each literal's first bit
+  uint64_t* vbit;     // S payload bit of each value's first byte
+  uint8_t* tflag;     // S tombstone flags
+  uint64_t* koff;     // S + 2 key arena offsets (scan output)
+  uint64_t* voff;     // S + 2 value arena offsets
+  uint32_t* tree;     // 2 P2 minimum tree over r (heap order, leaves at P2)
+  uint32_t* pse;      // S: the last earlier record with a smaller r (kFiInf: none)
+  uint8_t* scan_ws;
+  size_t scan_bytes;
+  size_t used;
+};
+
+static FiLayout fi_layout(void* ws, uint32_t S) {
+  FiLayout L{};
+  L.S = S;
+  L.nb = (S + kFiRecs - 1) / kFiRecs;
+  L.P2 = 1;
+  while (L.P2 < S) L.P2 <<= 1;
+  WsCursor cur{static_cast<uint8_t*>(ws), 0};
+  const size_t n = static_cast<size_t>(S) + 2;
+  L.starts = cur.take<uint64_t>(L.nb + 1);
+  L.r = cur.take<uint32_t>(n);
+  L.kbytes = cur.take<uint32_t>(n);
+  L.vbytes = cur.take<uint32_t>(n);
+  L.lit = cur.take<uint64_t>(n);
+  L.vbit = cur.take<uint64_t>(n);
+  L.tflag = cur.take<uint8_t>(n);
+  L.koff = cur.take<uint64_t>(n);
+  L.voff = cur.take<uint64_t>(n);
+  L.tree = cur.take<uint32_t>(2 * static_cast<size_t>(L.P2));
+  L.pse = cur.take<uint32_t>(n);
+  L.scan_bytes = scan_ws(S + 1);
+  L.scan_ws = cur.take<uint8_t>(L.scan_bytes);
+  L.used = cur.used;
+  return L;
+}
+
+static inline uint32_t fi_blocks(uint64_t n) { return static_cast<uint32_t>((n + kFiBlock - 1) / kFiBlock); }
+
+// The payload as a bit stream: 32 bits starting at bit x (MSB first), zero
+// past the stored words.
+struct FiBits {
+  const uint32_t* w;
+  uint64_t nwords;
+  __device__ __forceinline__ uint32_t word(uint64_t i) const {
+    return i < nwords ? __builtin_bswap32(w[i]) : 0u;
+  }
+  __device__ __forceinline__ uint32_t at32(uint64_t x) const {
+    const uint64_t i = x >> 5;
+    const uint32_t s = static_cast<uint32_t>(x & 31u);
+    const uint32_t hi = word(i), lo = word(i + 1);
+    return s ? __builtin_amdgcn_alignbit(hi, lo, 32u - s) : hi;
+  }
+};
+
+// A bit reader bounded by T; a read past T sets kFiErrRange.
+struct FiReader {
+  FiBits b;
+  uint64_t pos, T;
+  uint64_t err;
+  __device__ __forceinline__ uint32_t take(uint32_t n) {  // n in 0..32
+    if (n == 0) return 0;
+    if (pos + n > T) {
+      err |= kFiErrRange;
+      pos = T;
+      return 0;
+    }
+    const uint32_t v = b.at32(pos) >> (32u - n);
+    pos += n;
+    return v;
+  }
+  // order-0 Exp-Golomb: z zero bits, then z + 1 bits holding x + 1 (x < 2^31 here)
+  __device__ __forceinline__ uint32_t eg0() {
+    const uint32_t win = pos < T ? b.at32(pos) : 0u;
+    const uint32_t z = win ? static_cast<uint32_t>(__builtin_clz(win)) : 32u;
+    if (z > 31u || pos + 2 * z + 1 > T) {
+      err |= kFiErrRange;
+      pos = T;
+      return 0;
+    }
+    pos += z;
+    return take(z + 1) - 1u;
+  }
+};
+
+// ---- block starts ----
+
+// From record offsets: block k starts at off[15k].
+__global__ __launch_bounds__(kFiBlock) void k_fi_starts_off(const uint64_t* __restrict__ off, uint32_t nb,
+                                                            uint64_t* __restrict__ starts) {
+  const uint32_t k = blockIdx.x * kFiBlock + threadIdx.x;
+  if (k < nb) starts[k] = off[static_cast<uint64_t>(k) * kFiRecs];
+}
+
+// From the navigation sections: select entry k (a sparse group lists its
+// high-bit positions; a dense one is walked from its sample), add the common
+// width times the ordinal back.
+__global__ __launch_bounds__(kFiBlock) void k_fi_starts_ef(const em_ef_info_t* __restrict__ info,
+                                                           const uint64_t* __restrict__ lows,
+                                                           const uint64_t* __restrict__ highs,
+                                                           const uint64_t* __restrict__ samples,
+                                                           const uint64_t* __restrict__ exceptions, uint32_t nb,
+                                                           uint64_t* __restrict__ starts) {
+  const uint32_t k = blockIdx.x * kFiBlock + threadIdx.x;
+  if (k >= nb) return;
+  const uint64_t L = info->L, w = info->width, G = info->groups, hw = info->high_words;
+  const uint32_t g = k / 256, rk = k % 256;
+  const uint64_t x0 = samples[2ull * g + 1];
+  const uint64_t x1 = g + 1 < G ? samples[2ull * g + 3] : info->exceptions;
+  uint64_t p;
+  if (x1 > x0) {
+    p = exceptions[x0 + rk];
+  } else {
+    // the rk-th set bit at or after the group's first one
+    p = samples[2ull * g];
+    uint64_t wi = p >> 6;
+    uint64_t word = wi < hw ? highs[wi] & (~0ull << (p & 63)) : 0ull;
+    uint32_t need = rk;
+    while (true) {
+      const uint32_t c = static_cast<uint32_t>(__builtin_popcountll(word));
+      if (need < c || wi + 1 >= hw) break;
+      need -= c;
+      word = highs[++wi];
+    }
+    for (uint32_t t = 0; t < need; ++t) word &= word - 1;  // drop the lower set bits
+    p = 64 * wi + (word ? static_cast<uint64_t>(__builtin_ctzll(word)) : 63ull);
+  }
+  uint64_t low = 0;
+  if (L) {
+    const uint64_t at = static_cast<uint64_t>(k) * L;
+    low = lows[at >> 6] >> (at & 63);
+    if ((at & 63) + L > 64) low |= lows[(at >> 6) + 1] << (64 - (at & 63));
+    low &= (L == 64 ? ~0ull : (1ull << L) - 1);
+  }
+  const uint64_t e = ((p - k) << L) | low;
+  starts[k] = e + static_cast<uint64_t>(k) * kFiRecs * w;
+}
+
+// ---- block parse: one thread per block of at most 15 records ----
+
+// 64 bits of the payload from bit x on (MSB first, zero past the stored words)
+__device__ __forceinline__ uint64_t fi_peek64(const uint32_t* __restrict__ w, uint64_t nwords, uint64_t x) {
+  const uint64_t i = x >> 5;
+  const uint32_t sft = static_cast<uint32_t>(x & 31u);
+  const uint32_t a = i < nwords ? __builtin_bswap32(w[i]) : 0u;
+  const uint32_t b = i + 1 < nwords ? __builtin_bswap32(w[i + 1]) : 0u;
+  const uint32_t c = i + 2 < nwords ? __builtin_bswap32(w[i + 2]) : 0u;
+  const uint32_t hi = sft ? __builtin_amdgcn_alignbit(a, b, 32u - sft) : a;
+  const uint32_t lo = sft ? __builtin_amdgcn_alignbit(b, c, 32u - sft) : b;
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One order-0 Exp-Golomb code at the top of a 64-bit window: its value and
+// length, or length 0 when the window does not hold it (a code here is at
+// most 63 bits: its value is below 2^31).
+__device__ __forceinline__ uint32_t fi_eg0_win(uint64_t win, uint32_t& len) {
+  const uint32_t z = win ? static_cast<uint32_t>(__builtin_clzll(win)) : 64u;
+  if (z > 31u) {
+    len = 0;
+    return 0;
+  }
+  len = 2 * z + 1;
+  return static_cast<uint32_t>(win >> (64 - len)) - 1u;
+}
+
+// Parse: one thread per block.  Each record costs two 64-bit windows (its
+// two controls, then the value header); the outputs go through restrict
+// pointers, so that no store holds back a later load.
+__global__ __launch_bounds__(kFiBlock) void k_fi_parse(const uint32_t* __restrict__ payload, uint64_t nwords,
+                                                       uint64_t T, uint32_t S, uint32_t nb,
+                                                       const uint64_t* __restrict__ starts,
+                                                       uint32_t* __restrict__ r_out, uint32_t* __restrict__ kbytes,
+                                                       uint32_t* __restrict__ vbytes, uint64_t* __restrict__ lit,
+                                                       uint64_t* __restrict__ vbit, uint8_t* __restrict__ tflag,
+                                                       uint64_t* __restrict__ err) {
+  const uint32_t k = blockIdx.x * kFiBlock + threadIdx.x;
+  if (k >= nb) return;
+  const uint32_t i0 = k * kFiRecs, i1 = min(i0 + kFiRecs, S);
+  uint64_t pos = starts[k];
+  const uint64_t end = k + 1 < nb ? starts[k + 1] : T;
+  uint64_t e = pos > T ? static_cast<uint64_t>(kFiErrBlock) : 0;
+  uint32_t kprev = 0;
+  for (uint32_t i = i0; i < i1 && !e; ++i) {
+    uint64_t win = fi_peek64(payload, nwords, pos);
+    uint32_t n1, n2;
+    const uint32_t c = fi_eg0_win(win, n1);
+    uint32_t s = 0;
+    if (n1) {
+      if (n1 < 64) s = fi_eg0_win(win << n1, n2);
+      if (n1 == 64 || n1 + n2 > 64 || n2 == 0) {  // (a rare long pair: read the second code afresh)
+        win = fi_peek64(payload, nwords, pos + n1);
+        s = fi_eg0_win(win, n2);
+        n2 = n2 ? n2 : 0;
+        if (!n2) e |= kFiErrRange;
+      }
+    } else {
+      e |= kFiErrRange;
+    }
+    if (pos + n1 + n2 > T) e |= kFiErrRange;
+    pos += n1 + n2;
+    uint32_t l;
+    if (i == i0) {  // i mod 15 = 0: c = 1 + l
+      l = c - 1u;
+      if (c == 0 || (i == 0 && l != 0)) e |= kFiErrPrefix;
+    } else {
+      l = kprev - c;
+      if (c > kprev) e |= kFiErrPrefix;
+    }
+    const uint64_t kb = static_cast<uint64_t>(l) + s;
+    if (kb & 7u) e |= kFiErrBytes;
+    r_out[i] = l;
+    kbytes[i] = static_cast<uint32_t>(kb >> 3);
+    lit[i] = pos;
+    pos += s;  // the literal
+    // value header: presence bit, then EG0(byte length)
+    const uint64_t vw = fi_peek64(payload, nwords, pos);
+    uint32_t vlen = 0, nv = 1;
+    const bool present = (vw >> 63) != 0;
+    if (present) {
+      uint32_t n3;
+      vlen = fi_eg0_win(vw << 1, n3);
+      if (!n3) e |= kFiErrRange;
+      nv += n3;
+    }
+    if (pos + nv > T) e |= kFiErrRange;
+    pos += nv;
+    vbit[i] = pos;
+    vbytes[i] = vlen;
+    tflag[i] = present ? 0 : 1;
+    pos += 8ull * vlen;
+    if (pos > T) e |= kFiErrRange;
+    kprev = static_cast<uint32_t>(kb);
+  }
+  // the block must end where the next one starts (the last one at T)
+  if (!e && pos != end) e |= kFiErrBlock;
+  if (k == 0) {
+    kbytes[S] = 0;
+    vbytes[S] = 0;
+  }
+  if (e) atomicOr(reinterpret_cast<unsigned long long*>(err), static_cast<unsigned long long>(e));
+}
+
+// ---- minimum tree over the retained lengths ----
+
+__global__ __launch_bounds__(kFiBlock) void k_fi_leaves(const uint32_t* __restrict__ r, uint32_t S, uint32_t P2,
+                                                        uint32_t* __restrict__ tree) {
+  const uint32_t i = blockIdx.x * kFiBlock + threadIdx.x;
+  if (i < P2) tree[P2 + i] = i < S ? r[i] : kFiInf;
+}
+
+// nodes [first, 2 first) from their children
+__global__ __launch_bounds__(kFiBlock) void k_fi_level(uint32_t* __restrict__ tree, uint32_t first) {
+  const uint32_t v = first + blockIdx.x * kFiBlock + threadIdx.x;
+  if (v < 2 * first) tree[v] = min(tree[2 * v], tree[2 * v + 1]);
+}
+
+// The literal owner of bit p of key i, p < r_i: j = max{t <= i : r_t <= p}.
+__device__ __forceinline__ uint32_t fi_owner(const uint32_t* __restrict__ tree, uint32_t P2, uint32_t i,
+                                             uint32_t p) {
+  uint32_t v = P2 + i;
+  while (v > 1) {
+    if ((v & 1u) && tree[v - 1] <= p) {  // a left sibling holds a record with r <= p
+      v -= 1;
+      while (v < P2) v = tree[2 * v + 1] <= p ? 2 * v + 1 : 2 * v;
+      return v - P2;
+    }
+    v >>= 1;
+  }
+  return kFiInf;  // none (only for p outside every key; the parse rules this out)
+}
+
+// ---- materialization ----
+// The owner chain of key i is a chain of "previous smaller" records: the
+// owner of bit r_i - 1 is pse(i) = max{t < i : r_t < r_i} (every record after
+// it up to i retains at least r_i bits), and the owner of the bit below
+// fragment j's start is pse(j).  pse comes from one owner query per record.
+// Block heads (records 15k) follow their chain to a record with r = 0; any
+// other record follows it while it stays inside its block and takes the
+// bits below from its block head's key, written by the kernel before (all
+// records from the head on keep those bits).
+
+__global__ __launch_bounds__(kFiBlock) void k_fi_pse(FiLayout L) {
+  const uint32_t i = blockIdx.x * kFiBlock + threadIdx.x;
+  if (i >= L.S) return;
+  const uint32_t r = L.r[i];
+  L.pse[i] = r ? fi_owner(L.tree, L.P2, i, r - 1) : kFiInf;
+}
+
+// nbytes bytes from payload bit x on: sixteen at a time, the four loads of
+// a group issued before its stores (a byte store may alias any load, so a
+// load after it would wait for it), whole words where the destination is
+// aligned.
+__device__ __forceinline__ void fi_copy_bytes(FiBits bits, uint64_t x, uint8_t* __restrict__ dst, uint32_t nbytes) {
+  uint32_t m = 0;
+  for (; m + 16 <= nbytes; m += 16) {
+    uint32_t v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = bits.at32(x + 8ull * (m + 4 * t));
+    if ((reinterpret_cast<uintptr_t>(dst + m) & 3) == 0) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) *reinterpret_cast<uint32_t*>(dst + m + 4 * t) = __builtin_bswap32(v[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) dst[m + t] = static_cast<uint8_t>(v[t >> 2] >> (24 - 8 * (t & 3)));
+    }
+  }
+  for (; m < nbytes; m += 4) {
+    const uint32_t v = bits.at32(x + 8ull * m);
+    const uint32_t n = nbytes - m < 4 ? nbytes - m : 4;
+    for (uint32_t t = 0; t < n; ++t) dst[m + t] = static_cast<uint8_t>(v >> (24 - 8 * t));
+  }
+}
+
+// Key i from the top byte down.  The current fragment (record j) covers key
+// bits [lo, hi] with key bit q at payload bit base + q.  head = kFiInf: the
+// chain runs to the end; else bits below a fragment whose pse is at or
+// before `head` come from the head's key in the arena.
+__device__ __forceinline__ void fi_key(FiBits bits, const FiLayout& L, uint32_t i, uint32_t head,
+                                       const uint8_t* __restrict__ head_key, uint8_t* __restrict__ key,
+                                       uint32_t kb, uint64_t* __restrict__ err) {
+  uint32_t j = i;
+  uint32_t lo = L.r[i];
+  uint64_t base = L.lit[i] - lo;
+  bool from_head = false;  // bits below lo are the head key's
+  // the bytes wholly inside the record's own literal: a straight copy
+  const uint32_t own = (lo + 7) >> 3;
+  if (own < kb) fi_copy_bytes(bits, base + 8ull * own, key + own, kb - own);
+  for (uint32_t b = own < kb ? own : kb; b-- > 0;) {
+    uint32_t byte = 0;
+    uint32_t hi = 8 * b + 7;  // highest key bit of this byte still to fill
+    while (true) {
+      if (lo > hi && !from_head) {
+        const uint32_t nj = L.pse[j];
+        if (head != kFiInf && (nj == kFiInf || nj <= head)) {
+          from_head = true;
+        } else {
+          if (nj == kFiInf || L.r[nj] > hi) {
+            atomicOr(reinterpret_cast<unsigned long long*>(err), static_cast<unsigned long long>(kFiErrPrefix));
+            return;
+          }
+          j = nj;
+          lo = L.r[j];
+          base = L.lit[j] - lo;
+        }
+      }
+      if (from_head && lo > hi) {  // bits [8b, hi] from the head key
+        byte |= head_key[b] & (0xFFu << (7u - (hi & 7u)));
+        break;
+      }
+      const uint32_t rl = max(8 * b, lo);  // run [rl, hi] from the current fragment, 1..8 bits
+      const uint32_t n = hi - rl + 1;
+      const uint32_t v = bits.at32(base + rl) >> (32u - n);
+      byte |= v << (7u - (hi & 7u));
+      if (rl == 8 * b) break;
+      hi = rl - 1;  // the rest of the byte lies below this fragment
+    }
+    key[b] = static_cast<uint8_t>(byte);
+  }
+}
+
+// a block's first record may not inherit more than its predecessor's key;
+// the arenas must hold the record
+__device__ __forceinline__ bool fi_record_ok(const FiLayout& L, uint32_t i, uint64_t key_cap, uint64_t val_cap) {
+  if (i > 0 && L.r[i] > 8u * L.kbytes[i - 1]) return false;
+  return L.koff[i] + L.kbytes[i] <= key_cap && L.voff[i] + L.vbytes[i] <= val_cap;
+}
+
+// block heads' keys, one thread each
+__global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, uint8_t* __restrict__ keys,
+                                                       uint64_t key_cap, uint64_t val_cap,
+                                                       uint64_t* __restrict__ err) {
+  const uint32_t k = blockIdx.x * kFiBlock + threadIdx.x;
+  if (k >= L.nb) return;
+  const uint32_t i = k * kFiRecs;
+  if (!fi_record_ok(L, i, key_cap, val_cap)) return;  // (flagged by k_fi_records)
+  fi_key(bits, L, i, kFiInf, nullptr, keys + L.koff[i], L.kbytes[i], err);
+}
+
+// every record: offsets, tombstone flag, value bytes, and the key of a
+// record that is not a block head
+__global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L, uint8_t* __restrict__ keys,
+                                                         uint64_t key_cap, uint32_t* __restrict__ key_off,
+                                                         uint8_t* __restrict__ vals, uint64_t val_cap,
+                                                         uint32_t* __restrict__ val_off,
+                                                         uint8_t* __restrict__ tomb,
+                                                         uint64_t* __restrict__ err) {
+  const uint32_t i = blockIdx.x * kFiBlock + threadIdx.x;
+  if (i > L.S) return;
+  if (L.S == 0) {  // (nothing was parsed or scanned)
+    key_off[0] = val_off[0] = 0;
+    return;
+  }
+  const uint64_t ko = L.koff[i], vo = L.voff[i];
+  key_off[i] = static_cast<uint32_t>(ko);
+  val_off[i] = static_cast<uint32_t>(vo);
+  if (i == L.S) return;
+  tomb[i] = L.tflag[i];
+  if (!fi_record_ok(L, i, key_cap, val_cap)) {
+    const bool prefix = i > 0 && L.r[i] > 8u * L.kbytes[i - 1];
+    atomicOr(reinterpret_cast<unsigned long long*>(err),
+             static_cast<unsigned long long>(prefix ? kFiErrPrefix : kFiErrCap));
+    return;
+  }
+  const uint32_t head = i - i % kFiRecs;
+  if (i != head) fi_key(bits, L, i, head, keys + L.koff[head], keys + ko, L.kbytes[i], err);
+  fi_copy_bytes(bits, L.vbit[i], vals + vo, L.vbytes[i]);
+}
+
+// totals and the size checks, after the scans
+__global__ void k_fi_totals(FiLayout L, uint64_t* __restrict__ totals) {
+  const uint64_t kt = L.koff[L.S], vt = L.voff[L.S];
+  totals[0] = kt;
+  totals[1] = vt;
+  if (kt > 0xFFFFFFFFull || vt > 0xFFFFFFFFull) totals[2] |= kFiErrTotal;
+}
+
+__global__ void k_fi_clear(uint64_t* totals) {
+  totals[0] = totals[1] = totals[2] = 0;
+}
+
+}  // namespace em
+
+using namespace em;
+
+extern "C" size_t em_fcin_workspace_bytes(uint32_t S) { return align_up(fi_layout(nullptr, S).used, 256); }
+
+extern "C" int em_fcin_parse(const uint32_t* payload, uint64_t payload_words, uint64_t T, uint32_t S,
+                             const uint64_t* off, const em_ef_info_t* nav_info, const uint64_t* nav_lows,
+                             const uint64_t* nav_highs, const uint64_t* nav_samples,
+                             const uint64_t* nav_exceptions, uint64_t* d_totals, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!d_totals || !ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return EM_EINVAL;
+  if (S >= EM_MAX_RECORDS) return EM_ERANGE;
+  if ((S == 0) != (T == 0)) return EM_EINVAL;
+  if (S && !payload) return EM_EINVAL;
+  if (payload_words < (T + 31) / 32) return EM_EINVAL;
+  if (S && !off && !(nav_info && nav_highs && nav_samples && nav_lows && nav_exceptions)) return EM_EINVAL;
+  if (ws_bytes < em_fcin_workspace_bytes(S)) return EM_ENOSPC;
+  hipStream_t st = as_stream(stream);
+  const FiLayout L = fi_layout(ws, S);
+  hipLaunchKernelGGL(k_fi_clear, dim3(1), dim3(1), 0, st, d_totals);
+  if (S == 0) return check_launch();
+  const FiBits bits{payload, payload_words};
+  if (off)
+    hipLaunchKernelGGL(k_fi_starts_off, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, off, L.nb, L.starts);
+  else
+    hipLaunchKernelGGL(k_fi_starts_ef, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, nav_info, nav_lows, nav_highs,
+                       nav_samples, nav_exceptions, L.nb, L.starts);
+  hipLaunchKernelGGL(k_fi_parse, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, payload, payload_words, T, S, L.nb,
+                     L.starts, L.r, L.kbytes, L.vbytes, L.lit, L.vbit, L.tflag, d_totals + 2);
+  int rc = check_launch();
+  if (rc) return rc;
+  rc = scan_launch<uint64_t>(L.kbytes, S + 1, L.koff, L.scan_ws, L.scan_bytes, st);
+  if (rc) return rc;
+  rc = scan_launch<uint64_t>(L.vbytes, S + 1, L.voff, L.scan_ws, L.scan_bytes, st);
+  if (rc) return rc;
+  hipLaunchKernelGGL(k_fi_totals, dim3(1), dim3(1), 0, st, L, d_totals);
+  // the minimum tree over the retained lengths
+  hipLaunchKernelGGL(k_fi_leaves, dim3(fi_blocks(L.P2)), dim3(kFiBlock), 0, st, L.r, S, L.P2, L.tree);
+  for (uint32_t first = L.P2 / 2; first >= 1; first /= 2)
+    hipLaunchKernelGGL(k_fi_level, dim3(fi_blocks(first)), dim3(kFiBlock), 0, st, L.tree, first);
+  hipLaunchKernelGGL(k_fi_pse, dim3(fi_blocks(S)), dim3(kFiBlock), 0, st, L);
+  return check_launch();
+}
+
+extern "C" int em_fcin_materialize(const uint32_t* payload, uint64_t payload_words, uint32_t S, uint8_t* keys,
+                                   uint64_t key_cap, uint32_t* key_off, uint8_t* vals, uint64_t val_cap,
+                                   uint32_t* val_off, uint8_t* tomb, uint64_t* d_totals, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!d_totals || !ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return EM_EINVAL;
+  if (S >= EM_MAX_RECORDS) return EM_ERANGE;
+  if (!key_off || !val_off || (S && (!payload || !tomb))) return EM_EINVAL;
+  if ((key_cap && !keys) || (val_cap && !vals)) return EM_EINVAL;
+  if (ws_bytes < em_fcin_workspace_bytes(S)) return EM_ENOSPC;
+  hipStream_t st = as_stream(stream);
+  const FiLayout L = fi_layout(ws, S);
+  const FiBits bits{payload, payload_words};
+  if (S)
+    hipLaunchKernelGGL(k_fi_heads, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, bits, L, keys, key_cap, val_cap,
+                       d_totals + 2);
+  hipLaunchKernelGGL(k_fi_records, dim3(fi_blocks(static_cast<uint64_t>(S) + 1)), dim3(kFiBlock), 0, st, bits, L,
+                     keys, key_cap, key_off, vals, val_cap, val_off, tomb, d_totals + 2);
+  return check_launch();
+}

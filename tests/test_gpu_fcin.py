@@ -1,0 +1,120 @@
+"""GPU parity of the front-coded input path (em_fcin_parse +
+em_fcin_materialize): payloads written by the GPU path are decoded back into
+arenas and compared byte for byte with the CPU oracle's decoder, with block
+starts taken from the record offsets and from the navigation sections; a
+decoded side is merged again and compared with the oracle; block edges,
+sub-byte prefixes, long inherited chains, fixed-width values, the empty
+payload and malformed lengths are covered."""
+import numpy as np
+import pytest
+
+import gen
+import oracle
+import torch  # imported at collection so that its first-load time is not charged to a test
+from gpu_util import check_path, require_gpu, run_gpu, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _host_side(d):
+    """A DeviceSide read back (arenas cut to their lengths)."""
+    n = d.n
+    key_off = d.key_off[:n + 1].cpu().numpy().view(np.uint32).copy()
+    val_off = d.val_off[:n + 1].cpu().numpy().view(np.uint32).copy()
+    return gen.HostSide(keys=d.keys[:d.key_bytes].cpu().numpy().copy(), key_off=key_off,
+                        vals=d.vals[:d.val_bytes].cpu().numpy().copy(), val_off=val_off,
+                        tomb=d.tomb[:n].cpu().numpy().copy())
+
+
+def _same_side(got, want, label):
+    for f in ("keys", "key_off", "vals", "val_off", "tomb"):
+        g, w = getattr(got, f), getattr(want, f)
+        assert g.size == w.size, f"{label}: {f} size {g.size} != {w.size}"
+        bad = np.nonzero(g != w)[0]
+        assert bad.size == 0, f"{label}: {f} differs at {bad[:5]}"
+
+
+def _round_trip(Ah, Bh, label, nav=False):
+    import merge_front_coded_amd as em
+    pl = run_gpu(Ah, Bh, items=256)
+    torch.cuda.synchronize()
+    S, T = pl.S, pl.T
+    payload_h = np.frombuffer(pl.payload_bytes(), np.uint8)
+    want = oracle.fc_decode(payload_h, T, S, int(Ah.keys.size + Bh.keys.size) + 16,
+                            int(Ah.vals.size + Bh.vals.size) + 16)
+    print(f"{label}: S={S} T={T}", flush=True)
+    d = em.fcin_decode(pl.payload, T, S, off=pl.off)
+    _same_side(_host_side(d), want, f"{label}/off")
+    if nav:
+        sec = pl.ef_navigation()
+        d2 = em.fcin_decode(pl.payload, T, S, nav=sec)
+        _same_side(_host_side(d2), want, f"{label}/navigation")
+    return d, want
+
+
+@pytest.mark.parametrize("wid,scale", [(1, 0.3), (2, 0.005), (3, 0.001), (4, 0.001), (5, 0.002)])
+def test_decode_generated_payloads(wid, scale):
+    A, B = workload(wid, scale)
+    _round_trip(A, B, f"workload {wid} at {scale}", nav=True)
+
+
+def test_decode_edges():
+    rng = np.random.default_rng(5)
+    empty = gen.side_from_records([])
+    for n in (1, 14, 15, 16, 29, 30, 31, 46):
+        keys = [b"blk/%04d/" % i + b"z" * (i % 5) for i in range(n)]
+        A = gen.side_from_records([(k, rng.bytes(int(rng.integers(0, 5)))) for k in keys[::2]])
+        B = gen.side_from_records([(k, None if i % 3 == 0 else b"v") for i, k in enumerate(keys[1::2])])
+        _round_trip(A, B, f"{n} records", nav=True)
+    # sub-byte prefixes: keys over bytes that differ in single bits
+    import itertools
+    alpha = [0x00, 0x01, 0x02, 0x40, 0x80, 0x81, 0xFE, 0xFF]
+    keys = sorted({bytes(t) for L in (1, 2, 3) for t in itertools.product(alpha, repeat=L)} | {b""})
+    A = gen.side_from_records([(k, b"a") for k in keys[::3]])
+    B = gen.side_from_records([(k, None if i % 4 == 0 else b"") for i, k in enumerate(keys[1::2])])
+    _round_trip(A, B, "sub-byte prefixes", nav=True)
+    # long inherited chains: each key extends a long shared prefix by one byte
+    keys = sorted({b"p" * int(rng.integers(1, 300)) + bytes([int(rng.integers(0, 256))]) for _ in range(700)})
+    A = gen.side_from_records([(k, rng.bytes(3)) for k in keys[::2]])
+    B = gen.side_from_records([(k, rng.bytes(1)) for k in keys[1::2]])
+    _round_trip(A, B, "long chains", nav=True)
+    # every value 16 bytes: the navigation subtracts a common width
+    keys = [b"fixed%06d" % i for i in range(3000)]
+    A = gen.side_from_records([(k, rng.bytes(16)) for k in keys[::2]])
+    B = gen.side_from_records([(k, rng.bytes(16)) for k in keys[1::2]])
+    _round_trip(A, B, "fixed width", nav=True)
+    # empty payload
+    _round_trip(empty, empty, "empty")
+
+
+def test_decoded_side_merges_again():
+    """A side decoded from a payload enters the merge like any other."""
+    import merge_front_coded_amd as em
+    A, B = workload(1, 0.2)
+    d, want = _round_trip(A, B, "merge again")
+    C, _ = workload(1, 0.1)
+    ref = oracle.run(want, C, items_per_part=256)
+    pl = em.Pipeline(d, em.DeviceSide.from_host(C), items_per_part=256)
+    pl.run()
+    torch.cuda.synchronize()
+    assert (pl.S, pl.T) == (ref["S"], ref["T"])
+    assert np.array_equal(pl.host("final", pl.S), ref["final"])
+    assert pl.payload_bytes() == ref["payload"].tobytes()
+
+
+def test_malformed_lengths_are_reported():
+    import merge_front_coded_amd as em
+    A, B = workload(1, 0.05)
+    pl = run_gpu(A, B, items=256)
+    torch.cuda.synchronize()
+    S, T = pl.S, pl.T
+    for bad_T in (T - 1, T + 1):
+        with pytest.raises(em.EmError):
+            em.fcin_decode(pl.payload, bad_T, S, off=pl.off)
+    with pytest.raises(em.EmError):  # one record fewer: the last block ends early
+        em.fcin_decode(pl.payload, T, S - 1, off=pl.off)

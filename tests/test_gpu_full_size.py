@@ -36,6 +36,49 @@ def _gpu():
     require_gpu()
 
 
+def _copy_runs(dst, dst_start, src, src_start, lens):
+    """dst[dst_start[t] + u] = src[src_start[t] + u] for u < lens[t], all t at once."""
+    lens = lens.astype(np.int64)
+    total = int(lens.sum())
+    if total == 0:
+        return
+    before = np.zeros(lens.size, np.int64)
+    np.cumsum(lens[:-1], out=before[1:])
+    step = np.arange(total, dtype=np.int64)
+    dst[np.repeat(dst_start.astype(np.int64) - before, lens) + step] = \
+        src[np.repeat(src_start.astype(np.int64) - before, lens) + step]
+
+
+def _merged_side(A, B, final):
+    """The survivors' records as one side: keys, values and tombstone flags
+    taken from the inputs through the final references."""
+    final = final.astype(np.int64)
+    isA = final < A.n
+    n = final.size
+    klen = np.zeros(n, np.int64)
+    vlen = np.zeros(n, np.int64)
+    tomb = np.zeros(n, np.uint8)
+    srcs = []
+    for side, mask, idx in ((A, isA, final), (B, ~isA, final - A.n)):
+        sel = np.nonzero(mask)[0]
+        r = idx[sel]
+        ko, vo = side.key_off.astype(np.int64), side.val_off.astype(np.int64)
+        klen[sel] = ko[r + 1] - ko[r]
+        tomb[sel] = side.tomb[r]
+        vlen[sel] = np.where(side.tomb[r] != 0, 0, vo[r + 1] - vo[r])
+        srcs.append((side, sel, r))
+    key_off = np.zeros(n + 1, np.int64)
+    np.cumsum(klen, out=key_off[1:])
+    val_off = np.zeros(n + 1, np.int64)
+    np.cumsum(vlen, out=val_off[1:])
+    keys = np.empty(int(key_off[-1]), np.uint8)
+    vals = np.empty(int(val_off[-1]), np.uint8)
+    for side, sel, r in srcs:
+        _copy_runs(keys, key_off[sel], side.keys, side.key_off[r], klen[sel])
+        _copy_runs(vals, val_off[sel], side.vals, side.val_off[r], vlen[sel])
+    return keys, key_off.astype(np.uint32), vals, val_off.astype(np.uint32), tomb
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_full_size_workload_matches_oracle(wid):
     with open(DIGESTS) as f:
@@ -72,5 +115,22 @@ def test_full_size_workload_matches_oracle(wid):
             want["splits"] = ref["splits"][str(pl.items)]
         bad = [k for k, v in got.items() if v != want[k]]
         assert not bad, f"{path}: outputs differing from the oracle: {bad}"
+        if path == "merge":
+            # the payload decoded back (front-coded input path), block starts
+            # from the offsets and from the navigation: the survivors' records
+            import merge_front_coded_amd as em
+            keys, key_off, vals, val_off, tomb = _merged_side(A, B, pl.host("final", S).astype(np.int64))
+            for how in ("off", "navigation"):
+                print(f"  decode the payload, block starts from {how}", flush=True)
+                d = em.fcin_decode(pl.payload, pl.T, S, **({"off": pl.off} if how == "off" else {"nav": pl.nav}))
+                torch.cuda.synchronize()
+                assert (d.key_bytes, d.val_bytes) == (keys.size, vals.size), how
+                assert np.array_equal(d.key_off[:S + 1].cpu().numpy().view(np.uint32), key_off), how
+                assert np.array_equal(d.val_off[:S + 1].cpu().numpy().view(np.uint32), val_off), how
+                assert np.array_equal(d.tomb[:S].cpu().numpy(), tomb), how
+                assert np.array_equal(d.keys[:keys.size].cpu().numpy(), keys), how
+                assert np.array_equal(d.vals[:vals.size].cpu().numpy(), vals), how
+                del d
+                torch.cuda.empty_cache()
         del pl
         torch.cuda.empty_cache()
