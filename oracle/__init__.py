@@ -15,7 +15,9 @@ sections, an independent section reader (every entry selected back), the
 exact sparse threshold and value widths read back from decoded payloads; the
 payload decoder by a hand-derived payload, malformed lengths, and round trips
 checked against the merged input records and the independent Python
-decoder.  No function here is "parity unpinned".
+decoder; the byte-profile encoder by hand-derived records, LEB128 edge
+values and an independent byte-profile reader.  No function here is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -75,6 +77,10 @@ def _load():
         lib.or_common_width.argtypes = [S, S, P, u32]
         lib.or_ef_entries.argtypes = [P, u32, ctypes.c_uint64, ctypes.c_uint64, P]
         lib.or_ef_encode.argtypes = [P, ctypes.c_uint64, ctypes.c_uint64, P, P, P, P, P]
+        lib.or_bp_width.restype = ctypes.c_uint64
+        lib.or_bp_width.argtypes = [S, S, P, u32]
+        lib.or_bp_encode.restype = ctypes.c_uint64
+        lib.or_bp_encode.argtypes = [S, S, P, u32, ctypes.c_uint64, P, P, P, P, ctypes.c_uint64]
         lib.or_fc_decode.restype = ctypes.c_int
         lib.or_fc_decode.argtypes = [P, ctypes.c_uint64, u32, P, ctypes.c_uint64, P, P, ctypes.c_uint64, P, P]
         _lib = lib
@@ -254,6 +260,30 @@ def fc_decode(payload: np.ndarray, T: int, S: int, key_cap: int, val_cap: int):
         raise ValueError("malformed payload or capacity too small")
     return gen.HostSide(keys=keys[:key_off[S]].copy(), key_off=key_off, vals=vals[:val_off[S]].copy(),
                         val_off=val_off, tomb=tomb)
+
+
+def bp_width(A, B, final: np.ndarray) -> int:
+    """Byte-profile framing width: 1 + L when every present survivor's value
+    is L bytes (or none is present), else 0 (variable framing)."""
+    f = np.ascontiguousarray(final, dtype=np.uint32)
+    return int(_load().or_bp_width(ctypes.byref(_side(A)), ctypes.byref(_side(B)), _ptr(f), f.size))
+
+
+def bp_encode(A, B, final: np.ndarray):
+    """Byte-profile encoding -> dict(width, len_bytes, lcp_bytes, off, T (bytes), payload)."""
+    f = np.ascontiguousarray(final, dtype=np.uint32)
+    S = int(f.size)
+    w = bp_width(A, B, f)
+    len_bytes = np.empty(S, np.uint32)
+    lcp_bytes = np.empty(S, np.uint32)
+    off = np.empty(S + 1, np.uint64)
+    cap = payload_capacity_bytes(A, B) + S * (24 + w)  # (+ w: a tombstone's filler bytes)
+    buf = np.zeros(cap, np.uint8)
+    T = _load().or_bp_encode(ctypes.byref(_side(A)), ctypes.byref(_side(B)), _ptr(f), S, w, _ptr(len_bytes),
+                             _ptr(lcp_bytes), _ptr(off), _ptr(buf), cap)
+    if T == 0xFFFFFFFFFFFFFFFF:
+        raise RuntimeError("oracle payload capacity exceeded")
+    return dict(width=w, len_bytes=len_bytes, lcp_bytes=lcp_bytes, off=off, T=int(T), payload=buf[:T].copy())
 
 
 def run(A, B, items_per_part: int = 2048):

@@ -28,6 +28,8 @@
  *        block-parse paragraph for decoding a payload back into arenas.
  *  [CB]  Everett, "Collision bitmap and rank experiment": "Corrected record
  *        ordinals" (collision bits, exclusive rank R, ordinal formulas).
+ *  [BP]  Everett, "Byte-profile GPU merge": "Pipeline" (byte LEB128 counts,
+ *        byte FC literals, optional-value tags, common value width).
  *
  * Readings where the pages leave a step open (each one is listed with its
  * reason in the project's design notes):
@@ -475,4 +477,133 @@ int or_fc_decode(const uint8_t *payload, uint64_t T, uint32_t S, uint8_t *keys, 
   key_off[S] = (uint32_t)kat;
   val_off[S] = (uint32_t)vat;
   return r.pos == T ? 0 : -1;
+}
+
+/*
+ * [BP]  Everett, "Byte-profile GPU merge": the "Pipeline" steps (byte LEB128
+ * counts, byte FC literals and optional-value tags; a common encoded value
+ * width, where width seventeen means a one-byte presence tag and sixteen
+ * payload bytes), with the control rule of [GC] counted in bytes.
+ *
+ * Readings (the page names the parts, not their bytes):
+ *  - l_i is the byte LCP with the preceding survivor (l_0 = 0), k_i the key
+ *    length in bytes; c_i = 1 + l_i when i mod 15 = 0, else k_{i-1} - l_i;
+ *  - a record is LEB128(c_i), LEB128(k_i - l_i), key bytes l_i .. k_i-1, then
+ *    its value; LEB128 is unsigned little-endian base 128 (low seven bits
+ *    first, the high bit of a byte set when another byte follows);
+ *  - fixed framing when every present survivor's value has the same byte
+ *    length L (or no survivor is present): width W = 1 + L, each value a tag
+ *    byte (1 present, 0 tombstone) and L bytes (zeros for a tombstone);
+ *  - otherwise variable framing: a tombstone is the tag byte 0, a present
+ *    value the tag byte 1, LEB128(byte length) and the bytes; width 0;
+ *  - no padding; the payload is the byte stream.
+ */
+static unsigned leb_len(uint64_t x) {
+  unsigned n = 1;
+  while (x >= 128) {
+    x >>= 7;
+    ++n;
+  }
+  return n;
+}
+
+static uint64_t put_leb(uint8_t *out, uint64_t at, uint64_t cap, uint64_t x, int *over) {
+  do {
+    uint8_t b = (uint8_t)(x & 127);
+    x >>= 7;
+    if (x) b |= 128;
+    if (at < cap)
+      out[at] = b;
+    else
+      *over = 1;
+    ++at;
+  } while (x);
+  return at;
+}
+
+static uint64_t byte_lcp(const uint8_t *p, uint64_t np, const uint8_t *x, uint64_t nx) {
+  uint64_t m = np < nx ? np : nx, t = 0;
+  while (t < m && p[t] == x[t]) ++t;
+  return t;
+}
+
+/* The framing width: 1 + L when every present survivor's value is L bytes
+ * (or none is present), else 0 (variable framing).  0 for S = 0. */
+uint64_t or_bp_width(const or_side *A, const or_side *B, const uint32_t *final_refs, uint32_t S) {
+  int seen = 0;
+  uint64_t L = 0;
+  for (uint32_t i = 0; i < S; ++i) {
+    uint32_t r;
+    const or_side *s = ref_side(A, B, final_refs[i], &r);
+    if (is_tomb(s, r)) continue;
+    uint64_t len = s->val_off[r + 1] - s->val_off[r];
+    if (!seen) {
+      L = len;
+      seen = 1;
+    } else if (len != L) {
+      return 0;
+    }
+  }
+  return S ? 1 + L : 0;
+}
+
+/* Byte-profile encoding of the survivors: len_bytes[S], lcp_bytes[S],
+ * off[S+1] (byte offsets), payload (payload_cap bytes, zeroed by the
+ * caller).  Returns the payload length, or UINT64_MAX when it does not fit. */
+uint64_t or_bp_encode(const or_side *A, const or_side *B, const uint32_t *final_refs, uint32_t S,
+                      uint64_t width, uint32_t *len_bytes, uint32_t *lcp_bytes, uint64_t *off,
+                      uint8_t *payload, uint64_t payload_cap) {
+  uint64_t at = 0, kprev = 0;
+  const uint8_t *prev = 0;
+  int over = 0;
+  for (uint32_t i = 0; i < S; ++i) {
+    uint32_t r;
+    const or_side *s = ref_side(A, B, final_refs[i], &r);
+    const uint8_t *x = key_ptr(s, r);
+    const uint64_t k = key_len(s, r);
+    const uint64_t l = i == 0 ? 0 : byte_lcp(prev, kprev, x, k);
+    const uint64_t c = (i % 15 == 0) ? 1 + l : kprev - l;
+    off[i] = at;
+    at = put_leb(payload, at, payload_cap, c, &over);
+    at = put_leb(payload, at, payload_cap, k - l, &over);
+    for (uint64_t b = l; b < k; ++b) {
+      if (at < payload_cap)
+        payload[at] = x[b];
+      else
+        over = 1;
+      ++at;
+    }
+    const int t = is_tomb(s, r);
+    const uint8_t *v = s->vals + s->val_off[r];
+    const uint64_t vlen = t ? 0 : s->val_off[r + 1] - s->val_off[r];
+    if (at < payload_cap)
+      payload[at] = t ? 0 : 1;
+    else
+      over = 1;
+    ++at;
+    if (width) {
+      for (uint64_t b = 0; b + 1 < width; ++b) {
+        if (at < payload_cap)
+          payload[at] = t ? 0 : v[b];
+        else
+          over = 1;
+        ++at;
+      }
+    } else if (!t) {
+      at = put_leb(payload, at, payload_cap, vlen, &over);
+      for (uint64_t b = 0; b < vlen; ++b) {
+        if (at < payload_cap)
+          payload[at] = v[b];
+        else
+          over = 1;
+        ++at;
+      }
+    }
+    len_bytes[i] = (uint32_t)(at - off[i]);
+    lcp_bytes[i] = (uint32_t)l;
+    prev = x;
+    kprev = k;
+  }
+  off[S] = at;
+  return over ? UINT64_MAX : at;
 }

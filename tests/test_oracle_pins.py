@@ -433,3 +433,69 @@ def test_fc_decode_round_trip(seed):
     # and the independent Python decoder reads the same records
     recs, _ = decode(r["payload"].tobytes(), r["T"], r["S"])
     assert recs == want
+
+
+# ---- byte profile: LEB128 counts, byte literals, presence tags ----
+
+def test_bp_hand_examples():
+    # ab (tombstone), abc ("Z"), b (""): present lengths 1 and 0 differ, so
+    # variable framing.  ab: c = 1, s = 2, 'ab', tag 0.  abc: l = 2,
+    # c = 2 - 2 = 0, s = 1, 'c', tag 1, length 1, 'Z'.  b: l = 0, c = 3 - 0 = 3,
+    # s = 1, 'b', tag 1, length 0.
+    A = gen.side_from_records([(b"ab", b"1"), (b"b", b"")])
+    B = gen.side_from_records([(b"ab", None), (b"abc", b"Z")])
+    r = oracle.run(A, B)
+    bp = oracle.bp_encode(A, B, r["final"])
+    assert bp["width"] == 0
+    assert bp["payload"].tobytes().hex() == "0102616200" + "00016301015a" + "0301620100"
+    assert list(bp["off"]) == [0, 5, 11, 16] and bp["T"] == 16
+    assert list(bp["lcp_bytes"]) == [0, 2, 0] and list(bp["len_bytes"]) == [5, 6, 5]
+    # k1 (tombstone), k2 ("yy"): the one present length is 2, so width 3;
+    # the tombstone's value is tag 0 and two zero bytes
+    A = gen.side_from_records([(b"k1", b"xx"), (b"k2", b"yy")])
+    B = gen.side_from_records([(b"k1", None)])
+    r = oracle.run(A, B)
+    bp = oracle.bp_encode(A, B, r["final"])
+    assert bp["width"] == 3
+    assert bp["payload"].tobytes().hex() == "01026b31000000" + "0101320179 79".replace(" ", "")
+    # LEB128 at 128 and 200: a 200-byte key (s = 200 -> c8 01) and a 128-byte
+    # value under variable framing (length -> 80 01)
+    A = gen.side_from_records([(b"x" * 200, b"v" * 128), (b"y", b"")])
+    r = oracle.run(A, gen.side_from_records([]))
+    bp = oracle.bp_encode(A, gen.side_from_records([]), r["final"])
+    p = bp["payload"].tobytes()
+    assert bp["width"] == 0
+    assert p[:3].hex() == "01c801" and p[203:206].hex() == "018001"
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_bp_round_trip(seed):
+    from bpdecode import decode as bp_decode
+    rng = random.Random(100 + seed)
+    alpha = [0x00, 0x41, 0x7F, 0x80, 0xFF]
+    keys = sorted({bytes(rng.choice(alpha) for _ in range(rng.randrange(0, 7))) for _ in range(300)}
+                  | {b"L" * rng.randrange(120, 260) for _ in range(3)})
+    fixed = seed % 2 == 0
+    def val():
+        if rng.random() < 0.15:
+            return None
+        return bytes(rng.randrange(256) for _ in range(16 if fixed else rng.randrange(0, 140)))
+    a, b = [], []
+    for k in keys:
+        u = rng.random()
+        if u < 0.3:
+            a.append((k, val()))
+            b.append((k, val()))
+        elif u < 0.65:
+            a.append((k, val()))
+        else:
+            b.append((k, val()))
+    A, B = gen.side_from_records(a), gen.side_from_records(b)
+    r = oracle.run(A, B)
+    bp = oracle.bp_encode(A, B, r["final"])
+    assert bp["width"] == (17 if fixed else 0)
+    recs, starts = bp_decode(bp["payload"].tobytes(), r["S"], bp["width"])
+    assert recs == _merged_records(A, B, r["final"])
+    assert starts + [bp["T"]] == [int(x) for x in bp["off"]]
+    # byte LCPs are the bit LCPs' whole bytes
+    assert np.array_equal(bp["lcp_bytes"], r["lcp_bits"] // 8)
