@@ -84,6 +84,9 @@ def parse():
                     help="fraction of the workload the CPU oracle is timed on")
     ap.add_argument("--navigation", action="store_true",
                     help="also time em_ef_navigation (the output navigation) on the step's outputs")
+    ap.add_argument("--byte-profile", action="store_true",
+                    help="also time the byte-profile encoding (em_bp_lengths, em_scan, em_bp_emit) of the step's "
+                         "survivors")
     ap.add_argument("--fcin", action="store_true",
                     help="also time decoding the step's payload back into arenas (em_fcin_parse + _materialize)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -304,6 +307,43 @@ def main():
         result["navigation"] = {"call": "em_ef_navigation", "ms": nav_ms, "entries": nav["n"], "L": nav["L"],
                                 "width": nav["width"], "sparse_entries": nav["n_exceptions"],
                                 "algorithmic_bytes": nav_bytes, "GBps": nav_bytes / (nav_ms * 1e-3) / 1e9}
+        if pn is not pl:
+            del pn
+    if args.byte_profile:
+        # the byte-profile encoding of this step's survivors (lengths and
+        # width, scan, emit; T is known from the warm-up pass, so the timed
+        # passes need no host read)
+        if fused:
+            pn = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
+            pn.run()
+        else:
+            pn = pl
+        W, T = pn.byte_profile()
+        torch.cuda.synchronize()
+        S = pn.S
+        ev = []
+        for it in range(args.steps + 1):
+            a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            a.record(stream)
+            em.em_bp_lengths(A, B, pn.final, pn.lcp, S, pn.bp_len, pn.bp_width, pn.bp_ws, stream)
+            b.record(stream)
+            em.em_scan(pn.bp_len, S, pn.bp_off, pn.ws, stream)
+            c.record(stream)
+            em.em_bp_emit(A, B, pn.final, pn.lcp, S, pn.bp_off, T, pn.bp_width, pn.bp_payload, pn.bp_over, stream)
+            d.record(stream)
+            if it:  # the first pass warms up
+                ev.append((a, b, c, d))
+        torch.cuda.synchronize()
+        assert int(pn.bp_over.item()) == 0 and int(pn.bp_off[S].item()) == T
+        part = [sum(x[k].elapsed_time(x[k + 1]) for x in ev) / len(ev) for k in range(3)]
+        # one pass's minimum: refs, LCPs, key and value offset pairs and tags
+        # read; the suffix and value bytes read (at most T); offsets and the
+        # payload written
+        bp_bytes = S * (4 + 4 + 8 + 8 + 1) + T + 8 * (S + 1) + T
+        result["byte_profile"] = {"calls": ["em_bp_lengths", "em_scan", "em_bp_emit"], "width": W, "T_bytes": T,
+                                  "lengths_ms": part[0], "scan_ms": part[1], "emit_ms": part[2],
+                                  "ms": sum(part), "algorithmic_bytes": bp_bytes,
+                                  "GBps": bp_bytes / (sum(part) * 1e-3) / 1e9}
         if pn is not pl:
             del pn
     if args.fcin:

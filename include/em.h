@@ -363,6 +363,42 @@ int em_fcin_materialize(const uint32_t *payload, uint64_t payload_words, uint32_
                         uint64_t key_cap, uint32_t *key_off, uint8_t *vals, uint64_t val_cap, uint32_t *val_off,
                         uint8_t *tomb, uint64_t *d_totals, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Byte-profile front coding (Everett, "Byte-profile GPU merge", "Pipeline":
+ * byte LEB128 counts, byte FC literals, optional-value tags, a common encoded
+ * value width -- width seventeen is a presence tag and sixteen payload
+ * bytes; with the c_i rule of "GPU construction experiment" in bytes).
+ * Record: LEB128(c_i), LEB128(k_i - l_i), key bytes l_i .. k_i-1, value;
+ * l_i = byte LCP with the preceding survivor (= lcp_bits >> 3), k_i = key
+ * bytes, c_i = 1 + l_i when i mod 15 = 0, else k_{i-1} - l_i.  Value: fixed
+ * framing when every present value has one byte length L (or none is
+ * present): width W = 1 + L, a tag byte (1 present, 0 tombstone) and L bytes
+ * (zeros for a tombstone); else W = 0: tag 0, or tag 1, LEB128(length) and the
+ * bytes.  LEB128 is unsigned, seven bits a byte, low group first.
+ *   em_bp_lengths: d_width[0] (device u32) = W, and len_bytes[S] (u32);
+ *     ws: em_bp_workspace_bytes(S), 256-byte aligned.
+ *   em_scan over len_bytes gives the byte offsets off[S+1] and T = off[S].
+ *   em_bp_emit: the payload bytes (payload_cap >= T); one thread per record.
+ *     d_overflow (device u32) is set to 1 when an offset does not match its
+ *     record, passes payload_cap, or a present value is not W - 1 bytes under
+ *     fixed framing; the payload bytes are then unspecified (nothing is
+ *     written at or past payload_cap).
+ *   em_bp_navigation: the navigation sections of em_ef_navigation over the
+ *     byte offsets, the width taken from d_width (entries off[15k] - 15k W and
+ *     T - S W); arguments and capacities as em_ef_navigation.
+ * final_refs and lcp_bits are those of the keep step and em_fc_lengths.
+ */
+size_t em_bp_workspace_bytes(uint32_t S);
+int em_bp_lengths(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs, const uint32_t *lcp_bits,
+                  uint32_t S, uint32_t *len_bytes, uint32_t *d_width, void *ws, size_t ws_bytes, void *stream);
+int em_bp_emit(const em_side_t *A, const em_side_t *B, const uint32_t *final_refs, const uint32_t *lcp_bits,
+               uint32_t S, const uint64_t *off, uint64_t T, const uint32_t *d_width, uint8_t *payload,
+               uint64_t payload_cap, uint32_t *d_overflow, void *stream);
+int em_bp_navigation(const uint64_t *off, uint32_t S, uint64_t T, const uint32_t *d_width, uint64_t *lows,
+                     uint64_t low_cap, uint64_t *highs, uint64_t high_cap, uint64_t *samples, uint64_t sample_cap,
+                     uint64_t *exceptions, uint64_t exception_cap, em_ef_info_t *info, void *ws, size_t ws_bytes,
+                     void *stream);
+
 /* Text for an EM_* code (static string). */
 const char *em_strerror(int code);
 

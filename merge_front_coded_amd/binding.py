@@ -76,6 +76,10 @@ def load_library(path: str = LIB_PATH):
         "em_fcin_workspace_bytes": (sz, [u32]),
         "em_fcin_parse": (i32, [P, u64, u64, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_fcin_materialize": (i32, [P, u64, u32, P, u64, P, P, u64, P, P, P, P, sz, P]),
+        "em_bp_workspace_bytes": (sz, [u32]),
+        "em_bp_lengths": (i32, [S, S, P, P, u32, P, P, P, sz, P]),
+        "em_bp_emit": (i32, [S, S, P, P, u32, P, u64, P, P, u64, P, P]),
+        "em_bp_navigation": (i32, [P, u32, u64, P, P, u64, P, u64, P, u64, P, u64, P, P, sz, P]),
         "em_strerror": (ctypes.c_char_p, [i32]),
         "em_last_hip_error": (i32, []),
     }
@@ -365,3 +369,24 @@ def fcin_decode(payload, T: int, S: int, off=None, nav: "EfSections | None" = No
         raise EmError(EM_EINVAL, "em_fcin_materialize: " + ", ".join(m for b, m in FCIN_ERRORS.items() if err & b),
                       lib())
     return DeviceSide(keys, key_off, vals, val_off, tomb, S, kb, vb)
+
+
+# ---- byte profile (include/em.h: em_bp_*) ----
+
+def em_bp_workspace_bytes(S: int) -> int:
+    return int(lib().em_bp_workspace_bytes(S))
+
+
+def em_bp_lengths(A, B, final_refs, lcp_bits, S, len_bytes, d_width, ws, stream=None):
+    _check(lib().em_bp_lengths(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), _p(lcp_bits), S,
+                               _p(len_bytes), _p(d_width), _p(ws), ws.numel(), _stream(stream)), "em_bp_lengths")
+
+
+def em_bp_emit(A, B, final_refs, lcp_bits, S, off, T, d_width, payload, d_overflow, stream=None):
+    _check(lib().em_bp_emit(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(final_refs), _p(lcp_bits), S,
+                            _p(off), T, _p(d_width), _p(payload), payload.numel(), _p(d_overflow), _stream(stream)),
+           "em_bp_emit")
+
+
+def em_bp_navigation(off, S, T, d_width, sec: "EfSections", stream=None):
+    _check(lib().em_bp_navigation(_p(off), S, T, _p(d_width), *sec._args(), _stream(stream)), "em_bp_navigation")

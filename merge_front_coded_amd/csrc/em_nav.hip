@@ -109,12 +109,18 @@ __global__ __launch_bounds__(kNavBlock) void k_ef_width(em_side_t A, em_side_t B
   }
 }
 
-// The header: common width, n, L, section lengths.
+// The header: common width, n, L, section lengths.  width_in >= 0: that
+// width; kWidthOnDevice: vmin[0] holds it; else the value widths' min and max
+// in vmin decide.
+constexpr int64_t kWidthOnDevice = -2;
+
 __global__ void k_ef_header(EfSrc src, uint32_t n, int64_t width_in, const uint32_t* __restrict__ vmin,
                             em_ef_info_t* __restrict__ info) {
   uint64_t w = 0;
   if (width_in >= 0)
     w = static_cast<uint64_t>(width_in);
+  else if (width_in == kWidthOnDevice)
+    w = vmin[0];
   else if (src.S > 0 && vmin[0] == vmin[1])
     w = vmin[0];
   const uint64_t last = src.entry(n - 1, w);
@@ -221,10 +227,14 @@ __global__ __launch_bounds__(kNavBlock) void k_ef_exceptions(EfSrc src, const em
 
 static int ef_run(const EfSrc& src, uint32_t n, int64_t width_in, const em_side_t* A, const em_side_t* B,
                   const uint32_t* final_refs, uint64_t* lows, uint64_t* highs, uint64_t* samples,
-                  uint64_t* exceptions, em_ef_info_t* info, void* ws, hipStream_t st) {
+                  uint64_t* exceptions, em_ef_info_t* info, void* ws, hipStream_t st,
+                  const uint32_t* width_dev = nullptr) {
   const uint32_t groups = (n + kNavGroup - 1) / kNavGroup;
-  const EfWs L = ef_layout(ws, groups);
-  if (width_in < 0) {
+  EfWs L = ef_layout(ws, groups);
+  if (width_dev) {
+    L.vmin = const_cast<uint32_t*>(width_dev);  // (read only)
+    width_in = kWidthOnDevice;
+  } else if (width_in < 0) {
     hipLaunchKernelGGL(k_ef_init, dim3(1), dim3(1), 0, st, L.vmin);
     if (src.S)
       hipLaunchKernelGGL(k_ef_width, dim3(min(nav_blocks(src.S), kNavWidthGrid)), dim3(kNavBlock), 0, st, *A, *B,
@@ -319,4 +329,23 @@ extern "C" int em_ef_encode(const uint64_t* entries, uint32_t n, uint64_t width,
   const EfSrc src{nullptr, entries, 0, 0};
   return ef_run(src, n, static_cast<int64_t>(width), nullptr, nullptr, nullptr, lows, highs, samples, exceptions,
                 info, ws, as_stream(stream));
+}
+
+extern "C" int em_bp_navigation(const uint64_t* off, uint32_t S, uint64_t T, const uint32_t* d_width,
+                                uint64_t* lows, uint64_t low_cap, uint64_t* highs, uint64_t high_cap,
+                                uint64_t* samples, uint64_t sample_cap, uint64_t* exceptions,
+                                uint64_t exception_cap, em_ef_info_t* info, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!d_width || (S && !off)) return EM_EINVAL;
+  if (S >= EM_MAX_RECORDS) return EM_ERANGE;
+  if ((S == 0) != (T == 0)) return EM_EINVAL;
+  const uint32_t n = ef_entries(S);
+  const uint64_t caps[4] = {low_cap, high_cap, sample_cap, exception_cap};
+  int rc = ef_check_out(n, lows, highs, samples, exceptions, info, caps);
+  if (rc) return rc;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return EM_EINVAL;
+  if (ws_bytes < em_ef_workspace_bytes(n)) return EM_ENOSPC;
+  const EfSrc src{off, nullptr, T, S};
+  return ef_run(src, n, kWidthOnDevice, nullptr, nullptr, nullptr, lows, highs, samples, exceptions, info, ws,
+                as_stream(stream), d_width);
 }

@@ -136,6 +136,38 @@ class Pipeline:
         em.em_ef_navigation(self.A, self.B, self.final, self.S, self.off, self.T, self.nav, stream)
         return self.nav
 
+    def byte_profile(self, stream=None):
+        """The byte-profile encoding of the last run's survivors (em_bp_lengths,
+        em_scan, em_bp_emit): returns (width, T in bytes); the payload is in
+        self.bp_payload, the byte offsets in self.bp_off.  Needs the
+        survivors' references and LCPs: any path but the fused one with
+        keep_all=False."""
+        if self.path == "fused" and not self.keep_all:
+            raise ValueError("the fused path keeps final refs and LCPs only with keep_all=True")
+        if self.lcp is None:
+            raise ValueError("the byte profile needs the bit LCPs (keep_lcp=True)")
+        if self.path == "fused":
+            self.read_counts()
+        S = self.S
+        if getattr(self, "bp_len", None) is None:
+            i32 = dict(dtype=torch.int32, device=self.final.device)
+            self.bp_len = torch.empty(max(self.N, 1) + 4, **i32)
+            self.bp_off = torch.empty(self.N + 1, dtype=torch.int64, device=self.final.device)
+            self.bp_width = torch.zeros(1, **i32)
+            self.bp_over = torch.zeros(1, **i32)
+            self.bp_ws = torch.empty(max(em.em_bp_workspace_bytes(self.N), 256), dtype=torch.uint8,
+                                     device=self.final.device)
+            self.bp_payload = None  # sized from T at the first call
+        em.em_bp_lengths(self.A, self.B, self.final, self.lcp, S, self.bp_len, self.bp_width, self.bp_ws, stream)
+        em.em_scan(self.bp_len, S, self.bp_off, self.ws, stream)
+        T = int(self.bp_off[S].item())
+        W = int(self.bp_width.item())
+        if self.bp_payload is None or self.bp_payload.numel() < T:
+            self.bp_payload = torch.zeros(max(T, 1) + 16, dtype=torch.uint8, device=self.final.device)
+        em.em_bp_emit(self.A, self.B, self.final, self.lcp, S, self.bp_off, T, self.bp_width, self.bp_payload,
+                      self.bp_over, stream)
+        return W, T
+
     def read_counts(self):
         self.S = int(self.d_S.item()) & 0xFFFFFFFF
         self.T = int(self.d_T.item())

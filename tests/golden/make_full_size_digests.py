@@ -44,6 +44,16 @@ def ef_digest(nav) -> str:
     return sha(head, nav["lows"], nav["highs"], nav["samples"], nav["exceptions"])
 
 
+def bp_digest(A, B, final) -> dict:
+    """The byte-profile encoding: width, T, and digests of the record lengths,
+    byte offsets, payload and the navigation over the byte offsets."""
+    bp = oracle.bp_encode(A, B, final)
+    S = int(final.size)
+    nav = oracle.ef_encode(oracle.ef_entries(bp["off"], S, bp["T"], bp["width"]), bp["width"])
+    return {"width": bp["width"], "T": bp["T"], "len_bytes": sha(bp["len_bytes"]), "off": sha(bp["off"]),
+            "payload": sha(bp["payload"]), "ef": ef_digest(nav)}
+
+
 def main(ids):
     data = {}
     if os.path.exists(OUT):
@@ -63,6 +73,7 @@ def main(ids):
             "len_bits": sha(len_bits), "lcp_bits": sha(lcp_bits), "off": sha(off),
             "payload": sha(payload), "payload_bytes": int(payload.size),
             "ef": ef_digest(oracle.ef_navigation(A, B, final, off, T)),
+            "bp": bp_digest(A, B, final),
         }
         print(f"workload {wid}: S={S} T={T} ({time.time() - t0:.1f}s)", flush=True)
         with open(OUT, "w") as f:

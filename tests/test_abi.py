@@ -123,3 +123,24 @@ def test_argument_errors_before_any_launch(lib):
     assert lib.em_collision_rank_mode(ctypes.byref(A5), ctypes.byref(B), 3, buf, None, None, buf,
                                       ctypes.c_void_p(0x100000), lib.em_collision_workspace_bytes(5, 0, 2),
                                       None) == -3
+
+
+def test_byte_profile_argument_errors(lib):
+    A5, B = _side(n=5, key_bytes=5, val_bytes=0), _side()
+    buf = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.em_bp_workspace_bytes(5) >= 16
+    # more survivors than records; no width output; misaligned or small workspace
+    assert lib.em_bp_lengths(ctypes.byref(A5), ctypes.byref(B), buf, buf, 6, buf, buf, ws, 256, None) == -1
+    assert lib.em_bp_lengths(ctypes.byref(A5), ctypes.byref(B), buf, buf, 5, buf, None, ws, 256, None) == -1
+    assert lib.em_bp_lengths(ctypes.byref(A5), ctypes.byref(B), buf, buf, 5, buf, buf,
+                             ctypes.c_void_p(0x100008), 256, None) == -1
+    assert lib.em_bp_lengths(ctypes.byref(A5), ctypes.byref(B), buf, buf, 5, buf, buf, ws, 0, None) == -3
+    # emit: S and T agree on emptiness; payload capacity; overflow flag required
+    assert lib.em_bp_emit(ctypes.byref(A5), ctypes.byref(B), buf, buf, 0, buf, 5, buf, buf, 10, buf, None) == -1
+    assert lib.em_bp_emit(ctypes.byref(A5), ctypes.byref(B), buf, buf, 5, buf, 50, buf, buf, 49, buf, None) == -3
+    assert lib.em_bp_emit(ctypes.byref(A5), ctypes.byref(B), buf, buf, 5, buf, 50, buf, buf, 64, None, None) == -1
+    # navigation over byte offsets: the width comes from the device; record cap
+    assert lib.em_bp_navigation(buf, 5, 50, None, buf, 8, buf, 8, buf, 8, buf, 8, buf, ws, 1 << 20, None) == -1
+    assert lib.em_bp_navigation(buf, 1 << 24, 50, buf, buf, 8, buf, 8, buf, 8, buf, 8, buf, ws, 1 << 20,
+                                None) == -2

@@ -79,6 +79,26 @@ def _merged_side(A, B, final):
     return keys, key_off.astype(np.uint32), vals, val_off.astype(np.uint32), tomb
 
 
+def _byte_profile_digest(pl):
+    """The byte-profile encoding of a run, digested as the oracle's is."""
+    import merge_front_coded_amd as em
+    W, T = pl.byte_profile()
+    torch.cuda.synchronize()
+    S = pl.S
+    assert int(pl.bp_over.item()) == 0
+    sec = em.EfSections(em.em_ef_entry_count(S))
+    em.em_bp_navigation(pl.bp_off, S, T, pl.bp_width, sec)
+    nav = sec.host()
+    head = np.array([nav[k] for k in ("n", "L", "width", "low_words", "high_bits", "high_words", "groups",
+                                      "n_exceptions")], np.uint64)
+    out = {"width": W, "T": T, "len_bytes": _sha(pl.bp_len[:S].cpu().numpy()),
+           "off": _sha(pl.bp_off[:S + 1].cpu().numpy()), "payload": _sha(pl.bp_payload[:T].cpu().numpy()),
+           "ef": _sha(head, nav["lows"], nav["highs"], nav["samples"], nav["exceptions"])}
+    del sec
+    pl.bp_payload = None
+    return out
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_full_size_workload_matches_oracle(wid):
     with open(DIGESTS) as f:
@@ -109,6 +129,7 @@ def test_full_size_workload_matches_oracle(wid):
         head = np.array([nav[k] for k in ("n", "L", "width", "low_words", "high_bits", "high_words", "groups",
                                           "n_exceptions")], np.uint64)
         got["ef"] = _sha(head, nav["lows"], nav["highs"], nav["samples"], nav["exceptions"])
+        got["bp"] = _byte_profile_digest(pl)
         want = dict(ref)
         if path == "merge":
             got["splits"] = _sha(pl.host("splits"))
