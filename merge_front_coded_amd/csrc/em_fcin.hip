@@ -24,6 +24,8 @@
 // contiguous: the owner j of bit r_i - 1 owns all of [r_j, r_i) (every record
 // after j up to i retains more than r_i - 1 bits), then the owner of bit
 // r_j - 1 takes over, and so on down to a record with r = 0.
+#include <algorithm>
+
 #include "em_internal.h"
 
 namespace em {
@@ -102,35 +104,36 @@ struct FiBits {
   }
 };
 
-// A bit reader bounded by T; a read past T sets kFiErrRange.
-struct FiReader {
-  FiBits b;
-  uint64_t pos, T;
-  uint64_t err;
-  __device__ __forceinline__ uint32_t take(uint32_t n) {  // n in 0..32
-    if (n == 0) return 0;
-    if (pos + n > T) {
-      err |= kFiErrRange;
-      pos = T;
-      return 0;
-    }
-    const uint32_t v = b.at32(pos) >> (32u - n);
-    pos += n;
-    return v;
+// The payload as a bit stream read through an LDS copy of words
+// [w0, w0 + n) (raw, as stored), the rest from global memory: the same
+// values as FiBits, for a workgroup that staged the span it reads.
+struct FiWin {
+  const uint32_t* lds;
+  uint64_t w0;
+  uint32_t n;
+  FiBits g;
+  __device__ __forceinline__ uint32_t word(uint64_t i) const {
+    const uint64_t d = i - w0;
+    return d < n ? __builtin_bswap32(lds[d]) : g.word(i);
   }
-  // order-0 Exp-Golomb: z zero bits, then z + 1 bits holding x + 1 (x < 2^31 here)
-  __device__ __forceinline__ uint32_t eg0() {
-    const uint32_t win = pos < T ? b.at32(pos) : 0u;
-    const uint32_t z = win ? static_cast<uint32_t>(__builtin_clz(win)) : 32u;
-    if (z > 31u || pos + 2 * z + 1 > T) {
-      err |= kFiErrRange;
-      pos = T;
-      return 0;
-    }
-    pos += z;
-    return take(z + 1) - 1u;
+  __device__ __forceinline__ uint32_t at32(uint64_t x) const {
+    const uint64_t i = x >> 5;
+    const uint32_t s = static_cast<uint32_t>(x & 31u);
+    const uint32_t hi = word(i), lo = word(i + 1);
+    return s ? __builtin_amdgcn_alignbit(hi, lo, 32u - s) : hi;
   }
 };
+
+// Words [w0, w1) of the payload (clamped to the stored words and to cap)
+// into lds by the whole workgroup, coalesced; returns how many it holds.
+// The caller synchronises before reading them.
+__device__ __forceinline__ uint32_t fi_stage(uint32_t* __restrict__ lds, uint32_t cap, const FiBits& g, uint64_t w0,
+                                             uint64_t w1) {
+  w1 = min(w1, g.nwords);
+  const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min<uint64_t>(w1 - w0, cap)) : 0u;
+  for (uint32_t t = threadIdx.x; t < n; t += blockDim.x) lds[t] = g.w[w0 + t];
+  return n;
+}
 
 // ---- block starts ----
 
@@ -188,14 +191,12 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_starts_ef(const em_ef_info_t* _
 // ---- block parse: one thread per block of at most 15 records ----
 
 // 64 bits of the payload from bit x on (MSB first, zero past the stored words)
-__device__ __forceinline__ uint64_t fi_peek64(const uint32_t* __restrict__ w, uint64_t nwords, uint64_t x) {
+__device__ __forceinline__ uint64_t fi_peek64(const FiWin& b, uint64_t x) {
   const uint64_t i = x >> 5;
   const uint32_t sft = static_cast<uint32_t>(x & 31u);
-  const uint32_t a = i < nwords ? __builtin_bswap32(w[i]) : 0u;
-  const uint32_t b = i + 1 < nwords ? __builtin_bswap32(w[i + 1]) : 0u;
-  const uint32_t c = i + 2 < nwords ? __builtin_bswap32(w[i + 2]) : 0u;
-  const uint32_t hi = sft ? __builtin_amdgcn_alignbit(a, b, 32u - sft) : a;
-  const uint32_t lo = sft ? __builtin_amdgcn_alignbit(b, c, 32u - sft) : b;
+  const uint32_t a = b.word(i), c1 = b.word(i + 1), c2 = b.word(i + 2);
+  const uint32_t hi = sft ? __builtin_amdgcn_alignbit(a, c1, 32u - sft) : a;
+  const uint32_t lo = sft ? __builtin_amdgcn_alignbit(c1, c2, 32u - sft) : c1;
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
@@ -212,34 +213,49 @@ __device__ __forceinline__ uint32_t fi_eg0_win(uint64_t win, uint32_t& len) {
   return static_cast<uint32_t>(win >> (64 - len)) - 1u;
 }
 
-// Parse: one thread per block.  Each record costs two 64-bit windows (its
-// two controls, then the value header); the outputs go through restrict
-// pointers, so that no store holds back a later load.
-__global__ __launch_bounds__(kFiBlock) void k_fi_parse(const uint32_t* __restrict__ payload, uint64_t nwords,
-                                                       uint64_t T, uint32_t S, uint32_t nb,
-                                                       const uint64_t* __restrict__ starts,
-                                                       uint32_t* __restrict__ r_out, uint32_t* __restrict__ kbytes,
-                                                       uint32_t* __restrict__ vbytes, uint64_t* __restrict__ lit,
-                                                       uint64_t* __restrict__ vbit, uint8_t* __restrict__ tflag,
-                                                       uint64_t* __restrict__ err) {
-  const uint32_t k = blockIdx.x * kFiBlock + threadIdx.x;
-  if (k >= nb) return;
+// Parse: a one-wave workgroup takes G consecutive blocks (G chosen so that
+// their span of the payload, which is contiguous, usually fits the LDS
+// window), stages that span with coalesced loads and parses one block per
+// lane from LDS (reads past the staged words go to global memory).  Each
+// record costs two 64-bit windows (its two controls, then the value header);
+// the outputs go through restrict pointers, so that no store holds back a
+// later load.
+constexpr uint32_t kFiParseWave = 64;
+constexpr uint32_t kFiParseWords = 2048;  // 8 KB of payload
+
+__global__ __launch_bounds__(kFiParseWave) void k_fi_parse(FiBits bits, uint64_t T, uint32_t S, uint32_t nb,
+                                                           uint32_t G, const uint64_t* __restrict__ starts,
+                                                           uint32_t* __restrict__ r_out,
+                                                           uint32_t* __restrict__ kbytes,
+                                                           uint32_t* __restrict__ vbytes, uint64_t* __restrict__ lit,
+                                                           uint64_t* __restrict__ vbit, uint8_t* __restrict__ tflag,
+                                                           uint64_t* __restrict__ err) {
+  __shared__ uint32_t span[kFiParseWords];
+  const uint32_t k0 = blockIdx.x * G;
+  const uint32_t k1 = min(k0 + G, nb);
+  const uint64_t p0 = starts[k0], p1 = k1 < nb ? starts[k1] : T;
+  // (+3 words: a 64-bit window at the last value header reads three)
+  const uint64_t w0 = p0 >> 5;
+  const uint32_t n = p1 >= p0 ? fi_stage(span, kFiParseWords, bits, w0, (p1 >> 5) + 3) : 0u;
+  __syncthreads();
+  const FiWin win{span, w0, n, bits};
+  const uint32_t k = k0 + threadIdx.x;
+  if (threadIdx.x >= G || k >= k1) return;
   const uint32_t i0 = k * kFiRecs, i1 = min(i0 + kFiRecs, S);
   uint64_t pos = starts[k];
   const uint64_t end = k + 1 < nb ? starts[k + 1] : T;
   uint64_t e = pos > T ? static_cast<uint64_t>(kFiErrBlock) : 0;
   uint32_t kprev = 0;
   for (uint32_t i = i0; i < i1 && !e; ++i) {
-    uint64_t win = fi_peek64(payload, nwords, pos);
+    uint64_t w64 = fi_peek64(win, pos);
     uint32_t n1, n2;
-    const uint32_t c = fi_eg0_win(win, n1);
+    const uint32_t c = fi_eg0_win(w64, n1);
     uint32_t s = 0;
     if (n1) {
-      if (n1 < 64) s = fi_eg0_win(win << n1, n2);
+      if (n1 < 64) s = fi_eg0_win(w64 << n1, n2);
       if (n1 == 64 || n1 + n2 > 64 || n2 == 0) {  // (a rare long pair: read the second code afresh)
-        win = fi_peek64(payload, nwords, pos + n1);
-        s = fi_eg0_win(win, n2);
-        n2 = n2 ? n2 : 0;
+        w64 = fi_peek64(win, pos + n1);
+        s = fi_eg0_win(w64, n2);
         if (!n2) e |= kFiErrRange;
       }
     } else {
@@ -262,7 +278,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_parse(const uint32_t* __restric
     lit[i] = pos;
     pos += s;  // the literal
     // value header: presence bit, then EG0(byte length)
-    const uint64_t vw = fi_peek64(payload, nwords, pos);
+    const uint64_t vw = fi_peek64(win, pos);
     uint32_t vlen = 0, nv = 1;
     const bool present = (vw >> 63) != 0;
     if (present) {
@@ -335,16 +351,30 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_pse(FiLayout L) {
   L.pse[i] = r ? fi_owner(L.tree, L.P2, i, r - 1) : kFiInf;
 }
 
-// nbytes bytes from payload bit x on: sixteen at a time, the four loads of
-// a group issued before its stores (a byte store may alias any load, so a
-// load after it would wait for it), whole words where the destination is
-// aligned.
-__device__ __forceinline__ void fi_copy_bytes(FiBits bits, uint64_t x, uint8_t* __restrict__ dst, uint32_t nbytes) {
+// nbytes bytes from payload bit x on.  Output dword m is bits
+// [x + 32m, x + 32m + 32), one funnel shift of payload words i0 + m and
+// i0 + m + 1 (i0 = x / 32), so each payload word is read once; sixteen bytes
+// at a time with the four loads of a group issued before its stores (a byte
+// store may alias any load, so a load after it would wait for it), whole
+// words where the destination is aligned.
+template <class Bits>
+__device__ __forceinline__ void fi_copy_bytes(const Bits& bits, uint64_t x, uint8_t* __restrict__ dst,
+                                              uint32_t nbytes) {
+  if (nbytes == 0) return;
+  const uint64_t i0 = x >> 5;
+  const uint32_t sh = static_cast<uint32_t>(x & 31u);
+  uint32_t prev = bits.word(i0);
   uint32_t m = 0;
   for (; m + 16 <= nbytes; m += 16) {
-    uint32_t v[4];
+    uint32_t nx[4], v[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = bits.at32(x + 8ull * (m + 4 * t));
+    for (int t = 0; t < 4; ++t) nx[t] = bits.word(i0 + m / 4 + 1 + t);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t a = t ? nx[t - 1] : prev;
+      v[t] = sh ? __builtin_amdgcn_alignbit(a, nx[t], 32u - sh) : a;
+    }
+    prev = nx[3];
     if ((reinterpret_cast<uintptr_t>(dst + m) & 3) == 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) *reinterpret_cast<uint32_t*>(dst + m + 4 * t) = __builtin_bswap32(v[t]);
@@ -354,7 +384,9 @@ __device__ __forceinline__ void fi_copy_bytes(FiBits bits, uint64_t x, uint8_t* 
     }
   }
   for (; m < nbytes; m += 4) {
-    const uint32_t v = bits.at32(x + 8ull * m);
+    const uint32_t nx = bits.word(i0 + m / 4 + 1);
+    const uint32_t v = sh ? __builtin_amdgcn_alignbit(prev, nx, 32u - sh) : prev;
+    prev = nx;
     const uint32_t n = nbytes - m < 4 ? nbytes - m : 4;
     for (uint32_t t = 0; t < n; ++t) dst[m + t] = static_cast<uint8_t>(v >> (24 - 8 * t));
   }
@@ -364,7 +396,8 @@ __device__ __forceinline__ void fi_copy_bytes(FiBits bits, uint64_t x, uint8_t* 
 // bits [lo, hi] with key bit q at payload bit base + q.  head = kFiInf: the
 // chain runs to the end; else bits below a fragment whose pse is at or
 // before `head` come from the head's key in the arena.
-__device__ __forceinline__ void fi_key(FiBits bits, const FiLayout& L, uint32_t i, uint32_t head,
+template <class Bits>
+__device__ __forceinline__ void fi_key(const Bits& bits, const FiLayout& L, uint32_t i, uint32_t head,
                                        const uint8_t* __restrict__ head_key, uint8_t* __restrict__ key,
                                        uint32_t kb, uint64_t* __restrict__ err) {
   uint32_t j = i;
@@ -426,33 +459,110 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
 }
 
 // every record: offsets, tombstone flag, value bytes, and the key of a
-// record that is not a block head
-__global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L, uint8_t* __restrict__ keys,
-                                                         uint64_t key_cap, uint32_t* __restrict__ key_off,
-                                                         uint8_t* __restrict__ vals, uint64_t val_cap,
-                                                         uint32_t* __restrict__ val_off,
-                                                         uint8_t* __restrict__ tomb,
-                                                         uint64_t* __restrict__ err) {
-  const uint32_t i = blockIdx.x * kFiBlock + threadIdx.x;
-  if (i > L.S) return;
+// record that is not a block head.  A workgroup takes rpb consecutive records
+// (one a thread; rpb a multiple of 15, so whole blocks), whose key bytes and
+// value bytes are two contiguous ranges.  When both fit the LDS window (each
+// from the 16-byte boundary below its start), the records are written there
+// and the workgroup copies the two ranges out with 16-byte stores, single
+// bytes only in the groups it shares with its neighbours.  In the window a key
+// is built as the encoder defined it: a block head's key is copied from the
+// arena (the kernel before wrote it); every other record writes its literal,
+// then, in fourteen rounds (round j: the records at block position j), takes
+// its first r_i bits from its predecessor's finished key.  A workgroup whose
+// ranges do not fit writes each record to the arenas directly, its key by the
+// owner chain.
+constexpr uint32_t kFiWin = 24576;
+
+// [b0, b1) of an arena from its window copy starting at base = b0 & ~15
+__device__ __forceinline__ void fi_copy_out(uint8_t* __restrict__ arena, const uint8_t* __restrict__ w,
+                                            uint64_t base, uint64_t b0, uint64_t b1) {
+  const uint32_t groups = static_cast<uint32_t>((b1 - base + 15) >> 4);
+  for (uint32_t g = threadIdx.x; g < groups; g += kFiBlock) {
+    const uint64_t a = base + 16ull * g;
+    if (a >= b0 && a + 16 <= b1) {
+      *reinterpret_cast<uint4*>(arena + a) = *reinterpret_cast<const uint4*>(w + 16 * g);
+    } else {
+      for (uint32_t t = 0; t < 16; ++t)
+        if (a + t >= b0 && a + t < b1) arena[a + t] = w[16 * g + t];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L, uint32_t rpb,
+                                                         uint8_t* __restrict__ keys, uint64_t key_cap,
+                                                         uint32_t* __restrict__ key_off, uint8_t* __restrict__ vals,
+                                                         uint64_t val_cap, uint32_t* __restrict__ val_off,
+                                                         uint8_t* __restrict__ tomb, uint64_t* __restrict__ err) {
+  __shared__ __align__(16) uint8_t win[kFiWin];
   if (L.S == 0) {  // (nothing was parsed or scanned)
-    key_off[0] = val_off[0] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) key_off[0] = val_off[0] = 0;
     return;
   }
-  const uint64_t ko = L.koff[i], vo = L.voff[i];
-  key_off[i] = static_cast<uint32_t>(ko);
-  val_off[i] = static_cast<uint32_t>(vo);
-  if (i == L.S) return;
-  tomb[i] = L.tflag[i];
-  if (!fi_record_ok(L, i, key_cap, val_cap)) {
-    const bool prefix = i > 0 && L.r[i] > 8u * L.kbytes[i - 1];
-    atomicOr(reinterpret_cast<unsigned long long*>(err),
-             static_cast<unsigned long long>(prefix ? kFiErrPrefix : kFiErrCap));
-    return;
+  const uint32_t r0 = blockIdx.x * rpb, r1 = min(r0 + rpb, L.S);
+  const uint64_t kb0 = L.koff[r0], kb1 = L.koff[r1], vb0 = L.voff[r0], vb1 = L.voff[r1];
+  const uint64_t kbase = kb0 & ~static_cast<uint64_t>(15), vbase = vb0 & ~static_cast<uint64_t>(15);
+  const uint64_t kspan = (kb1 - kbase + 15) & ~static_cast<uint64_t>(15);
+  const uint64_t vspan = (vb1 - vbase + 15) & ~static_cast<uint64_t>(15);
+  const bool staged = kb0 <= kb1 && vb0 <= vb1 && kb1 <= key_cap && vb1 <= val_cap &&
+                      kspan + vspan <= kFiWin;  // (uniform over the workgroup)
+  uint8_t* kwin = win;
+  uint8_t* vwin = win + (staged ? kspan : 0);
+  const uint32_t i = r0 + threadIdx.x;
+  bool ok = false;  // a staged record that takes its prefix in the rounds
+  if (threadIdx.x < rpb && i < r1) {
+    const uint64_t ko = L.koff[i], vo = L.voff[i];
+    key_off[i] = static_cast<uint32_t>(ko);
+    val_off[i] = static_cast<uint32_t>(vo);
+    tomb[i] = L.tflag[i];
+    const uint32_t kb = L.kbytes[i], vb = L.vbytes[i];
+    const uint32_t head = i - i % kFiRecs;
+    if (!fi_record_ok(L, i, key_cap, val_cap)) {
+      const bool prefix = i > 0 && L.r[i] > 8u * L.kbytes[i - 1];
+      atomicOr(reinterpret_cast<unsigned long long*>(err),
+               static_cast<unsigned long long>(prefix ? kFiErrPrefix : kFiErrCap));
+    } else if (staged) {
+      uint8_t* key = kwin + (ko - kbase);
+      if (i != head) {
+        // the literal: key bits [r_i, 8 kb); a byte it shares with the
+        // inherited prefix gets its low bits here, its high bits in the round
+        const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
+        if (part && b < kb) {
+          key[b] = static_cast<uint8_t>(bits.at32(L.lit[i]) >> (24u + part));
+          fi_copy_bytes(bits, L.lit[i] + (8u - part), key + b + 1, kb - b - 1);
+        } else if (b < kb) {
+          fi_copy_bytes(bits, L.lit[i], key + b, kb - b);
+        }
+        ok = true;
+      } else {
+        for (uint32_t t = 0; t < kb; ++t) key[t] = keys[ko + t];
+      }
+      fi_copy_bytes(bits, L.vbit[i], vwin + (vo - vbase), vb);
+    } else {
+      if (i != head) fi_key(bits, L, i, head, keys + L.koff[head], keys + ko, kb, err);
+      fi_copy_bytes(bits, L.vbit[i], vals + vo, vb);
+    }
   }
-  const uint32_t head = i - i % kFiRecs;
-  if (i != head) fi_key(bits, L, i, head, keys + L.koff[head], keys + ko, L.kbytes[i], err);
-  fi_copy_bytes(bits, L.vbit[i], vals + vo, L.vbytes[i]);
+  if (r1 == L.S && threadIdx.x == 0) {
+    key_off[L.S] = static_cast<uint32_t>(L.koff[L.S]);
+    val_off[L.S] = static_cast<uint32_t>(L.voff[L.S]);
+  }
+  if (!staged) return;
+  const uint32_t pos = threadIdx.x % kFiRecs;  // (r0 is a multiple of 15)
+  for (uint32_t j = 1; j < kFiRecs; ++j) {
+    __syncthreads();
+    if (ok && pos == j) {
+      // bits [0, r_i) from the predecessor's key (at least r_i bits long: the
+      // record passed the prefix check)
+      uint8_t* key = kwin + (L.koff[i] - kbase);
+      const uint8_t* pk = kwin + (L.koff[i - 1] - kbase);
+      const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
+      for (uint32_t t = 0; t < b; ++t) key[t] = pk[t];
+      if (part && b < L.kbytes[i]) key[b] = static_cast<uint8_t>((pk[b] & (0xFF00u >> part)) | key[b]);
+    }
+  }
+  __syncthreads();
+  fi_copy_out(keys, kwin, kbase, kb0, kb1);
+  fi_copy_out(vals, vwin, vbase, vb0, vb1);
 }
 
 // totals and the size checks, after the scans
@@ -495,8 +605,12 @@ extern "C" int em_fcin_parse(const uint32_t* payload, uint64_t payload_words, ui
   else
     hipLaunchKernelGGL(k_fi_starts_ef, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, nav_info, nav_lows, nav_highs,
                        nav_samples, nav_exceptions, L.nb, L.starts);
-  hipLaunchKernelGGL(k_fi_parse, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, payload, payload_words, T, S, L.nb,
-                     L.starts, L.r, L.kbytes, L.vbytes, L.lit, L.vbit, L.tflag, d_totals + 2);
+  // blocks per parse workgroup: the mean block filling three quarters of the staged span
+  const uint64_t mean_block = std::max<uint64_t>(1, (T / 8 + L.nb - 1) / L.nb);
+  const uint32_t G = static_cast<uint32_t>(
+      std::max<uint64_t>(1, std::min<uint64_t>(kFiParseWave, (3 * 4 * kFiParseWords / 4) / mean_block)));
+  hipLaunchKernelGGL(k_fi_parse, dim3((L.nb + G - 1) / G), dim3(kFiParseWave), 0, st, bits, T, S, L.nb, G, L.starts,
+                     L.r, L.kbytes, L.vbytes, L.lit, L.vbit, L.tflag, d_totals + 2);
   int rc = check_launch();
   if (rc) return rc;
   rc = scan_launch<uint64_t>(L.kbytes, S + 1, L.koff, L.scan_ws, L.scan_bytes, st);
@@ -527,7 +641,13 @@ extern "C" int em_fcin_materialize(const uint32_t* payload, uint64_t payload_wor
   if (S)
     hipLaunchKernelGGL(k_fi_heads, dim3(fi_blocks(L.nb)), dim3(kFiBlock), 0, st, bits, L, keys, key_cap, val_cap,
                        d_totals + 2);
-  hipLaunchKernelGGL(k_fi_records, dim3(fi_blocks(static_cast<uint64_t>(S) + 1)), dim3(kFiBlock), 0, st, bits, L,
-                     keys, key_cap, key_off, vals, val_cap, val_off, tomb, d_totals + 2);
+  // records per workgroup: the mean record (from the arena capacities, at
+  // least its size) filling two thirds of the window
+  const uint64_t mean = S ? (key_cap + val_cap + S - 1) / S : 1;
+  uint32_t rpb = static_cast<uint32_t>(
+      std::max<uint64_t>(kFiRecs, std::min<uint64_t>(kFiBlock, (2 * kFiWin / 3) / std::max<uint64_t>(mean, 1))));
+  rpb -= rpb % kFiRecs;  // whole blocks
+  hipLaunchKernelGGL(k_fi_records, dim3(S ? (S + rpb - 1) / rpb : 1), dim3(kFiBlock), 0, st, bits, L, rpb, keys,
+                     key_cap, key_off, vals, val_cap, val_off, tomb, d_totals + 2);
   return check_launch();
 }
