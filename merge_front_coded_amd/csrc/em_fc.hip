@@ -104,7 +104,9 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
                                             const uint32_t* vbase, uint64_t T, uint32_t* payload,
                                             uint32_t ticket) {
   const uint32_t tid = threadIdx.x;
-  const uint64_t wb = (sh.bit_lo >> 5) << 5;           // first bit of window word 0
+  // first bit of window word 0: a multiple of 128 bits, so that four-word
+  // groups of the payload are four-word groups of the window
+  const uint64_t wb = (sh.bit_lo >> 7) << 7;
   const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
   const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
   // bits past the last owned word are not needed
@@ -144,8 +146,11 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
     auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
     const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
     for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
-    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock)
-      *reinterpret_cast<uint4*>(payload + w) = uint4{win(w), win(w + 1), win(w + 2), win(w + 3)};
+    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock) {
+      const uint4 v = reinterpret_cast<const uint4*>(sh.out)[static_cast<uint32_t>(w - wbase) / 4];
+      *reinterpret_cast<uint4*>(payload + w) = uint4{__builtin_bswap32(v.x), __builtin_bswap32(v.y),
+                                                     __builtin_bswap32(v.z), __builtin_bswap32(v.w)};
+    }
     for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
     __syncthreads();
   }
@@ -256,6 +261,18 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     klen = x.len;
     isB = s.isB;
     sh.kbits[j] = 8u * x.len;
+    if (j == 0) sh.bit_lo = rec_off;
+    if (j == nown - 1) sh.bit_hi = rec_end;
+    if (j == cnt - 1) sh.bit_ext = rec_end;
+    if (kTiled && off_out && j < nown) {
+      off_out[r] = rec_off;
+      if (r + 1 == S) off_out[S] = T;
+    }
+  }
+  __syncthreads();
+  // the source spans: the owned records', and those of the records after them
+  // that start inside the last owned word (usually one)
+  if (active && (j < nown || rec_off < 32ull * ((sh.bit_hi + 31) >> 5))) {
     const uint32_t q = isB ? 1u : 0u;
     const uint32_t klo = kpos + (l >> 3);
     if (klo < kpos + klen) {
@@ -265,13 +282,6 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     if (vlen) {
       atomicMin(&sh.span_lo[2 + q], vpos);
       atomicMax(&sh.span_hi[2 + q], vpos + vlen);
-    }
-    if (j == 0) sh.bit_lo = rec_off;
-    if (j == nown - 1) sh.bit_hi = rec_end;
-    if (j == cnt - 1) sh.bit_ext = rec_end;
-    if (kTiled && off_out && j < nown) {
-      off_out[r] = rec_off;
-      if (r + 1 == S) off_out[S] = T;
     }
   }
   __syncthreads();

@@ -82,3 +82,15 @@ def test_byte_profile_edges():
                f"{n} records")
     empty = gen.side_from_records([])
     _check(empty, empty, "empty")
+
+
+def test_byte_profile_window_fallback():
+    """Workgroups whose bytes overflow the LDS window write to the payload
+    directly, beside workgroups that use it."""
+    rng = np.random.default_rng(12)
+    keys = [b"w%05d/" % i + b"k" * int(rng.integers(0, 30)) for i in range(2000)]
+    vals = [rng.bytes(30000) if i % 97 == 0 else (None if i % 7 == 0 else rng.bytes(int(rng.integers(0, 40))))
+            for i in range(2000)]
+    A = gen.side_from_records(list(zip(keys[::2], vals[::2])))
+    B = gen.side_from_records(list(zip(keys[1::2], vals[1::2])))
+    _check(A, B, "window fallback")

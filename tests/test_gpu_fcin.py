@@ -92,6 +92,40 @@ def test_decode_edges():
     _round_trip(empty, empty, "empty")
 
 
+def test_decode_window_fallback():
+    """Workgroups whose key and value bytes overflow the LDS window write to
+    the arenas directly, beside workgroups that use it; oversized arena
+    capacities change the records per workgroup, not the arenas."""
+    import merge_front_coded_amd as em
+    rng = np.random.default_rng(11)
+    keys = [b"w%05d/" % i + b"k" * int(rng.integers(0, 30)) for i in range(2000)]
+    vals = [rng.bytes(30000) if i % 97 == 0 else (None if i % 7 == 0 else rng.bytes(int(rng.integers(0, 40))))
+            for i in range(2000)]
+    A = gen.side_from_records(list(zip(keys[::2], vals[::2])))
+    B = gen.side_from_records(list(zip(keys[1::2], vals[1::2])))
+    d, want = _round_trip(A, B, "window fallback", nav=True)
+    pl = run_gpu(A, B, items=256)
+    S, T = pl.S, pl.T
+    for scale in (1, 40):
+        ws = torch.empty(max(em.em_fcin_workspace_bytes(S), 256), dtype=torch.uint8, device="cuda")
+        tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+        em.em_fcin_parse(pl.payload, T, S, tot, ws, off=pl.off)
+        kb, vb, err = (int(x) for x in tot.cpu())
+        assert err == 0 and (kb, vb) == (want.keys.size, want.vals.size)
+        keys_d = torch.zeros(kb * scale + 64, dtype=torch.uint8, device="cuda")
+        vals_d = torch.zeros(vb * scale + 64, dtype=torch.uint8, device="cuda")
+        ko = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+        vo = torch.empty(S + 1, dtype=torch.int32, device="cuda")
+        tb = torch.empty(S, dtype=torch.uint8, device="cuda")
+        em.em_fcin_materialize(pl.payload, S, keys_d, ko, vals_d, vo, tb, tot, ws)
+        torch.cuda.synchronize()
+        assert int(tot[2].item()) == 0
+        got = gen.HostSide(keys=keys_d[:kb].cpu().numpy(), key_off=ko.cpu().numpy().view(np.uint32),
+                           vals=vals_d[:vb].cpu().numpy(), val_off=vo.cpu().numpy().view(np.uint32),
+                           tomb=tb.cpu().numpy())
+        _same_side(got, want, f"arena capacity x{scale}")
+
+
 def test_decoded_side_merges_again():
     """A side decoded from a payload enters the merge like any other."""
     import merge_front_coded_amd as em
