@@ -49,8 +49,8 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
 # x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
 # only while the kernel sources hash to the fingerprint it was taken with.
 TRAFFIC = {
-    "em_emit_merged": (2538675305, ("em_fc.hip", "em_tile.h", "em_internal.h"), "b392889c5a8e3b17"),
-    "em_merge_lengths": (1446445861, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "08043bf52ec42983"),
+    "em_emit_merged": (2429782013, ("em_fc.hip", "em_tile.h", "em_internal.h"), "b19d313b34272479"),
+    "em_merge_lengths": (1439553853, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "08043bf52ec42983"),
 }
 
 
