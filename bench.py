@@ -90,7 +90,9 @@ def parse():
     ap.add_argument("--fcin", action="store_true",
                     help="also time decoding the step's payload back into arenas (em_fcin_parse + _materialize)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+                    help="run the plain 1 GiB device copy (the default; kept for the counter-scaling commands)")
+    ap.add_argument("--no-copy", action="store_true",
+                    help="skip the plain 1 GiB device copy that measures the achievable copy rate")
     return ap.parse_args()
 
 
@@ -219,25 +221,47 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
     for c in calls:
         setattr(em.pipeline.em, c, timed(c))
+    step_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     try:
         start.record(stream)
-        for _ in range(args.steps):
+        for k in range(args.steps):
             pl.run(read_counts=not fused)  # the fused path needs no host read inside a step
+            step_end[k].record(stream)
         end.record(stream)
         torch.cuda.synchronize()
     finally:
         for c in calls:
             setattr(em.pipeline.em, c, orig[c])
     wall = time.perf_counter() - t0
+    steps_ms = [(start if k == 0 else step_end[k - 1]).elapsed_time(step_end[k]) for k in range(args.steps)]
+    complete_ms = None
     if fused:
         pl.read_counts()
+        # the same steps with the host reading S and T after each (the
+        # "complete" time; the six-call path's steps already include them)
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(args.steps):
+            pl.run(read_counts=True)
+        e0.record(stream)
+        torch.cuda.synchronize()
+        complete_ms = s0.elapsed_time(e0) / args.steps
         # the per-record arrays, for the algorithmic-byte count only (not timed)
         pl2 = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
         pl2.run()
         torch.cuda.synchronize()
         assert (pl2.S, pl2.T) == (pl.S, pl.T)
         pl.final_host, pl.lcp_host = pl2.host("final", pl.S), pl2.host("lcp", pl.S)
+        ord_A = pl2.host("ord_A", Ah.n)
         del pl2
+    else:
+        ord_A = pl.host("ord_A", Ah.n)
+    # value bytes of the replaced A records: B_io less these is the minimum
+    # any path must move
+    a_vlen = np.diff(Ah.val_off.astype(np.int64))
+    if Ah.tomb is not None:
+        a_vlen = np.where(Ah.tomb != 0, 0, a_vlen)
+    replaced_val_bytes = int(a_vlen[ord_A == 0xFFFFFFFF].sum())
     dev_ms = start.elapsed_time(end)
     ms_per_step = dev_ms / args.steps
     per_call_ms = {c: sum(s.elapsed_time(e) for s, e in ev[c]) / len(ev[c]) for c in calls}
@@ -389,7 +413,11 @@ def main():
                                        "GBps": fcin_bytes / ((parse_ms + mat_ms) * 1e-3) / 1e9}
         if pn is not pl:
             del pn
-    if args.copy_calibration:
+    result["step_ms"] = {"median": float(np.median(steps_ms)), "min": min(steps_ms), "max": max(steps_ms)}
+    result["ms_per_step_with_host_reads"] = complete_ms if fused else ms_per_step
+    result["B_min_bytes"] = b_io - replaced_val_bytes
+    result["pipeline_GBps_B_min"] = (b_io - replaced_val_bytes) / (ms_per_step * 1e-3) / 1e9
+    if not args.no_copy:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -124,14 +124,32 @@ struct FiWin {
   }
 };
 
-// Words [w0, w1) of the payload (clamped to the stored words and to cap)
-// into lds by the whole workgroup, coalesced; returns how many it holds.
-// The caller synchronises before reading them.
-__device__ __forceinline__ uint32_t fi_stage(uint32_t* __restrict__ lds, uint32_t cap, const FiBits& g, uint64_t w0,
-                                             uint64_t w1) {
+// Words [w0, w1) of the payload, from w0 rounded down to a multiple of four,
+// clamped to the stored words and to kWords, into lds (16-byte aligned) by the
+// workgroup of kThreads: 16-byte loads, all issued before the stores.
+// Returns how many words lds holds (w0 is updated); the caller synchronises
+// before reading them.
+template <int kThreads, uint32_t kWords>
+__device__ __forceinline__ uint32_t fi_stage(uint32_t* __restrict__ lds, const FiBits& g, uint64_t& w0, uint64_t w1) {
+  static_assert(kWords % (4 * kThreads) == 0, "whole rounds of 16-byte loads");
+  constexpr int kIters = kWords / (4 * kThreads);
+  w0 &= ~static_cast<uint64_t>(3);
   w1 = min(w1, g.nwords);
-  const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min<uint64_t>(w1 - w0, cap)) : 0u;
-  for (uint32_t t = threadIdx.x; t < n; t += blockDim.x) lds[t] = g.w[w0 + t];
+  const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min<uint64_t>(w1 - w0, kWords)) : 0u;
+  const uint32_t n4 = n / 4;
+  const uint4* src = reinterpret_cast<const uint4*>(g.w + w0);
+  uint4 v[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const uint32_t x = threadIdx.x + it * kThreads;
+    if (x < n4) v[it] = src[x];
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const uint32_t x = threadIdx.x + it * kThreads;
+    if (x < n4) reinterpret_cast<uint4*>(lds)[x] = v[it];
+  }
+  for (uint32_t t = 4 * n4 + threadIdx.x; t < n; t += kThreads) lds[t] = g.w[w0 + t];
   return n;
 }
 
@@ -230,13 +248,13 @@ __global__ __launch_bounds__(kFiParseWave) void k_fi_parse(FiBits bits, uint64_t
                                                            uint32_t* __restrict__ vbytes, uint64_t* __restrict__ lit,
                                                            uint64_t* __restrict__ vbit, uint8_t* __restrict__ tflag,
                                                            uint64_t* __restrict__ err) {
-  __shared__ uint32_t span[kFiParseWords];
+  __shared__ __align__(16) uint32_t span[kFiParseWords];
   const uint32_t k0 = blockIdx.x * G;
   const uint32_t k1 = min(k0 + G, nb);
   const uint64_t p0 = starts[k0], p1 = k1 < nb ? starts[k1] : T;
   // (+3 words: a 64-bit window at the last value header reads three)
-  const uint64_t w0 = p0 >> 5;
-  const uint32_t n = p1 >= p0 ? fi_stage(span, kFiParseWords, bits, w0, (p1 >> 5) + 3) : 0u;
+  uint64_t w0 = p0 >> 5;
+  const uint32_t n = p1 >= p0 ? fi_stage<kFiParseWave, kFiParseWords>(span, bits, w0, (p1 >> 5) + 3) : 0u;
   __syncthreads();
   const FiWin win{span, w0, n, bits};
   const uint32_t k = k0 + threadIdx.x;
