@@ -41,7 +41,8 @@ METRIC = "merged records/s and pipeline GB/s (% of HBM peak) at 8M+8M string key
 KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em_fc_lengths": "k_fc_lengths",
              "em_scan": "k_scan", "em_emit": "k_emit",
              "em_collision_rank_mode": "k_mark, rank build, scatter or compact + merge",
-             "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit"}
+             "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit",
+             "em_merge_fc_onepass": "k_merge_len<4, true> + k_edge_fix"}
 
 
 # Scaled HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes on
@@ -72,7 +73,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
-    ap.add_argument("--path", choices=("fused", "merge", "collision"), default="fused")
+    ap.add_argument("--path", choices=("fused", "onepass", "merge", "collision"), default="fused")
     ap.add_argument("--items", type=int, default=0,
                     help="outputs per merge partition (0: chosen from the mean key length)")
     ap.add_argument("--collision-mode", choices=("512", "2048", "512-tiled", "512-compact"),
@@ -141,6 +142,9 @@ def algorithmic_bytes(Ah, Bh, pl, path):
         # emission: refs, LCPs, offsets (16 B), key_off and val_off pairs,
         # tombstone, key suffixes, values; writes the payload
         "em_emit_merged": S * (16 + 8 + 8 + 1) + suffix_bytes + value_bytes + payload,
+        # the single pass: every key byte, key and value offsets, tombstones,
+        # the survivors' value bytes; writes the payload
+        "em_merge_fc_onepass": keys + offs + vmeta + value_bytes + payload,
     }
     return out
 
@@ -183,11 +187,14 @@ def main():
     print(f"# generated {w.name}: {Ah.n}+{Bh.n} records in {t_gen:.1f}s", file=sys.stderr, flush=True)
     A = em.DeviceSide.from_host(Ah)
     B = em.DeviceSide.from_host(Bh)
-    fused = args.path == "fused"
+    fused = args.path in ("fused", "onepass")
     extra = {"coarse_parts": args.coarse_parts} if (fused and args.coarse_parts) else {}
     if args.path == "collision":
         extra["collision_mode"] = args.collision_mode
-    pl = em.Pipeline(A, B, items_per_part=args.items or None, path=args.path, keep_all=not fused, **extra)
+    if args.path == "onepass":
+        extra["one_pass"] = True
+    pl = em.Pipeline(A, B, items_per_part=args.items or None, path="fused" if fused else args.path,
+                     keep_all=not fused, **extra)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -200,7 +207,8 @@ def main():
     stream = torch.cuda.current_stream()
     calls = {"merge": ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"],
              "collision": ["em_collision_rank_mode", "em_fc_lengths", "em_scan", "em_emit"],
-             "fused": ["em_partition", "em_merge_lengths", "em_emit_merged"]}[args.path]
+             "fused": ["em_partition", "em_merge_lengths", "em_emit_merged"],
+             "onepass": ["em_partition", "em_merge_fc_onepass"]}[args.path]
     ev = {c: [] for c in calls}
     orig = {c: getattr(em.pipeline.em, c) for c in calls}
 

@@ -255,6 +255,23 @@ int em_merge_fc(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_s
                 uint64_t *off, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The whole path in one pass (Everett, "GPU construction experiment": the
+ * same steps; each output word is written once): em_merge_fc's arguments
+ * and results, but each partition's workgroup also takes its bit base from a
+ * second decoupled look-back over the partitions' bit totals and writes its
+ * records' payload words itself, in slices of an LDS window, reading the key
+ * suffixes and values in place.  The word a partition shares with the next
+ * one goes to the workspace and a small second kernel combines the two
+ * parts.  final_refs, ord_A, ord_B, len_bits, lcp_bits and off are optional
+ * (nullable); the workspace is em_merge_fc_workspace_bytes.
+ */
+int em_merge_fc_onepass(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_splits,
+                        uint32_t coarse_items, uint32_t items_per_part, uint32_t *payload,
+                        uint64_t payload_words, uint32_t *d_S, uint64_t *d_T, uint32_t *final_refs,
+                        uint32_t *ord_A, uint32_t *ord_B, uint32_t *len_bits, uint32_t *lcp_bits,
+                        uint64_t *off, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Rank512 probe (Everett, "Collision bitmap and rank experiment",
  * "Validation and measurement plan": compare GPU rank queries against scalar
  * prefix counts).  Builds the same temporary rank512 directory that

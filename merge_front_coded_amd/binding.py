@@ -64,6 +64,7 @@ def load_library(path: str = LIB_PATH):
         "em_rank512_probe": (i32, [P, u32, P, u32, P, P, sz, P]),
         "em_merge_fc_workspace_bytes": (sz, [u32, u32, u32]),
         "em_merge_fc": (i32, [S, S, P, u32, u32, P, u64, P, P, P, P, P, P, P, P, P, sz, P]),
+        "em_merge_fc_onepass": (i32, [S, S, P, u32, u32, P, u64, P, P, P, P, P, P, P, P, P, sz, P]),
         "em_merge_lengths": (i32, [S, S, P, u32, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_emit_merged": (i32, [S, S, u32, P, u64, P, P, P, P, P, P, sz, P]),
         "em_rank512_workspace_bytes": (sz, [u32]),
@@ -249,6 +250,16 @@ def em_merge_fc(A, B, coarse_splits, coarse_items, items_per_part, payload, d_S,
                              _p(d_T), _p(final_refs), _p(ord_A), _p(ord_B), _p(len_bits),
                              _p(lcp_bits), _p(off), _p(ws), ws.numel(), _stream(stream)),
            "em_merge_fc")
+
+
+def em_merge_fc_onepass(A, B, coarse_splits, coarse_items, items_per_part, payload, d_S, d_T, ws,
+                        final_refs=None, ord_A=None, ord_B=None, len_bits=None, lcp_bits=None, off=None,
+                        stream=None):
+    _check(lib().em_merge_fc_onepass(ctypes.byref(A.struct), ctypes.byref(B.struct), _p(coarse_splits),
+                                     coarse_items, items_per_part, _p(payload), payload.numel(), _p(d_S),
+                                     _p(d_T), _p(final_refs), _p(ord_A), _p(ord_B), _p(len_bits),
+                                     _p(lcp_bits), _p(off), _p(ws), ws.numel(), _stream(stream)),
+           "em_merge_fc_onepass")
 
 
 def em_merge_lengths(A, B, coarse_splits, coarse_items, items_per_part, d_S, d_T, ws, final_refs=None,

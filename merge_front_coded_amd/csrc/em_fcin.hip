@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kFiParseWave) void k_fi_parse(FiBits bits, uint64_t
   uint32_t kprev = 0;
   for (uint32_t i = i0; i < i1 && !e; ++i) {
     uint64_t w64 = fi_peek64(win, pos);
-    uint32_t n1, n2;
+    uint32_t n1, n2 = 0;
     const uint32_t c = fi_eg0_win(w64, n1);
     uint32_t s = 0;
     if (n1) {

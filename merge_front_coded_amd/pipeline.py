@@ -7,7 +7,9 @@ Paths:
              "512-compact") instead of partition + merge_keep
   fused      partition -> merge_lengths (merge, keep, LCPs, lengths, bit
              offsets) -> emit_merged (the emitter); S and T stay on the
-             device.  one_call=True runs the same work as em_merge_fc.
+             device.  one_call=True runs the same work as em_merge_fc;
+             one_pass=True runs em_merge_fc_onepass (each partition emits
+             its own words).
 All buffers are allocated once up front (sized from em_workspace_bytes and
 em_payload_bound_bits) and reused by every run.
 """
@@ -42,7 +44,7 @@ class Pipeline:
     def __init__(self, A: em.DeviceSide, B: em.DeviceSide, items_per_part: int | None = None,
                  path: str = "merge", keep_ordinals: bool = True, keep_lcp: bool = True,
                  keep_all: bool = True, coarse_parts: int = _FUSE_COARSE_PARTS, one_call: bool = False,
-                 collision_mode: str = "512-tiled", device="cuda"):
+                 collision_mode: str = "512-tiled", one_pass: bool = False, device="cuda"):
         if path not in ("merge", "collision", "fused"):
             raise ValueError("path is 'merge', 'collision' or 'fused'")
         self.A, self.B = A, B
@@ -58,6 +60,7 @@ class Pipeline:
         self.collision_mode = em.COLLISION_MODES[collision_mode]
         self.keep_all = keep_all
         self.one_call = one_call
+        self.one_pass = one_pass
         N = A.n + B.n
         self.N = N
         P = (N + (self.coarse or self.items) - 1) // (self.coarse or self.items)
@@ -95,7 +98,10 @@ class Pipeline:
             outs = dict(final_refs=self.final if k else None, ord_A=self.ord_A if k else None,
                         ord_B=self.ord_B if k else None, len_bits=self.len_bits if k else None,
                         lcp_bits=self.lcp if k else None)
-            if self.one_call:
+            if self.one_pass:
+                em.em_merge_fc_onepass(A, B, self.splits, self.coarse, self.items, self.payload, self.d_S,
+                                       self.d_T, self.ws, off=self.off if k else None, stream=stream, **outs)
+            elif self.one_call:
                 em.em_merge_fc(A, B, self.splits, self.coarse, self.items, self.payload, self.d_S, self.d_T,
                                self.ws, off=self.off if k else None, stream=stream, **outs)
             else:

@@ -107,7 +107,7 @@ def test_full_size_workload_matches_oracle(wid):
     A, B = gen.make(wid)
     assert _sha(A.keys, A.key_off, A.vals, A.val_off, A.tomb, B.keys, B.key_off, B.vals, B.val_off,
                 B.tomb) == ref["input"], "generator output drifted from the digested inputs"
-    runs = [("fused", {}), ("merge", {})] + [("collision", {"collision_mode": m})
+    runs = [("fused", {}), ("fused", {"one_pass": True}), ("merge", {})] + [("collision", {"collision_mode": m})
                                              for m in ("512-tiled", "512", "2048", "512-compact")]
     for path, kw in runs:
         print(f"  path {path} {kw}", flush=True)
