@@ -193,24 +193,26 @@ __device__ __forceinline__ void bp_zero(uint8_t* __restrict__ dst, uint32_t n) {
   for (uint32_t t = h + 4 * m; t < n; ++t) dst[t] = 0;
 }
 
-// Record i's bytes at dst[at ..): with dst a window in LDS or the payload
-// itself (each call site passes one of them, so its stores have one address
-// space).
+// Record i's bytes at dst[at ..), its key suffix from ksrc and its value from
+// vsrc: dst a window in LDS or the payload itself, the sources staged in LDS
+// or in place (each call site passes one combination, so that its loads and
+// stores have one address space).
 __device__ __forceinline__ void bp_write_record(uint8_t* __restrict__ dst, uint64_t at, const BpRec& r, uint32_t W,
-                                                const em_side_t& A, const em_side_t& B) {
+                                                const uint8_t* __restrict__ ksrc,
+                                                const uint8_t* __restrict__ vsrc) {
   at = bp_put_leb(dst, at, r.c);
   at = bp_put_leb(dst, at, r.sfx);
-  bp_copy(dst + at, (r.isB ? B.keys : A.keys) + r.kpos, r.sfx);
+  bp_copy(dst + at, ksrc, r.sfx);
   at += r.sfx;
   dst[at++] = r.tomb ? 0 : 1;
   if (W) {
     if (r.tomb)
       bp_zero(dst + at, W - 1);
     else
-      bp_copy(dst + at, (r.isB ? B.vals : A.vals) + r.vpos, W - 1);
+      bp_copy(dst + at, vsrc, W - 1);
   } else if (!r.tomb) {
     at = bp_put_leb(dst, at, r.vlen);
-    bp_copy(dst + at, (r.isB ? B.vals : A.vals) + r.vpos, r.vlen);
+    bp_copy(dst + at, vsrc, r.vlen);
   }
 }
 
@@ -219,8 +221,20 @@ __device__ __forceinline__ void bp_write_record(uint8_t* __restrict__ dst, uint6
 // window starting at the 16-byte boundary below off[r0]), each thread writes
 // its record there and the workgroup copies the window out with 16-byte
 // stores, single bytes only in the two groups it shares with its neighbours;
-// otherwise each thread writes its record to the payload directly.
-constexpr uint32_t kBpWin = 24576;
+// otherwise each thread writes its record to the payload directly.  The
+// records' sources lie in four contiguous spans (A keys, B keys, A values, B
+// values: the survivors of one side are increasing), which a windowed
+// workgroup stages in LDS with 16-byte LDS-DMA loads when they fit, so that
+// its threads copy from LDS instead of reading scattered global addresses.
+constexpr uint32_t kBpWin = 12288;    // output bytes
+constexpr uint32_t kBpStage = 12288;  // staged source bytes
+
+struct BpShared {
+  uint4 win[kBpWin / 16];
+  uint4 stage[kBpStage / 16];
+  uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
+  uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
+};
 
 __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
                                                       const uint32_t* __restrict__ final_refs,
@@ -229,36 +243,112 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
                                                       const uint32_t* __restrict__ d_width,
                                                       uint8_t* __restrict__ payload, uint64_t cap,
                                                       uint32_t* __restrict__ overflow) {
-  __shared__ __align__(16) uint8_t win[kBpWin];
+  __shared__ BpShared sh;
+  const uint32_t tid = threadIdx.x;
   const uint32_t r0 = blockIdx.x * rpb;
   const uint32_t r1 = min(r0 + rpb, S);
   const uint64_t b0 = off[r0], b1 = off[r1];
   const uint64_t base = b0 & ~static_cast<uint64_t>(15);
   const bool staged = b0 <= b1 && b1 <= cap && b1 - base <= kBpWin;  // (uniform over the workgroup)
   const uint32_t W = d_width[0];
-  const uint32_t i = r0 + threadIdx.x;
-  if (threadIdx.x < rpb && i < r1) {
-    const BpRec r = bp_record(A, B, final_refs, lcp_bits, i);
-    const uint64_t at = off[i], end = off[i + 1];
+  if (tid < 4) {
+    sh.span_lo[tid] = 0xFFFFFFFFu;
+    sh.span_hi[tid] = 0;
+  }
+  __syncthreads();
+  const uint32_t i = r0 + tid;
+  bool ok = false;
+  BpRec r{};
+  uint64_t at = 0;
+  uint32_t vn = 0;  // value bytes copied from the source
+  if (tid < rpb && i < r1) {
+    r = bp_record(A, B, final_refs, lcp_bits, i);
+    at = off[i];
+    const uint64_t end = off[i + 1];
     // offsets or a width that do not belong to these records, or no room:
     // flag it and write nothing of the record (within the window, that
     // leaves its bytes unspecified)
     if (at > end || end > cap || end - at != leb_bytes(r.c) + leb_bytes(r.sfx) + r.sfx + bp_value_bytes(r, W) ||
         (W && !r.tomb && r.vlen != W - 1) || (staged && (at < b0 || end > b1))) {
       atomicOr(overflow, 1u);
-    } else if (staged) {
-      bp_write_record(win, at - base, r, W, A, B);
     } else {
-      bp_write_record(payload, at, r, W, A, B);
+      ok = true;
+      vn = r.tomb ? 0u : r.vlen;
+      if (staged) {
+        const uint32_t q = r.isB ? 1u : 0u;
+        if (r.sfx) {
+          atomicMin(&sh.span_lo[q], r.kpos);
+          atomicMax(&sh.span_hi[q], r.kpos + r.sfx);
+        }
+        if (vn) {
+          atomicMin(&sh.span_lo[2 + q], r.vpos);
+          atomicMax(&sh.span_hi[2 + q], r.vpos + vn);
+        }
+      }
     }
   }
-  if (!staged) return;
+  if (!staged) {  // (uniform)
+    if (ok)
+      bp_write_record(payload, at, r, W, (r.isB ? B.keys : A.keys) + r.kpos, (r.isB ? B.vals : A.vals) + r.vpos);
+    return;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t s_at = 0;
+    for (int q = 0; q < 4; ++q) {
+      sh.stage_at[q] = s_at;
+      if (sh.span_lo[q] < sh.span_hi[q]) {
+        // the copy reads up to 4 bytes past a span's last byte
+        const uint32_t lo = sh.span_lo[q] & ~15u, hi = (sh.span_hi[q] + 4u + 15u) & ~15u;
+        sh.span_lo[q] = lo;
+        sh.span_hi[q] = hi;
+        s_at += hi - lo;
+      } else {
+        sh.span_lo[q] = sh.span_hi[q] = 0;
+      }
+    }
+    sh.stage_at[4] = s_at;
+  }
+  __syncthreads();
+  const bool src_staged = sh.stage_at[4] <= kBpStage;  // (uniform)
+  if (src_staged && sh.stage_at[4] > 0) {
+    // global -> LDS without registers: each wave moves 64 consecutive
+    // 16-byte chunks, lane i's chunk landing 16 i bytes after the wave's base
+    const uint32_t total16 = sh.stage_at[4] / 16;
+    const uint32_t at1 = sh.stage_at[1], at2 = sh.stage_at[2], at3 = sh.stage_at[3];
+    const uint32_t lane = tid & (kWave - 1);
+    for (uint32_t c0 = (tid / kWave) * kWave; c0 < total16; c0 += kBpBlock) {
+      const uint32_t c = c0 + lane;
+      if (c < total16) {
+        const uint32_t byte = c * 16;
+        const uint32_t q = (byte >= at1) + (byte >= at2) + (byte >= at3);
+        const uint8_t* src = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
+        lds_dma16(src + sh.span_lo[q] + (byte - sh.stage_at[q]), sh.stage + c0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  uint8_t* win = reinterpret_cast<uint8_t*>(sh.win);
+  if (ok) {
+    if (src_staged) {
+      const uint8_t* st = reinterpret_cast<const uint8_t*>(sh.stage);
+      const uint32_t qk = r.isB ? 1u : 0u, qv = 2u + qk;
+      // (an empty field's source is never read)
+      const uint8_t* ks = st + (r.sfx ? sh.stage_at[qk] + (r.kpos - sh.span_lo[qk]) : 0u);
+      const uint8_t* vs = st + (vn ? sh.stage_at[qv] + (r.vpos - sh.span_lo[qv]) : 0u);
+      bp_write_record(win, at - base, r, W, ks, vs);
+    } else {
+      bp_write_record(win, at - base, r, W, (r.isB ? B.keys : A.keys) + r.kpos,
+                      (r.isB ? B.vals : A.vals) + r.vpos);
+    }
+  }
   __syncthreads();
   const uint32_t groups = static_cast<uint32_t>((b1 - base + 15) >> 4);
-  for (uint32_t g = threadIdx.x; g < groups; g += kBpBlock) {
+  for (uint32_t g = tid; g < groups; g += kBpBlock) {
     const uint64_t a = base + 16ull * g;
     if (a >= b0 && a + 16 <= b1) {
-      *reinterpret_cast<uint4*>(payload + a) = *reinterpret_cast<const uint4*>(win + 16 * g);
+      *reinterpret_cast<uint4*>(payload + a) = sh.win[g];
     } else {
       for (uint32_t t = 0; t < 16; ++t)
         if (a + t >= b0 && a + t < b1) payload[a + t] = win[16 * g + t];
