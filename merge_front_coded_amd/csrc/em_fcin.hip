@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_starts_ef(const em_ef_info_t* _
   starts[k] = e + static_cast<uint64_t>(k) * kFiRecs * w;
 }
 
-// ---- block parse: one thread per block of at most 15 records ----
+// ---- block parse: one lane per block of at most 15 records ----
 
 // 64 bits of the payload from bit x on (MSB first, zero past the stored words)
 __device__ __forceinline__ uint64_t fi_peek64(const FiWin& b, uint64_t x) {
