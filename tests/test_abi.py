@@ -144,3 +144,21 @@ def test_byte_profile_argument_errors(lib):
     assert lib.em_bp_navigation(buf, 5, 50, None, buf, 8, buf, 8, buf, 8, buf, 8, buf, ws, 1 << 20, None) == -1
     assert lib.em_bp_navigation(buf, 1 << 24, 50, buf, buf, 8, buf, 8, buf, 8, buf, 8, buf, ws, 1 << 20,
                                 None) == -2
+
+
+def test_onepass_argument_errors(lib):
+    A, B = _side(), _side()
+    buf = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x100000)
+    # partition sizes, coarse splits that are not a multiple, a misaligned payload, no splits
+    for items, coarse in ((0, 256), (2049, 4098), (64, 100)):
+        assert lib.em_merge_fc_onepass(ctypes.byref(A), ctypes.byref(B), buf, coarse, items, buf, 1 << 20, buf,
+                                       buf, None, None, None, None, None, None, ws, 1 << 20, None) == -1
+    assert lib.em_merge_fc_onepass(ctypes.byref(A), ctypes.byref(B), buf, 64, 64, ctypes.c_void_p(0x100008),
+                                   1 << 20, buf, buf, None, None, None, None, None, None, ws, 1 << 20, None) == -1
+    assert lib.em_merge_fc_onepass(ctypes.byref(A), ctypes.byref(B), None, 64, 64, buf, 1 << 20, buf, buf, None,
+                                   None, None, None, None, None, ws, 1 << 20, None) == -1
+    # workspace too small
+    A5 = _side(n=5, key_bytes=5, val_bytes=0)
+    assert lib.em_merge_fc_onepass(ctypes.byref(A5), ctypes.byref(B), buf, 64, 64, buf, 1 << 20, buf, buf, None,
+                                   None, None, None, None, None, ws, 0, None) == -3
