@@ -102,6 +102,21 @@ struct FiBits {
     const uint32_t hi = word(i), lo = word(i + 1);
     return s ? __builtin_amdgcn_alignbit(hi, lo, 32u - s) : hi;
   }
+  // words i .. i+3 with one 16-byte load (multi-dword loads need only dword
+  // alignment), word by word at the end of the payload
+  __device__ __forceinline__ void word4(uint64_t i, uint32_t (&v)[4]) const {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(4)));
+    if (i + 3 < nwords) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(w + i);
+      v[0] = __builtin_bswap32(q.x);
+      v[1] = __builtin_bswap32(q.y);
+      v[2] = __builtin_bswap32(q.z);
+      v[3] = __builtin_bswap32(q.w);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = word(i + t);
+    }
+  }
 };
 
 // The payload as a bit stream read through an LDS copy of words
@@ -372,9 +387,9 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_pse(FiLayout L) {
 // nbytes bytes from payload bit x on.  Output dword m is bits
 // [x + 32m, x + 32m + 32), one funnel shift of payload words i0 + m and
 // i0 + m + 1 (i0 = x / 32), so each payload word is read once; sixteen bytes
-// at a time with the four loads of a group issued before its stores (a byte
-// store may alias any load, so a load after it would wait for it), whole
-// words where the destination is aligned.
+// at a time, the four words of a group in one 16-byte load issued before the
+// group's stores (a byte store may alias any load, so a load after it would
+// wait for it), whole words where the destination is aligned.
 template <class Bits>
 __device__ __forceinline__ void fi_copy_bytes(const Bits& bits, uint64_t x, uint8_t* __restrict__ dst,
                                               uint32_t nbytes) {
@@ -385,8 +400,7 @@ __device__ __forceinline__ void fi_copy_bytes(const Bits& bits, uint64_t x, uint
   uint32_t m = 0;
   for (; m + 16 <= nbytes; m += 16) {
     uint32_t nx[4], v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) nx[t] = bits.word(i0 + m / 4 + 1 + t);
+    bits.word4(i0 + m / 4 + 1, nx);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t a = t ? nx[t - 1] : prev;
