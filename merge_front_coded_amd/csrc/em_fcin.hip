@@ -96,10 +96,21 @@ struct FiBits {
   __device__ __forceinline__ uint32_t word(uint64_t i) const {
     return i < nwords ? __builtin_bswap32(w[i]) : 0u;
   }
+  // (the two words in one 8-byte load: multi-dword loads need only dword
+  // alignment)
   __device__ __forceinline__ uint32_t at32(uint64_t x) const {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(4)));
     const uint64_t i = x >> 5;
     const uint32_t s = static_cast<uint32_t>(x & 31u);
-    const uint32_t hi = word(i), lo = word(i + 1);
+    uint32_t hi, lo;
+    if (i + 1 < nwords) {
+      const u32x2 q = *reinterpret_cast<const u32x2*>(w + i);
+      hi = __builtin_bswap32(q.x);
+      lo = __builtin_bswap32(q.y);
+    } else {
+      hi = word(i);
+      lo = word(i + 1);
+    }
     return s ? __builtin_amdgcn_alignbit(hi, lo, 32u - s) : hi;
   }
   // words i .. i+3 with one 16-byte load (multi-dword loads need only dword
