@@ -357,10 +357,33 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_leaves(const uint32_t* __restri
   if (i < P2) tree[P2 + i] = i < S ? r[i] : kFiInf;
 }
 
-// nodes [first, 2 first) from their children
-__global__ __launch_bounds__(kFiBlock) void k_fi_level(uint32_t* __restrict__ tree, uint32_t first) {
-  const uint32_t v = first + blockIdx.x * kFiBlock + threadIdx.x;
-  if (v < 2 * first) tree[v] = min(tree[2 * v], tree[2 * v + 1]);
+// Levels first, first / 2, ... of the tree, from their children: a
+// workgroup takes cnt0 = min(256, first) consecutive nodes of level `first`
+// and the subtree above them in LDS, down to one node (1 + log2 cnt0 levels
+// per launch).
+__global__ __launch_bounds__(kFiBlock) void k_fi_levels(uint32_t* __restrict__ tree, uint32_t first,
+                                                        uint32_t cnt0) {
+  __shared__ uint32_t buf[kFiBlock];
+  const uint32_t t = threadIdx.x;
+  uint32_t cnt = cnt0, f = first;
+  uint32_t m = kFiInf;
+  if (t < cnt) {
+    const uint32_t v = f + blockIdx.x * cnt + t;
+    m = min(tree[2 * v], tree[2 * v + 1]);
+    tree[v] = m;
+    buf[t] = m;
+  }
+  while (cnt > 1) {
+    __syncthreads();
+    cnt >>= 1;
+    f >>= 1;
+    if (t < cnt) m = min(buf[2 * t], buf[2 * t + 1]);
+    __syncthreads();
+    if (t < cnt) {
+      buf[t] = m;
+      tree[f + blockIdx.x * cnt + t] = m;
+    }
+  }
 }
 
 // The literal owner of bit p of key i, p < r_i: j = max{t <= i : r_t <= p}.
@@ -663,8 +686,13 @@ extern "C" int em_fcin_parse(const uint32_t* payload, uint64_t payload_words, ui
   hipLaunchKernelGGL(k_fi_totals, dim3(1), dim3(1), 0, st, L, d_totals);
   // the minimum tree over the retained lengths
   hipLaunchKernelGGL(k_fi_leaves, dim3(fi_blocks(L.P2)), dim3(kFiBlock), 0, st, L.r, S, L.P2, L.tree);
-  for (uint32_t first = L.P2 / 2; first >= 1; first /= 2)
-    hipLaunchKernelGGL(k_fi_level, dim3(fi_blocks(first)), dim3(kFiBlock), 0, st, L.tree, first);
+  for (uint32_t first = L.P2 / 2; first >= 1;) {
+    const uint32_t cnt0 = first < static_cast<uint32_t>(kFiBlock) ? first : static_cast<uint32_t>(kFiBlock);
+    hipLaunchKernelGGL(k_fi_levels, dim3(first / cnt0), dim3(kFiBlock), 0, st, L.tree, first, cnt0);
+    uint32_t lev = 1;  // 1 + log2(cnt0) levels built
+    for (uint32_t c = cnt0; c > 1; c >>= 1) ++lev;
+    first >>= lev;
+  }
   hipLaunchKernelGGL(k_fi_pse, dim3(fi_blocks(S)), dim3(kFiBlock), 0, st, L);
   return check_launch();
 }

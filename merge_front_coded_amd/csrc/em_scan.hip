@@ -14,6 +14,10 @@ constexpr int kScanBlock = 256;
 constexpr int kScanIpt = 16;
 constexpr uint32_t kScanTile = kScanBlock * kScanIpt;
 
+// A tile moves between global memory and registers through LDS, so that
+// both its loads and its stores are 16 bytes a lane on consecutive addresses
+// (a thread's own sixteen consecutive values, loaded or stored directly, put
+// 64 scattered addresses on every memory instruction).
 template <class OutT>
 __global__ __launch_bounds__(kScanBlock) void k_scan(const uint32_t* __restrict__ in, uint32_t n,
                                                      OutT* __restrict__ out, uint32_t* __restrict__ ticket,
@@ -21,18 +25,28 @@ __global__ __launch_bounds__(kScanBlock) void k_scan(const uint32_t* __restrict_
   __shared__ uint64_t wsum[kScanBlock / kWave + 1];
   __shared__ uint32_t s_tile;
   __shared__ uint64_t s_base;
+  __shared__ uint4 stage[kScanTile * sizeof(OutT) / 16];
   const uint32_t tid = threadIdx.x;
   if (tid == 0) s_tile = atomicAdd(ticket, 1u);
   __syncthreads();
   const uint32_t tile = s_tile;
-  const uint32_t first = tile * kScanTile + tid * kScanIpt;
+  const uint32_t base = tile * kScanTile;
+  const uint32_t first = base + tid * kScanIpt;
+  // (uniform; the 16-byte paths need 16-byte aligned arrays)
+  const bool full = base + kScanTile <= n && (reinterpret_cast<uintptr_t>(in) & 15) == 0;
+  const bool full_out = full && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
 
   uint32_t v[kScanIpt];
-  if (first + kScanIpt <= n) {
-    const uint4* p = reinterpret_cast<const uint4*>(in + first);
+  if (full) {
+    // striped 16-byte loads into LDS, then each thread's own values
+    const uint4* p = reinterpret_cast<const uint4*>(in + base);
+#pragma unroll
+    for (int q = 0; q < kScanIpt / 4; ++q) stage[q * kScanBlock + tid] = p[q * kScanBlock + tid];
+    __syncthreads();
+    const uint4* mine = stage + tid * (kScanIpt / 4);
 #pragma unroll
     for (int q = 0; q < kScanIpt / 4; ++q) {
-      const uint4 t = p[q];
+      const uint4 t = mine[q];
       v[4 * q] = t.x;
       v[4 * q + 1] = t.y;
       v[4 * q + 2] = t.z;
@@ -54,12 +68,19 @@ __global__ __launch_bounds__(kScanBlock) void k_scan(const uint32_t* __restrict_
   }
   __syncthreads();
   uint64_t run = s_base + excl;
-  if (first + kScanIpt <= n) {
+  if (full_out) {
+    // each thread's values into LDS, then striped 16-byte stores
+    OutT* so = reinterpret_cast<OutT*>(stage) + tid * kScanIpt;
 #pragma unroll
     for (int q = 0; q < kScanIpt; ++q) {
-      out[first + q] = static_cast<OutT>(run);
+      so[q] = static_cast<OutT>(run);
       run += v[q];
     }
+    __syncthreads();
+    uint4* po = reinterpret_cast<uint4*>(out + base);
+    constexpr int kChunks = kScanTile * sizeof(OutT) / 16 / kScanBlock;
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q) po[q * kScanBlock + tid] = stage[q * kScanBlock + tid];
   } else {
 #pragma unroll
     for (int q = 0; q < kScanIpt; ++q) {
