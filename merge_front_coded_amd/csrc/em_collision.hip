@@ -216,40 +216,73 @@ __global__ __launch_bounds__(kColBlock) void k_scatter_A_search(em_side_t A, em_
   if (ord_A) ord_A[i] = o;
 }
 
-// A in tiles of kTileA consecutive records: one search in the saved lower
-// bounds, then a monotone cursor; the rank is queried once per tile and then
-// advanced by the tile's own collision bits.
+// A in tiles of 64 kTileA consecutive records, one tile per wave: one search
+// in the saved lower bounds and one rank query per tile, then runs of 64
+// records, a lane each, so that consecutive lanes write consecutive
+// ordinals and references.  For a run starting at i0 (a multiple of 64), the
+// B records whose lower bound lies in [i0, i0 + 64) are counted by position
+// in an LDS histogram (their lower bounds are the next entries of the sorted
+// array, read 64 at a time), whose prefix gives each lane #{j : lb_j <= i};
+// its collisions before i are the run's start rank plus a popcount of the
+// run's 64 bitmap bits below it.
 __global__ __launch_bounds__(kColBlock) void k_scatter_A(uint32_t nA, uint32_t nB, Rank512View rv,
                                                          const uint32_t* __restrict__ lb,
                                                          uint32_t* __restrict__ final_refs,
                                                          uint32_t* __restrict__ ord_A) {
-  const uint32_t t = blockIdx.x * kColBlock + threadIdx.x;
-  const uint32_t i0 = t * kTileA;
-  if (i0 >= nA) return;
-  const uint32_t i1 = i0 + kTileA < nA ? i0 + kTileA : nA;
-  // cur = #{j : lb_j <= i0}
+  __shared__ uint32_t hist[kColBlock / kWave][kWave];
+  const uint32_t lane = threadIdx.x & (kWave - 1);
+  uint32_t* h = hist[threadIdx.x / kWave];
+  const uint64_t start = (static_cast<uint64_t>(blockIdx.x) * kColBlock + threadIdx.x) / kWave * (kWave * kTileA);
+  if (start >= nA) return;  // (the whole wave; no workgroup barrier follows)
+  const uint32_t i_start = static_cast<uint32_t>(start);
+  // cb = #{j : lb_j < i_start}, then the rank at i_start (the same in every lane)
   uint32_t lo = 0, hi = nB;
   while (lo < hi) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
-    if (lb[mid] <= i0)
+    if (lb[mid] < i_start)
       lo = mid + 1;
     else
       hi = mid;
   }
-  uint32_t cur = lo;
-  uint32_t r = rv.rank(i0);
-  const uint32_t cbits = rv.bits[i0 >> 5];  // kTileA == 32: the tile is one bitmap word
-  for (uint32_t i = i0; i < i1; ++i) {
-    const uint32_t c = (cbits >> (i - i0)) & 1u;
-    if (c) {
-      if (ord_A) ord_A[i] = EM_NONE;
-    } else {
-      while (cur < nB && lb[cur] <= i) ++cur;
-      const uint32_t o = i + cur - r;
-      final_refs[o] = i;
-      if (ord_A) ord_A[i] = o;
+  uint32_t cb = lo;
+  uint32_t r0 = rv.rank(i_start);
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  for (uint32_t k = 0; k < kTileA; ++k) {
+    const uint32_t i0 = i_start + kWave * k;
+    if (i0 >= nA) break;
+    h[lane] = 0;
+    wave_sync();
+    uint32_t cend = cb;
+    while (true) {
+      const uint32_t j = cend + lane;
+      const uint32_t v = j < nB ? lb[j] : 0xFFFFFFFFu;
+      const bool in = v >= i0 && v < i0 + kWave;  // (v >= i0 holds for sorted inputs: the j < cb are below i0)
+      if (in) atomicAdd(&h[v - i0], 1u);
+      const uint32_t n_in = static_cast<uint32_t>(__builtin_popcountll(__ballot(in)));  // a prefix of the lanes
+      cend += n_in;
+      if (n_in < kWave) break;
     }
-    r += c;
+    wave_sync();
+    const uint32_t cur = cb + wave_inclusive_scan<uint32_t>(h[lane]);
+    const uint64_t word = rv.bits[i0 >> 5] | (static_cast<uint64_t>(rv.bits[(i0 >> 5) + 1]) << 32);
+    const uint32_t i = i0 + lane;
+    if (i < nA) {
+      if ((word >> lane) & 1u) {
+        if (ord_A) ord_A[i] = EM_NONE;
+      } else {
+        const uint32_t r = r0 + static_cast<uint32_t>(__builtin_popcountll(word & ((1ull << lane) - 1)));
+        const uint32_t o = i + cur - r;
+        final_refs[o] = i;
+        if (ord_A) ord_A[i] = o;
+      }
+    }
+    r0 += static_cast<uint32_t>(__builtin_popcountll(word));
+    cb = cend;
+    wave_sync();  // (the histogram is cleared for the next run after every lane read it)
   }
 }
 
@@ -473,8 +506,10 @@ static int collision_run(const em_side_t& A, const em_side_t& B, uint32_t mode, 
                        v512, lb, final_refs, ord_B);
   if (A.n) {
     if (mode == EM_COLLISION_512_TILED)
-      hipLaunchKernelGGL(k_scatter_A, dim3(blocks_for((A.n + kTileA - 1) / kTileA)), dim3(kColBlock), 0, st,
-                         A.n, B.n, v512, lb, final_refs, ord_A);
+      hipLaunchKernelGGL(k_scatter_A,
+                         dim3(blocks_for(static_cast<uint64_t>(kWave) *
+                                         ((A.n + kWave * kTileA - 1) / (kWave * kTileA)))),
+                         dim3(kColBlock), 0, st, A.n, B.n, v512, lb, final_refs, ord_A);
     else
       hipLaunchKernelGGL(k_scatter_A_search<Rank512View>, dim3(blocks_for(A.n)), dim3(kColBlock), 0, st, A,
                          B, v512, final_refs, ord_A);
