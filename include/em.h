@@ -90,7 +90,7 @@ size_t em_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t items_per_part);
  * 8 * (all key and value arena bytes) + (|A| + |B|) * 184, since each record
  * spends at most 61 bits on each of EG0(c), EG0(k-l) and EG0(value length)
  * plus one presence bit under the caps (Everett, "GPU construction
- * experiment": the host checks a conservative 64-bit bound before the scan).
+ * experiment": the output is sized on the host from an upper bound before any scan).
  * Writes *bound (host pointer).  EM_EINVAL on NULL arguments, EM_ERANGE when a
  * cap is exceeded.
  */
@@ -188,11 +188,11 @@ int em_scan(const uint32_t *len_bits, uint32_t S, uint64_t *off, void *ws, size_
             void *stream);
 
 /*
- * Word-owned payload emission (Everett, "GPU construction experiment": one
- * invocation owns each final 32-bit word, gathers its bits and writes it
- * once; payload bits are MSB first; no padding between records; unused final
- * bits are zero; the output key suffix is copied from the selected source
- * record's own key).  Record i occupies bits [off[i], off[i+1]):
+ * Word-owned payload emission (Everett, "GPU construction experiment": every
+ * 32-bit output word has a single writer, which collects all of its bits and
+ * stores it one time; bits run most significant first; records follow each
+ * other with no gaps; the bits after the last record are zero; the key suffix
+ * comes from the source record's own key).  Record i occupies bits [off[i], off[i+1]):
  * EG0(c_i) EG0(k_i - l_i) key bits [l_i, k_i) then 0 (tombstone) or
  * 1 EG0(value length) value bytes.  EG0(x) is floor(log2(x+1)) zero bits
  * followed by x+1 in binary.  Stream bit p is bit 7 - (p mod 8) of payload

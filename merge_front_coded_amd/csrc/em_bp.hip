@@ -3,8 +3,8 @@
 //
 // Everett, "Byte-profile GPU merge", "Pipeline": the GPU detects the common
 // encoded value width, sizes and scans the output records and emits their
-// byte FC payload (width seventeen: a one-byte presence tag and sixteen
-// payload bytes); the control rule is the bit profile's ("GPU construction
+// byte FC payload (width seventeen: a tag byte for presence followed by
+// sixteen bytes of value); the control rule is the bit profile's ("GPU construction
 // experiment", the c_i equation) counted in bytes.
 //
 // Record layout (read as; the page names the parts only): LEB128(c_i),

@@ -7,9 +7,10 @@
 //    bitmap word); the bitmap is cleared on the GPU first and bits past |A|
 //    stay zero.  With R(i) = sum_{t<i} C_t, B_j lands at j + lb_j - R(lb_j)
 //    and a surviving A_i at i + lower_bound(B, A_i) - R(i).
-//  * "Temporary rank layouts": rank512 gives each 512-bit block a 32-bit
-//    absolute prefix and seven 9-bit prefixes for its 64-bit pairs; a query
-//    reads the directory and one masked 64-bit word.  rank2048 gives each
+//  * "Temporary rank layouts": rank512 stores, per 512-bit block, the set
+//    bits before the block (32 bits) and, for each of its 64-bit words after
+//    the first, the set bits before that word inside the block (seven 9-bit
+//    fields); a query reads the directory and one masked 64-bit word.  rank2048 gives each
 //    2048-bit block one 8-byte entry: a 32-bit absolute prefix and the
 //    populations before its second, third and fourth 512-bit runs, packed
 //    (10, 11 and 11 bits); a query adds the popcounts of up to seven whole

@@ -3,14 +3,15 @@
 //
 // Everett, "GPU construction experiment":
 //  * the control equation: c_i = 1 + l_i when i mod 15 = 0, else
-//    k_{i-1} - l_i, with l_i the exact bit LCP with the preceding survivor
-//    (l_0 = 0) and k_i the key length in bits;
-//  * the record grammar: EG0(c_i), EG0(k_i - l_i), the remaining key bits and
-//    the value (0 for a tombstone; 1, EG0(byte length) and the bytes
-//    otherwise); E(x) = 2 floor(log2(x+1)) + 1; MSB-first bits; no padding;
-//  * emission: one invocation owns each final 32-bit word, gathers its bits
-//    and writes it once; unused final bits are zero; the key suffix is copied
-//    from the selected record's own key (every distinct key survives, so the
+//    k_{i-1} - l_i, where l_i counts the leading bits survivor i shares with
+//    survivor i - 1 (l_0 = 0) and k_i is the key length in bits;
+//  * the record grammar: EG0(c_i), EG0(k_i - l_i), key bits l_i .. k_i - 1,
+//    then the value (0 for a tombstone; 1, EG0(byte length) and the bytes
+//    otherwise); E(x) = 2 floor(log2(x+1)) + 1; most significant bit first;
+//    records back to back;
+//  * emission: every 32-bit output word has one writer, which collects its
+//    bits and stores it once; the tail after the last record is zero; the key
+//    suffix comes from the source record's own key (every distinct key survives, so the
 //    merged predecessor shares at least the source predecessor's prefix).
 #include "em_tile.h"
 

@@ -11,9 +11,9 @@
 //  * literal owners: with r_i record i's retained key length, bit p of key i
 //    belongs to the literal of j = max{t <= i : r_t <= p}; a minimum tree over
 //    the retained lengths answers that query in O(log n): from the record's
-//    leaf, climb until a left sibling has minimum <= p, then descend
-//    right-first through children with minimum <= p; unused leaves hold an
-//    infinite sentinel.  A byte resolved from its highest bit backward can
+//    leaf, go up until some left sibling's minimum is <= p, then go down
+//    into the right child whenever its minimum is <= p (else the left one);
+//    leaves past the last record hold an infinite value.  A byte resolved from its highest bit backward can
 //    combine several literal fragments;
 //  * full-key materialization as a consumer of the same descriptors (the
 //    paragraph that names it as the alternative to owner searches during

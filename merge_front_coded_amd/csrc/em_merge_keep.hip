@@ -1,10 +1,10 @@
 // Stable merge of each partition plus the keep-newer scan and compaction.
 //
 // Everett, "GPU construction experiment", merge paragraph: merge by diagonal
-// partitions, equal keys put the older input first, a neighbouring-key
-// comparison and an exclusive scan keep the last reference of each equal-key
-// run (so the newer record wins; a newer tombstone stays), and the compacted
-// order fixes every survivor's ordinal.  "CUDA merge path: merging sorted
+// partitions with ties going to the older side, then compare each output
+// with its neighbour and keep only the final reference of a run of equal
+// keys (the newer record, a newer tombstone included), an exclusive scan
+// giving each kept reference its ordinal in the compacted order.  "CUDA merge path: merging sorted
 // arrays in parallel": each worker starts from its own co-rank and takes
 // exactly as many steps as its slice is long.
 //

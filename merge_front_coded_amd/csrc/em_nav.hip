@@ -2,12 +2,13 @@
 // record offsets.
 //
 // Everett, "GPU construction experiment":
-//  * the KV03 paragraph: physical offsets are sampled at ordinals 0, 15, 30,
-//    ... plus EOF; when every encoded value has the same width, that width
-//    times the sample's ordinal is subtracted;
-//  * the output-EF paragraph: each entry is derived from the record-offset
-//    scan (the last from the payload extent); every 256-entry group works out
-//    whether its span in the high bits is at least 4096 bits; a scan of the
+//  * the KV03 paragraph: the sampled offsets are those of every fifteenth
+//    record from the first, and the end of the payload; with one encoded
+//    value width shared by all records, the sample's ordinal times that width
+//    is taken off;
+//  * the output-EF paragraph: the entries come from the record-offset scan
+//    (the last from the payload length); a group of 256 entries is sparse
+//    when its high positions spread over 4096 bits or more; a scan of the
 //    sparse groups' counts assigns their exception ranges; word-owned kernels
 //    write the packed lows, the high bits, the sample pairs and the sparse
 //    positions, zero padded.

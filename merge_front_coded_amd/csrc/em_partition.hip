@@ -1,8 +1,8 @@
 // Merge-path partition: the co-rank of every partition diagonal.
 //
 // "CUDA merge path: merging sorted arrays in parallel", "The merge matrix, and
-// the diagonal that cuts it": the first d outputs of the merge are A[0..i) and
-// B[0..d-i); i is found by bisection over [max(0, d-|B|), min(d, |A|)].  With
+// the diagonal that cuts it": the merge's first d outputs consist of A[0..i)
+// and B[0..d-i); i is found by bisection over [max(0, d-|B|), min(d, |A|)].  With
 // ties going to A (Everett, "GPU construction experiment", the merge
 // paragraph) a candidate i is too large exactly when A[i-1] > B[d-i]; that
 // test is false up to the co-rank and true after it.

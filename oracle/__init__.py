@@ -205,7 +205,7 @@ def common_width(A, B, final: np.ndarray) -> int:
 
 
 def ef_entries(off: np.ndarray, S: int, T: int, width: int) -> np.ndarray:
-    """Offsets at ordinals 0, 15, 30, ... and EOF, less width x ordinal."""
+    """The offsets of records 0, 15, 30, ... and T, each less width x its ordinal."""
     o = np.ascontiguousarray(off, dtype=np.uint64)
     e = np.empty((S + 14) // 15 + 1, np.uint64)
     _load().or_ef_entries(_ptr(o), S, T, width, _ptr(e))

@@ -88,7 +88,7 @@ static const or_side *ref_side(const or_side *A, const or_side *B, uint32_t ref,
 
 /*
  * [MP] sequential loop, [DSA] two-pointer baseline: take A's head while it is
- * <= B's head, so equal keys put the older input first ([GC] merge paragraph).
+ * <= B's head, so that ties go to the older side ([GC] merge paragraph).
  * refs has |A|+|B| entries.
  */
 void or_merge(const or_side *A, const or_side *B, uint32_t *refs) {
@@ -113,9 +113,9 @@ uint32_t or_corank(const uint32_t *refs, uint32_t nA, uint32_t d) {
 }
 
 /*
- * [GC] merge paragraph: a neighbouring-key comparison keeps the last
- * reference of each equal-key run, so the newer record wins; a tombstone stays
- * a record.  The position of a kept reference in the compacted order is its
+ * [GC] merge paragraph: comparing each reference's key with the next one's,
+ * only the final reference of a run of equal keys is kept, so that the newer
+ * record wins (a tombstone is a record like any other).  The position of a kept reference in the compacted order is its
  * output ordinal.  ord_A / ord_B receive that ordinal, or OR_NONE for a
  * dropped record.  Returns the survivor count S.
  */
@@ -482,8 +482,8 @@ int or_fc_decode(const uint8_t *payload, uint64_t T, uint32_t S, uint8_t *keys, 
 /*
  * [BP]  Everett, "Byte-profile GPU merge": the "Pipeline" steps (byte LEB128
  * counts, byte FC literals and optional-value tags; a common encoded value
- * width, where width seventeen means a one-byte presence tag and sixteen
- * payload bytes), with the control rule of [GC] counted in bytes.
+ * width, width seventeen being a tag byte for presence followed by sixteen
+ * bytes of value), with the control rule of [GC] counted in bytes.
  *
  * Readings (the page names the parts, not their bytes):
  *  - l_i is the byte LCP with the preceding survivor (l_0 = 0), k_i the key

@@ -69,7 +69,7 @@ def test_modes_on_edge_cases(mode):
             a.append((k, None if rng.random() < 0.2 else _rand_bytes(rng, 0, 5)))
         else:
             b.append((k, _rand_bytes(rng, 0, 5)))
-    _check(gen.side_from_records(a), gen.side_from_records(b), mode, "binary and proper-prefix keys")
+    _check(gen.side_from_records(a), gen.side_from_records(b), mode, "byte keys with proper prefixes")
     # a large older side and a small newer side, collisions at bitmap word and
     # rank block edges
     big = [b"k%07d" % i for i in range(9000)]
