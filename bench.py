@@ -50,7 +50,7 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
 # x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
 # only while the kernel sources hash to the fingerprint it was taken with.
 TRAFFIC = {
-    "em_emit_merged": (2429776349, ("em_fc.hip", "em_tile.h", "em_internal.h"), "b19d313b34272479"),
+    "em_emit_merged": (2429776349, ("em_fc.hip", "em_tile.h", "em_internal.h"), "d371d775a25b82f6"),
     "em_merge_lengths": (1365603059, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "df298f27f1fe338d"),
 }
 
