@@ -162,3 +162,10 @@ def test_onepass_argument_errors(lib):
     A5 = _side(n=5, key_bytes=5, val_bytes=0)
     assert lib.em_merge_fc_onepass(ctypes.byref(A5), ctypes.byref(B), buf, 64, 64, buf, 1 << 20, buf, buf, None,
                                    None, None, None, None, None, ws, 0, None) == -3
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the HIP library the binding raises; there is no CPU fallback."""
+    from merge_front_coded_amd import binding
+    with pytest.raises(ImportError):
+        binding.load_library(str(tmp_path / "libem.so"))
