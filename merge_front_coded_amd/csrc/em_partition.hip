@@ -7,17 +7,19 @@
 // paragraph) a candidate i is too large exactly when A[i-1] > B[d-i]; that
 // test is false up to the co-rank and true after it.
 //
-// gfx950 design: a group of 16 lanes per diagonal, four diagonals per wave.
-// Each round the group tests 16 evenly spaced candidates at once and a ballot
-// locates the crossing, so the range shrinks 16-fold per round (six rounds
-// for 8M-record inputs) for 96 key reads per diagonal, against ~23 dependent
-// bisection steps or 256 reads for a whole-wave 64-way search.
+// gfx950 design: a group of 4 lanes per diagonal, sixteen diagonals per
+// wave.  Each round the group tests 4 evenly spaced candidates at once and a
+// ballot locates the crossing, so the range shrinks 4-fold per round (twelve
+// rounds for 8M-record inputs, 48 key reads per diagonal).  The search is
+// bound by its key reads rather than by its rounds: at 8M+8M (7,813
+// diagonals) groups of 2, 4, 8, 16, 32 and 64 lanes took 42, 27, 31, 46, 73
+// and 114 us.
 #include "em_tile.h"
 
 namespace em {
 
 constexpr int kPartBlock = 256;
-constexpr uint32_t kGroup = 16;  // lanes per diagonal (corank16)
+constexpr uint32_t kGroup = 4;  // lanes per diagonal
 
 __global__ __launch_bounds__(kPartBlock) void k_partition(em_side_t A, em_side_t B, uint32_t items,
                                                           uint32_t P, uint32_t* __restrict__ splits) {
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kPartBlock) void k_partition(em_side_t A, em_side_t
   uint32_t lo = live ? (d > B.n ? d - B.n : 0) : 0;
   uint32_t hi = live ? (d < A.n ? d : A.n) : 0;
   // the co-rank lies in [lo, hi] and the "too large" test is false at lo
-  lo = corank16(A, B, d, lo, hi, t, gshift);
+  lo = corank_group<kGroup>(A, B, d, lo, hi, t, gshift);
   if (live && t == 0) splits[diag] = lo;
 }
 

@@ -426,13 +426,14 @@ __device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, 
 
 // Co-rank of diagonal d (A records among the first d outputs of the stable
 // merge, ties to A) inside [lo, hi], where the "too large" test A[i-1] > B[d-i]
-// is false at lo.  Searched by a group of 16 lanes: t is the lane in the
-// group, gshift the group's first lane in the wave.  Each round tests 16
-// evenly spaced candidates and a ballot finds the crossing, shrinking the
-// range 16-fold.
-__device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t& B, uint32_t d,
-                                             uint32_t lo, uint32_t hi, uint32_t t, uint32_t gshift) {
-  constexpr uint32_t G = 16;
+// is false at lo.  Searched by a group of G lanes (G a power of two up to
+// 64): t is the lane in the group, gshift the group's first lane in the
+// wave.  Each round tests G evenly spaced candidates and a ballot finds the
+// crossing, shrinking the range G-fold.
+template <uint32_t G>
+__device__ __forceinline__ uint32_t corank_group(const em_side_t& A, const em_side_t& B, uint32_t d, uint32_t lo,
+                                                 uint32_t hi, uint32_t t, uint32_t gshift) {
+  static_assert(G >= 2 && G <= 64 && (G & (G - 1)) == 0, "a power of two lanes, at most a wave");
   while (lo < hi) {
     const uint32_t span = hi - lo;
     const uint32_t c = lo + static_cast<uint32_t>((static_cast<uint64_t>(t + 1) * span) / G);
@@ -440,9 +441,10 @@ __device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t
     if (c > 0 && d - c < B.n && c > lo) {
       too_big = cmp_keys(A.keys, key_of(A, c - 1), B.keys, key_of(B, d - c)) > 0;
     }
-    const uint32_t mask = static_cast<uint32_t>((__ballot(too_big) >> gshift) & 0xFFFFu);
-    // lanes [0, f) of the group are false and lanes [f, 16) true (monotone predicate)
-    const uint32_t f = mask ? static_cast<uint32_t>(__builtin_ctz(mask)) : G;
+    const uint64_t gmask = G == 64 ? ~0ull : ((1ull << G) - 1);
+    const uint64_t mask = (__ballot(too_big) >> gshift) & gmask;
+    // lanes [0, f) of the group are false and lanes [f, G) true (monotone predicate)
+    const uint32_t f = mask ? static_cast<uint32_t>(__builtin_ctzll(mask)) : G;
     const uint32_t c_prev = lo + static_cast<uint32_t>((static_cast<uint64_t>(f) * span) / G);
     if (f == G) {
       lo = hi;
@@ -453,6 +455,11 @@ __device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t
     }
   }
   return lo;
+}
+
+__device__ __forceinline__ uint32_t corank16(const em_side_t& A, const em_side_t& B, uint32_t d, uint32_t lo,
+                                             uint32_t hi, uint32_t t, uint32_t gshift) {
+  return corank_group<16>(A, B, d, lo, hi, t, gshift);
 }
 
 // Co-rank of diagonal d given coarse co-ranks around it: csplits[c] is the
