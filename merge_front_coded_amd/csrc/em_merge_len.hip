@@ -2,10 +2,13 @@
 // merge with keep-newer, exact bit LCPs, record lengths and partition-local
 // bit offsets; (2) one workgroup scans the partitions' bit totals; (3) the
 // word-owned payload emitter, reading the survivor count and payload length
-// the first two left in device memory.
+// the first two left in device memory.  A single-pass variant of kernel 1
+// (kEmit) takes each partition's bit base from a second look-back and writes
+// the partition's payload words itself; a small kernel then writes the words
+// that partition boundaries cut.
 //
 // Everett, "GPU construction experiment": merge by diagonal partitions with
-// equal keys older first; keep the last reference of each equal-key run; the
+// ties to the older side; keep the last reference of each equal-key run; the
 // compacted order fixes predecessors and ordinals; exact lengths (c_i
 // equation, record grammar) are scanned into bit offsets by one global scan
 // with no per-chunk reset (here: a scan inside each partition plus a scan of
