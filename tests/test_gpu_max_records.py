@@ -2,8 +2,9 @@
 accepts.  Three-byte big-endian keys (A: the even numbers below 2^24; B: the
 numbers that are 0 or 1 mod 4, less the last, so that a quarter of all keys is
 in both sides), values of 0..4 bytes, tombstones on B.  Every output of the
-fused path in the bench's launch configuration, of the six-call path and of
-the collision path is compared element by element with the CPU oracle."""
+fused path in the bench's launch configuration, of its single-pass variant,
+of the six-call path and of the collision path is compared element by element
+with the CPU oracle."""
 import numpy as np
 import pytest
 
@@ -41,9 +42,10 @@ def test_record_cap():
     print("oracle on 2^24 - 1 records", flush=True)
     ref = oracle.run(Ah, Bh, items_per_part=2048)
     assert ref["S"] == a.size + b.size - (1 << 22)
-    for path, kw in (("fused", {}), ("merge", {"items": 2048}), ("collision", {"items": 2048})):
-        print(f"  path {path}", flush=True)
-        pl = run_gpu(Ah, Bh, path=path, **({"items": None} if path == "fused" else kw))
+    for path, kw in (("fused", {"items": None}), ("fused", {"items": None, "one_pass": True}),
+                     ("merge", {"items": 2048}), ("collision", {"items": 2048})):
+        print(f"  path {path} {kw}", flush=True)
+        pl = run_gpu(Ah, Bh, path=path, **kw)
         compare(pl, ref, Ah, Bh, label=f"record cap, {path}")
         del pl
         torch.cuda.empty_cache()
