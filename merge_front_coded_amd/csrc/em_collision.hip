@@ -161,19 +161,45 @@ __global__ __launch_bounds__(kColBlock) void k_rank2048_finish(const uint32_t* _
 }
 
 // mark: lower bound of every B key in A, collision bit on an equal key.
-__global__ __launch_bounds__(kColBlock) void k_mark(em_side_t A, em_side_t B, uint32_t* __restrict__ bits,
-                                                    uint32_t* __restrict__ lb_out) {
-  const uint32_t j = blockIdx.x * kColBlock + threadIdx.x;
-  if (j >= B.n) return;
-  const KeyRef kb = key_of(B, j);
-  uint32_t lo = 0, hi = A.n;
+// lower_bound(A, key) inside [lo, hi]
+__device__ __forceinline__ uint32_t lower_bound_in(const em_side_t& A, const uint8_t* kbytes, KeyRef k, uint32_t lo,
+                                                   uint32_t hi) {
   while (lo < hi) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
-    if (cmp_keys(A.keys, key_of(A, mid), B.keys, kb) < 0)
+    if (cmp_keys(A.keys, key_of(A, mid), kbytes, k) < 0)
       lo = mid + 1;
     else
       hi = mid;
   }
+  return lo;
+}
+
+// B in groups of 64 consecutive records: a first kernel finds the lower
+// bound of each group's first key in all of A (and A.n after the last
+// group); each record then searches only between its group's bound and the
+// next group's (B is sorted, so its lower bounds are monotone): about 7
+// instead of 23 dependent key comparisons per record at 8M + 8M.  Used when
+// B holds at least one record per 64 of A (else, edges == nullptr, every
+// record searches all of A: with few B records a group's range stays wide
+// and the first kernel's searches only add a serial step).
+constexpr uint32_t kMarkGroup = 64;
+
+__global__ __launch_bounds__(kColBlock) void k_mark_edges(em_side_t A, em_side_t B, uint32_t groups,
+                                                          uint32_t* __restrict__ edges) {
+  const uint32_t g = blockIdx.x * kColBlock + threadIdx.x;
+  if (g > groups) return;
+  edges[g] = g < groups ? lower_bound_in(A, B.keys, key_of(B, g * kMarkGroup), 0, A.n) : A.n;
+}
+
+__global__ __launch_bounds__(kColBlock) void k_mark(em_side_t A, em_side_t B, const uint32_t* __restrict__ edges,
+                                                    uint32_t* __restrict__ bits, uint32_t* __restrict__ lb_out) {
+  const uint32_t j = blockIdx.x * kColBlock + threadIdx.x;
+  if (j >= B.n) return;
+  const KeyRef kb = key_of(B, j);
+  // (for unsorted inputs the bounds may be out of order: the result is then
+  // the lower one, still inside A)
+  const uint32_t lo = edges ? lower_bound_in(A, B.keys, kb, edges[j / kMarkGroup], edges[j / kMarkGroup + 1])
+                            : lower_bound_in(A, B.keys, kb, 0, A.n);
   if (lo < A.n && cmp_keys(A.keys, key_of(A, lo), B.keys, kb) == 0)
     atomicOr(bits + (lo >> 5), 1u << (lo & 31u));
   lb_out[j] = lo;
@@ -194,7 +220,10 @@ __global__ __launch_bounds__(kColBlock) void k_scatter_B(uint32_t nA, uint32_t n
 
 // Independent lower bounds: each surviving A_i searches B's keys.
 template <class View>
+// (edges, when not null: the lower bounds in B of the first keys of A's
+// groups of 64, as k_mark's, to narrow each search)
 __global__ __launch_bounds__(kColBlock) void k_scatter_A_search(em_side_t A, em_side_t B, View rv,
+                                                                const uint32_t* __restrict__ edges,
                                                                 uint32_t* __restrict__ final_refs,
                                                                 uint32_t* __restrict__ ord_A) {
   const uint32_t i = blockIdx.x * kColBlock + threadIdx.x;
@@ -204,14 +233,8 @@ __global__ __launch_bounds__(kColBlock) void k_scatter_A_search(em_side_t A, em_
     return;
   }
   const KeyRef ka = key_of(A, i);
-  uint32_t lo = 0, hi = B.n;
-  while (lo < hi) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    if (cmp_keys(B.keys, key_of(B, mid), A.keys, ka) < 0)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
+  const uint32_t lo = edges ? lower_bound_in(B, A.keys, ka, edges[i / kMarkGroup], edges[i / kMarkGroup + 1])
+                            : lower_bound_in(B, A.keys, ka, 0, B.n);
   const uint32_t o = i + lo - rv.rank(i);
   final_refs[o] = i;
   if (ord_A) ord_A[i] = o;
@@ -434,8 +457,13 @@ size_t rank_ws(uint32_t nbits) { return align_up(rank_layout(nullptr, nbits).use
 
 // Collision workspace of one mode: the rank layout, the saved B lower bounds
 // and (compact mode) the compact A list.
+static size_t mark_edges_bytes(uint32_t nB) {
+  return align_up((static_cast<size_t>(nB) / kMarkGroup + 2) * sizeof(uint32_t), 256);
+}
+
 static size_t collision_mode_ws(uint32_t nA, uint32_t nB, uint32_t mode) {
-  size_t b = rank_ws(nA) + align_up(static_cast<size_t>(nB) * sizeof(uint32_t) + 4, 256);
+  size_t b = rank_ws(nA) + align_up(static_cast<size_t>(nB) * sizeof(uint32_t) + 4, 256) + mark_edges_bytes(nB) +
+             mark_edges_bytes(nA);
   if (mode == EM_COLLISION_512_COMPACT) b += align_up(static_cast<size_t>(nA) * sizeof(uint32_t) + 4, 256);
   return b;
 }
@@ -471,9 +499,28 @@ static int collision_run(const em_side_t& A, const em_side_t& B, uint32_t mode, 
   RankLayout L = rank_layout(ws, A.n);
   uint8_t* after = static_cast<uint8_t*>(ws) + align_up(L.used, 256);
   uint32_t* lb = reinterpret_cast<uint32_t*>(after);
-  uint32_t* cA = reinterpret_cast<uint32_t*>(after + align_up(static_cast<size_t>(B.n) * 4 + 4, 256));
+  uint32_t* edges = reinterpret_cast<uint32_t*>(after + align_up(static_cast<size_t>(B.n) * 4 + 4, 256));
+  uint32_t* edgesA = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(edges) + mark_edges_bytes(B.n));
+  uint32_t* cA = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(edgesA) + mark_edges_bytes(A.n));
+  // the A-side searches of B (modes 512 and 2048) narrowed the same way
+  const uint32_t* a_edges = nullptr;
+  if (A.n && B.n && (mode == EM_COLLISION_512 || mode == EM_COLLISION_2048) &&
+      static_cast<uint64_t>(A.n) * kMarkGroup >= B.n) {
+    const uint32_t groups = (A.n + kMarkGroup - 1) / kMarkGroup;
+    hipLaunchKernelGGL(k_mark_edges, dim3(blocks_for(static_cast<uint64_t>(groups) + 1)), dim3(kColBlock), 0, st, B,
+                       A, groups, edgesA);
+    a_edges = edgesA;
+  }
   clear_u32(L.bits, 64 * static_cast<size_t>(L.nsb) + 16, st);
-  if (B.n) hipLaunchKernelGGL(k_mark, dim3(blocks_for(B.n)), dim3(kColBlock), 0, st, A, B, L.bits, lb);
+  if (B.n) {
+    const uint32_t groups = (B.n + kMarkGroup - 1) / kMarkGroup;
+    const bool narrow = static_cast<uint64_t>(B.n) * kMarkGroup >= A.n;
+    if (narrow)
+      hipLaunchKernelGGL(k_mark_edges, dim3(blocks_for(static_cast<uint64_t>(groups) + 1)), dim3(kColBlock), 0, st,
+                         A, B, groups, edges);
+    hipLaunchKernelGGL(k_mark, dim3(blocks_for(B.n)), dim3(kColBlock), 0, st, A, B, narrow ? edges : nullptr, L.bits,
+                       lb);
+  }
   int rc = check_launch();
   if (rc) return rc;
   const bool r2048 = mode == EM_COLLISION_2048;
@@ -498,7 +545,7 @@ static int collision_run(const em_side_t& A, const em_side_t& B, uint32_t mode, 
                          v2048, lb, final_refs, ord_B);
     if (A.n)
       hipLaunchKernelGGL(k_scatter_A_search<Rank2048View>, dim3(blocks_for(A.n)), dim3(kColBlock), 0, st, A,
-                         B, v2048, final_refs, ord_A);
+                         B, v2048, a_edges, final_refs, ord_A);
     hipLaunchKernelGGL(k_collision_total<Rank2048View>, dim3(1), dim3(1), 0, st, A.n, B.n, v2048, d_S);
     return check_launch();
   }
@@ -513,7 +560,7 @@ static int collision_run(const em_side_t& A, const em_side_t& B, uint32_t mode, 
                          dim3(kColBlock), 0, st, A.n, B.n, v512, lb, final_refs, ord_A);
     else
       hipLaunchKernelGGL(k_scatter_A_search<Rank512View>, dim3(blocks_for(A.n)), dim3(kColBlock), 0, st, A,
-                         B, v512, final_refs, ord_A);
+                         B, v512, a_edges, final_refs, ord_A);
   }
   hipLaunchKernelGGL(k_collision_total<Rank512View>, dim3(1), dim3(1), 0, st, A.n, B.n, v512, d_S);
   return check_launch();
