@@ -406,10 +406,10 @@ __device__ __forceinline__ uint32_t fi_owner(const uint32_t* __restrict__ tree, 
 // owner of bit r_i - 1 is pse(i) = max{t < i : r_t < r_i} (every record after
 // it up to i retains at least r_i bits), and the owner of the bit below
 // fragment j's start is pse(j).  pse comes from one owner query per record.
-// Block heads (records 15k) follow their chain to a record with r = 0; any
-// other record follows it while it stays inside its block and takes the
-// bits below from its block head's key, written by the kernel before (all
-// records from the head on keep those bits).
+// Block heads (records 15k) follow their chain to a record with r = 0 for
+// their inherited bytes (the kernel before writes those); any other record
+// follows it while it stays inside its block and takes the bits below from
+// its block head's key (all records from the head on keep those bits).
 
 __global__ __launch_bounds__(kFiBlock) void k_fi_pse(FiLayout L) {
   const uint32_t i = blockIdx.x * kFiBlock + threadIdx.x;
@@ -513,7 +513,13 @@ __device__ __forceinline__ bool fi_record_ok(const FiLayout& L, uint32_t i, uint
   return L.koff[i] + L.kbytes[i] <= key_cap && L.voff[i] + L.vbytes[i] <= val_cap;
 }
 
-// block heads' keys, one thread each
+// block heads' inherited bytes, one thread each: key bytes [0, ceil(r_i / 8)),
+// the last of them complete (it also holds the literal's first bits).  The
+// literal bytes after them are the records kernel's.
+__device__ __forceinline__ uint32_t fi_head_bytes(const FiLayout& L, uint32_t i) {
+  return min((L.r[i] + 7u) >> 3, L.kbytes[i]);
+}
+
 __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, uint8_t* __restrict__ keys,
                                                        uint64_t key_cap, uint64_t val_cap,
                                                        uint64_t* __restrict__ err) {
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
   if (k >= L.nb) return;
   const uint32_t i = k * kFiRecs;
   if (!fi_record_ok(L, i, key_cap, val_cap)) return;  // (flagged by k_fi_records)
-  fi_key(bits, L, i, kFiInf, nullptr, keys + L.koff[i], L.kbytes[i], err);
+  fi_key(bits, L, i, kFiInf, nullptr, keys + L.koff[i], fi_head_bytes(L, i), err);
 }
 
 // every record: offsets, tombstone flag, value bytes, and the key of a
@@ -531,12 +537,13 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
 // from the 16-byte boundary below its start), the records are written there
 // and the workgroup copies the two ranges out with 16-byte stores, single
 // bytes only in the groups it shares with its neighbours.  In the window a key
-// is built as the encoder defined it: a block head's key is copied from the
-// arena (the kernel before wrote it); every other record writes its literal,
+// is built as the encoder defined it: a block head's inherited bytes are
+// copied from the arena (the kernel before wrote them) and its literal from
+// the payload; every other record writes its literal,
 // then, in fourteen rounds (round j: the records at block position j), takes
 // its first r_i bits from its predecessor's finished key.  A workgroup whose
 // ranges do not fit writes each record to the arenas directly, its key by the
-// owner chain.
+// owner chain (after a barrier, so that the heads' literals are there).
 constexpr uint32_t kFiWin = 24576;
 
 // [b0, b1) of an arena from its window copy starting at base = b0 & ~15
@@ -574,7 +581,8 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
   uint8_t* kwin = win;
   uint8_t* vwin = win + (staged ? kspan : 0);
   const uint32_t i = r0 + threadIdx.x;
-  bool ok = false;  // a staged record that takes its prefix in the rounds
+  bool ok = false;     // a staged record that takes its prefix in the rounds
+  bool chain = false;  // an unstaged record that takes its key by the owner chain
   if (threadIdx.x < rpb && i < r1) {
     const uint64_t ko = L.koff[i], vo = L.voff[i];
     key_off[i] = static_cast<uint32_t>(ko);
@@ -600,11 +608,18 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
         }
         ok = true;
       } else {
-        for (uint32_t t = 0; t < kb; ++t) key[t] = keys[ko + t];
+        const uint32_t own = fi_head_bytes(L, i);
+        for (uint32_t t = 0; t < own; ++t) key[t] = keys[ko + t];
+        if (own < kb) fi_copy_bytes(bits, L.lit[i] + (8ull * own - L.r[i]), key + own, kb - own);
       }
       fi_copy_bytes(bits, L.vbit[i], vwin + (vo - vbase), vb);
     } else {
-      if (i != head) fi_key(bits, L, i, head, keys + L.koff[head], keys + ko, kb, err);
+      if (i == head) {
+        const uint32_t own = fi_head_bytes(L, i);
+        if (own < kb) fi_copy_bytes(bits, L.lit[i] + (8ull * own - L.r[i]), keys + ko + own, kb - own);
+      } else {
+        chain = true;
+      }
       fi_copy_bytes(bits, L.vbit[i], vals + vo, vb);
     }
   }
@@ -612,7 +627,11 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
     key_off[L.S] = static_cast<uint32_t>(L.koff[L.S]);
     val_off[L.S] = static_cast<uint32_t>(L.voff[L.S]);
   }
-  if (!staged) return;
+  if (!staged) {  // (uniform over the workgroup)
+    __syncthreads();  // the heads' literals are in the arena
+    if (chain) fi_key(bits, L, i, i - i % kFiRecs, keys + L.koff[i - i % kFiRecs], keys + L.koff[i], L.kbytes[i], err);
+    return;
+  }
   const uint32_t pos = threadIdx.x % kFiRecs;  // (r0 is a multiple of 15)
   for (uint32_t j = 1; j < kFiRecs; ++j) {
     __syncthreads();
