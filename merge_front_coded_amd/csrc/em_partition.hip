@@ -12,8 +12,10 @@
 // ballot locates the crossing, so the range shrinks 4-fold per round (twelve
 // rounds for 8M-record inputs, 48 key reads per diagonal).  The search is
 // bound by its key reads rather than by its rounds: at 8M+8M (7,813
-// diagonals) groups of 2, 4, 8, 16, 32 and 64 lanes took 42, 27, 31, 46, 73
-// and 114 us.
+// diagonals), run alone in a loop so that the keys it reads stay cached,
+// groups of 2, 4, 8, 16, 32 and 64 lanes took 42, 27, 31, 46, 73 and 114 us.
+// Run after an emitter has swept the caches, 4 and 16 lanes both take 42 us:
+// the cold key reads, twelve dependent rounds of them, set the time.
 #include "em_tile.h"
 
 namespace em {
