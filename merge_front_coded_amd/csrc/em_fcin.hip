@@ -520,6 +520,63 @@ __device__ __forceinline__ uint32_t fi_head_bytes(const FiLayout& L, uint32_t i)
   return min((L.r[i] + 7u) >> 3, L.kbytes[i]);
 }
 
+// Key bytes [0, nbytes) of record i down its whole owner chain (the same
+// fragments as fi_key with no head), written as they complete from the top.
+// A head's chain is long (about a dozen owners at 8M+8M, each covering a few
+// bits) and every owner's fields are a cold load, so each step issues the
+// current fragment's payload reads and the next owner's r, literal position
+// and pse together: one memory round trip per owner instead of three.
+template <class Bits>
+__device__ __forceinline__ void fi_head_prefix(const Bits& bits, const FiLayout& L, uint32_t i,
+                                               uint8_t* __restrict__ key, uint32_t nbytes,
+                                               uint64_t* __restrict__ err) {
+  if (nbytes == 0) return;
+  uint32_t hi = 8u * nbytes;  // key bits [hi, 8 nbytes) are done (pending byte aside)
+  uint32_t lo = min(L.r[i], hi);
+  uint64_t base = L.lit[i] - L.r[i];  // key bit q of the current owner is payload bit base + q
+  uint32_t np = L.pse[i];
+  uint32_t pv = 0;  // key byte hi >> 3 as far as it is filled (when hi is not byte aligned)
+  while (true) {
+    // this fragment's partial bytes: the top one (completing the pending
+    // byte) and the bottom one; whole bytes between them are copied below
+    const uint32_t top_lo = max(lo, hi & ~7u);
+    const bool has_top = (hi & 7u) && top_lo < hi;
+    const uint32_t t_hi = has_top ? top_lo : hi;          // byte aligned, or lo
+    const uint32_t w_lo = min((lo + 7u) & ~7u, t_hi);     // whole bytes [w_lo, t_hi)
+    const bool has_bot = lo < w_lo;                        // bits [lo, w_lo) of byte lo >> 3
+    const uint32_t vt = has_top ? bits.at32(base + top_lo) : 0u;
+    const uint32_t vb = has_bot ? bits.at32(base + lo) : 0u;
+    // the next owner, loaded alongside
+    const bool more = lo > 0;
+    uint32_t nr = 0, nnp = kFiInf;
+    uint64_t nlit = 0;
+    if (more && np != kFiInf) {
+      nr = L.r[np];
+      nlit = L.lit[np];
+      nnp = L.pse[np];
+    }
+    if (has_top) {  // key bits [top_lo, hi) into the pending byte
+      const uint32_t n = hi - top_lo;
+      pv |= (vt >> (32u - n)) << (8u - (hi & 7u));
+      if (top_lo == (hi & ~7u)) key[hi >> 3] = static_cast<uint8_t>(pv), pv = 0;
+    }
+    if (w_lo < t_hi) fi_copy_bytes(bits, base + w_lo, key + (w_lo >> 3), (t_hi - w_lo) >> 3);
+    if (has_bot) {  // key bits [lo, w_lo): the low end of byte lo >> 3, pending
+      const uint32_t n = w_lo - lo;
+      pv = vb >> (32u - n);  // (w_lo is the byte's end)
+    }
+    if (!more) return;  // (lo = 0: nothing is pending)
+    if (np == kFiInf || nr >= lo) {  // no earlier owner for the bits below
+      atomicOr(reinterpret_cast<unsigned long long*>(err), static_cast<unsigned long long>(kFiErrPrefix));
+      return;
+    }
+    hi = lo;
+    lo = nr;
+    base = nlit - nr;
+    np = nnp;
+  }
+}
+
 __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, uint8_t* __restrict__ keys,
                                                        uint64_t key_cap, uint64_t val_cap,
                                                        uint64_t* __restrict__ err) {
@@ -527,7 +584,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
   if (k >= L.nb) return;
   const uint32_t i = k * kFiRecs;
   if (!fi_record_ok(L, i, key_cap, val_cap)) return;  // (flagged by k_fi_records)
-  fi_key(bits, L, i, kFiInf, nullptr, keys + L.koff[i], fi_head_bytes(L, i), err);
+  fi_head_prefix(bits, L, i, keys + L.koff[i], fi_head_bytes(L, i), err);
 }
 
 // every record: offsets, tombstone flag, value bytes, and the key of a
