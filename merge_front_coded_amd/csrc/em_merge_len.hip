@@ -528,8 +528,12 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(kEmit 
 }
 
 // Exclusive scan of the partitions' bit totals into bit bases (one
-// workgroup; P is at most 2^16), and T.
+// workgroup; P is at most 2^16), and T.  Up to 8192 partitions (8M+8M at
+// 2048 outputs each is 7,813) a thread's values are loaded at once and kept
+// in registers: the kernel is a chain of latencies, and a loop of dependent
+// loads, read twice, took 11 us.
 constexpr int kTsBlock = 1024;
+constexpr uint32_t kTsRegs = 8;
 
 __global__ __launch_bounds__(kTsBlock) void k_tile_scan(const uint64_t* __restrict__ tile_bits, uint32_t P,
                                                         uint64_t* __restrict__ tbase, uint64_t* __restrict__ d_T) {
@@ -537,14 +541,30 @@ __global__ __launch_bounds__(kTsBlock) void k_tile_scan(const uint64_t* __restri
   const uint32_t tid = threadIdx.x;
   const uint32_t per = (P + kTsBlock - 1) / kTsBlock;
   const uint32_t lo = min(tid * per, P), hi = min(lo + per, P);
-  uint64_t sum = 0;
-  for (uint32_t t = lo; t < hi; ++t) sum += tile_bits[t];
   uint64_t total;
-  uint64_t acc = block_exclusive_scan<uint64_t, kTsBlock>(sum, scan, total);
-  for (uint32_t t = lo; t < hi; ++t) {
-    const uint64_t v = tile_bits[t];
-    tbase[t] = acc;
-    acc += v;
+  if (per <= kTsRegs) {  // (uniform)
+    uint64_t v[kTsRegs];
+    uint64_t sum = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kTsRegs; ++q) {
+      v[q] = lo + q < hi ? tile_bits[lo + q] : 0ull;
+      sum += v[q];
+    }
+    uint64_t acc = block_exclusive_scan<uint64_t, kTsBlock>(sum, scan, total);
+#pragma unroll
+    for (uint32_t q = 0; q < kTsRegs; ++q) {
+      if (lo + q < hi) tbase[lo + q] = acc;
+      acc += v[q];
+    }
+  } else {
+    uint64_t sum = 0;
+    for (uint32_t t = lo; t < hi; ++t) sum += tile_bits[t];
+    uint64_t acc = block_exclusive_scan<uint64_t, kTsBlock>(sum, scan, total);
+    for (uint32_t t = lo; t < hi; ++t) {
+      const uint64_t v = tile_bits[t];
+      tbase[t] = acc;
+      acc += v;
+    }
   }
   if (tid == 0) d_T[0] = total;
 }

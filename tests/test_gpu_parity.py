@@ -68,6 +68,17 @@ def test_fused_every_partition_size(items, coarse_parts):
     check_path(A, B, items=items, path="fused", coarse_parts=coarse_parts)
 
 
+@pytest.mark.parametrize("scale,items", [(0.4096, 1), (0.4097, 1), (1.0, 2), (1.0, 1)])
+def test_fused_many_partitions(scale, items):
+    """8192, 8194, 10000 and 20000 partitions: the scan of partition bit
+    totals keeps up to eight values per thread in registers and loops above
+    that (8192 is the last count that fits)."""
+    A, B = workload(1, scale)
+    P = -(-(A.n + B.n) // items)
+    print(f"fused uniform-az {A.n}+{B.n} items={items}: {P} partitions", flush=True)
+    check_path(A, B, items=items, path="fused")
+
+
 @pytest.mark.parametrize("items", [64, 1024, 2048])
 def test_fused_one_call_matches_oracle(items):
     """em_merge_fc (both halves in one call) gives the same outputs."""
