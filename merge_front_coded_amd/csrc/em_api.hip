@@ -47,6 +47,26 @@ __global__ void k_clear_u32(uint32_t* p, size_t n) {
   for (; i < n; i += static_cast<size_t>(gridDim.x) * blockDim.x) p[i] = 0;
 }
 
+__global__ void k_clear_lookback(uint32_t* t, size_t nt, uint64_t* d0, uint64_t* d1, size_t nd) {
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < nt || i < nd; i += stride) {
+    if (i < nt) t[i] = 0;
+    if (i < nd) {
+      d0[i] = 0;
+      if (d1) d1[i] = 0;
+    }
+  }
+}
+
+void clear_lookback(uint32_t* ticket, size_t nt, uint64_t* d0, uint64_t* d1, size_t nd, hipStream_t st) {
+  const size_t n = nt > nd ? nt : nd;
+  if (!n) return;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_clear_lookback, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, st, ticket, nt, d0, d1,
+                     nd);
+}
+
 void clear_u64(uint64_t* p, size_t n, hipStream_t st) {
   if (!n) return;
   size_t blocks = (n + 255) / 256;

@@ -308,6 +308,9 @@ void clear_u64(uint64_t* p, size_t n, hipStream_t st);
 template <class OutT>
 int scan_launch(const uint32_t* in, uint32_t n, OutT* out, void* ws, size_t ws_bytes, hipStream_t st);
 void clear_u32(uint32_t* p, size_t n, hipStream_t st);
+// A look-back's state in one launch: nt u32 ticket words and nd u64
+// descriptors of d0 (and of d1 when it is not null).
+void clear_lookback(uint32_t* ticket, size_t nt, uint64_t* d0, uint64_t* d1, size_t nd, hipStream_t st);
 
 // A record offset in partition form: partition number (< 2^24) above this
 // bit, the offset inside the partition's bits below it.

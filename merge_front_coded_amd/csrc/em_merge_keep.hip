@@ -200,8 +200,7 @@ extern "C" int em_merge_keep(const em_side_t* A, const em_side_t* B, const uint3
   WsCursor cur{static_cast<uint8_t*>(ws), 0};
   uint32_t* ticket = cur.take<uint32_t>(64);
   uint64_t* desc = cur.take<uint64_t>(P);
-  clear_u32(ticket, 1, st);
-  clear_u64(desc, P, st);
+  clear_lookback(ticket, 1, desc, nullptr, P, st);
   const uint32_t ipt = (items_per_part + kMergeBlock - 1) / kMergeBlock;
   if (ipt <= 1)
     launch_merge<1>(*A, *B, splits, items_per_part, P, final_refs, ord_A, ord_B, d_S, ticket, desc, st);

@@ -693,8 +693,7 @@ extern "C" int em_merge_lengths(const em_side_t* A, const em_side_t* B, const ui
   }
   const uint32_t P = (N + items_per_part - 1) / items_per_part;
   const MlLayout L = ml_layout(ws, N, items_per_part);
-  clear_u32(L.ticket, kEmitCtrStride + kEmitCtrWords, st);
-  clear_u64(L.desc_s, P, st);
+  clear_lookback(L.ticket, kEmitCtrStride + kEmitCtrWords, L.desc_s, nullptr, P, st);
   MlOut o{d_S, final_refs ? final_refs : L.refs, lcp_bits ? lcp_bits : L.lcp, L.toff, L.tile_bits,
           ord_A, ord_B, len_bits, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   launch_ml_items<false>(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);
@@ -771,9 +770,7 @@ extern "C" int em_merge_fc_onepass(const em_side_t* A, const em_side_t* B, const
   }
   const uint32_t P = (N + items_per_part - 1) / items_per_part;
   const MlLayout L = ml_layout(ws, N, items_per_part);
-  clear_u32(L.ticket, 1, st);
-  clear_u64(L.desc_s, P, st);
-  clear_u64(L.desc_b, P, st);
+  clear_lookback(L.ticket, 1, L.desc_s, L.desc_b, P, st);
   MlOut o{d_S, final_refs, lcp_bits, nullptr, L.tile_bits, ord_A, ord_B, len_bits,
           payload, L.desc_b, L.edge_lo, L.edge_hi, off, d_T};
   launch_ml_items<true>(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);

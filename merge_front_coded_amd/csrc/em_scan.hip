@@ -112,8 +112,7 @@ int scan_launch(const uint32_t* in, uint32_t n, OutT* out, void* ws, size_t ws_b
   WsCursor cur{static_cast<uint8_t*>(ws), 0};
   uint32_t* ticket = cur.take<uint32_t>(64);
   uint64_t* desc = cur.take<uint64_t>(ntiles);
-  clear_u32(ticket, 1, st);
-  clear_u64(desc, ntiles, st);
+  clear_lookback(ticket, 1, desc, nullptr, ntiles, st);
   hipLaunchKernelGGL(k_scan<OutT>, dim3(ntiles), dim3(kScanBlock), 0, st, in, n, out, ticket, desc,
                      ntiles);
   return check_launch();
