@@ -587,8 +587,9 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
   fi_head_prefix(bits, L, i, keys + L.koff[i], fi_head_bytes(L, i), err);
 }
 
-// every record: offsets, tombstone flag, value bytes, and the key of a
-// record that is not a block head.  A workgroup takes rpb consecutive records
+// every record: offsets, tombstone flag, value bytes, and the key bytes not
+// written before (all of a record's that is not a block head; a head's
+// literal).  A workgroup takes rpb consecutive records
 // (one a thread; rpb a multiple of 15, so whole blocks), whose key bytes and
 // value bytes are two contiguous ranges.  When both fit the LDS window (each
 // from the 16-byte boundary below its start), the records are written there
@@ -596,11 +597,12 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
 // bytes only in the groups it shares with its neighbours.  In the window a key
 // is built as the encoder defined it: a block head's inherited bytes are
 // copied from the arena (the kernel before wrote them) and its literal from
-// the payload; every other record writes its literal,
-// then, in fourteen rounds (round j: the records at block position j), takes
-// its first r_i bits from its predecessor's finished key.  A workgroup whose
-// ranges do not fit writes each record to the arenas directly, its key by the
-// owner chain (after a barrier, so that the heads' literals are there).
+// the payload; every other record writes its literal, then, in fourteen
+// rounds (round j: the records at block position j), takes its first r_i bits
+// from its predecessor's finished key.  A workgroup whose ranges do not fit
+// writes each record to the arenas directly: the heads' literals first, then,
+// after a barrier, every other key by the owner chain, which may read a
+// head's literal bytes.
 constexpr uint32_t kFiWin = 24576;
 
 // [b0, b1) of an arena from its window copy starting at base = b0 & ~15
