@@ -70,7 +70,7 @@ def measured_traffic(call, workload):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)  # (about 50 ms timed: enough steps to average out run-to-run spread)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
     ap.add_argument("--path", choices=("fused", "onepass", "merge", "collision"), default="fused")
