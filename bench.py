@@ -50,8 +50,8 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
 # x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
 # only while the kernel sources hash to the fingerprint it was taken with.
 TRAFFIC = {
-    "em_emit_merged": (2448232189, ("em_fc.hip", "em_tile.h", "em_internal.h"), "c8d2f1aea60c8aa8"),
-    "em_merge_lengths": (1362976845, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "1e287638ee2bf0dd"),
+    "em_emit_merged": (2448967025, ("em_fc.hip", "em_tile.h", "em_internal.h"), "ec2ae1f6c1a0a1d3"),
+    "em_merge_lengths": (1369414239, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "46804e2764cf09db"),
 }
 
 
