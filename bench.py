@@ -50,8 +50,8 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
 # x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
 # only while the kernel sources hash to the fingerprint it was taken with.
 TRAFFIC = {
-    "em_emit_merged": (2448967025, ("em_fc.hip", "em_tile.h", "em_internal.h"), "ec2ae1f6c1a0a1d3"),
-    "em_merge_lengths": (1369414239, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "46804e2764cf09db"),
+    "em_emit_merged": (2448967025, ("em_fc.hip", "em_tile.h", "em_internal.h"), "9f59be35adeafe05"),
+    "em_merge_lengths": (1369414239, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "23d8a1b0ebd1ec29"),
 }
 
 

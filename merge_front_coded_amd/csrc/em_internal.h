@@ -120,9 +120,8 @@ __device__ __forceinline__ uint32_t eg0_len(uint64_t x) {
 // `lds_wave_base` is the same for the whole wave.  The caller waits for the
 // loads (s_waitcnt vmcnt) and synchronises before reading the LDS.
 // The sources staged this way are read once, so the loads carry the
-// non-temporal cache policy (cache-policy bit 1): the emitter's timings were
-// the same at best and never showed the occasional 6% slower run that they
-// did with the default policy.
+// non-temporal cache policy (cache-policy bit 1).  The emitter measured the
+// same with either policy, within the run-to-run spread.
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(src), lds_wave_base, 16, 0, 2);
 }
