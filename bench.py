@@ -18,8 +18,17 @@ synchronisations.  Prints one JSON line.
   GB/s       B_io / step time, B_io = both sides' key and value arenas, u32
              offsets and tombstone bytes, plus the payload bytes
   roofline   the dominant kernel's algorithmic bytes per launch over its
-             average launch time (HIP events on the launch stream)
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload
+             average launch time (HIP events on the launch stream); the
+             algorithmic bytes are the input and output bytes the call must
+             move (arenas, offsets, tombstone flags, payload), not the
+             references, lengths and offsets one kernel hands to another
+  parity     before any timing, the payload, S and T of the timed
+             configuration are compared with the oracle's digests of the same
+             workload (tests/golden/full_size_digests.json) or, for a scaled
+             workload, with the oracle run on the same host buffers; a
+             mismatch exits with status 3 and no timing
+  cpu_baseline  the CPU oracle (one thread) on the same host buffers as the
+             timed step, its payload compared with the GPU's
 """
 from __future__ import annotations
 
@@ -42,29 +51,75 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
              "em_scan": "k_scan", "em_emit": "k_emit",
              "em_collision_rank_mode": "k_mark, rank build, scatter or compact + merge",
              "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit",
-             "em_merge_fc_onepass": "k_merge_len<4, true> + k_edge_fix"}
+             "em_merge_fc_onepass": "k_merge_len<4, true> + k_edge_fix",
+             "em_merge_fc": "k_merge_len + k_tile_scan + k_emit"}
 
 
-# Scaled HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE passes on
-# the 8M+8M base64 workload (profiles/traffic_fused_base64_8M+8M.md: FETCH_SIZE
-# x 2.0, WRITE_SIZE x 1.0, from a 1 GiB device copy).  A figure is reported
-# only while the kernel sources hash to the fingerprint it was taken with.
-TRAFFIC = {
-    "em_emit_merged": (2448967025, ("em_fc.hip", "em_tile.h", "em_internal.h"), "9f59be35adeafe05"),
-    "em_merge_lengths": (1369414239, ("em_merge_len.hip", "em_tile.h", "em_internal.h"), "23d8a1b0ebd1ec29"),
-}
+def measured_traffic(call, workload_name):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of the call's kernel,
+    from profiles/traffic_<workload>.md, while its sources still hash to the
+    fingerprint recorded there by the rocprofv3 run (else None)."""
+    from merge_front_coded_amd import profiling
+    return profiling.measured_traffic(call, workload_name)
 
 
-def measured_traffic(call, workload):
+def make_pipeline(A, B, path="fused", items=None, coarse_parts=0, collision_mode="512-tiled"):
+    """The pipeline in the configuration the benchmark times: the fused paths
+    keep no per-record arrays (final refs, ordinals, lengths, LCPs and offsets
+    are not written; the emitter's inputs live in the workspace)."""
+    import merge_front_coded_amd as em
+    fused = path in ("fused", "onepass", "onecall")
+    extra = {"coarse_parts": coarse_parts} if (fused and coarse_parts) else {}
+    if path == "collision":
+        extra["collision_mode"] = collision_mode
+    if path == "onepass":
+        extra["one_pass"] = True
+    if path == "onecall":
+        extra["one_call"] = True
+    return em.Pipeline(A, B, items_per_part=items or None, path="fused" if fused else path,
+                       keep_all=not fused, **extra)
+
+
+def payload_digest(pl) -> str:
     import hashlib
-    if workload != 3 or call not in TRAFFIC:
+    return hashlib.sha256(pl.payload_bytes()).hexdigest()
+
+
+def reference_digest(workload_id, scale=1.0):
+    """The oracle's (S, T, payload SHA-256) for a full-size workload, from the
+    digests tests/golden/make_full_size_digests.py wrote (None if absent)."""
+    path = os.path.join(ROOT, "tests", "golden", "full_size_digests.json")
+    if scale != 1.0 or not os.path.exists(path):
         return None
-    nbytes, files, want = TRAFFIC[call]
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "merge_front_coded_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return nbytes if h.hexdigest()[:16] == want else None
+    with open(path) as f:
+        d = json.load(f).get(str(workload_id))
+    return None if d is None else (d["S"], d["T"], d["payload"])
+
+
+def oracle_run(Ah, Bh):
+    """The CPU oracle on the given host buffers: merge, keep-newer, bitwise
+    encoding.  Returns (S, T, payload SHA-256, seconds)."""
+    import hashlib
+    import oracle
+    t0 = time.perf_counter()
+    refs = oracle.merge(Ah, Bh)
+    final, _, _, S = oracle.keep(Ah, Bh, refs)
+    _, _, _, T, payload = oracle.encode(Ah, Bh, final)
+    dt = time.perf_counter() - t0
+    return S, T, hashlib.sha256(payload.tobytes()).hexdigest(), dt
+
+
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
 
 
 def parse():
@@ -73,7 +128,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)  # (about 50 ms timed: enough steps to average out run-to-run spread)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="workload number 1..5 (3 = 8M+8M)")
-    ap.add_argument("--path", choices=("fused", "onepass", "merge", "collision"), default="fused")
+    ap.add_argument("--path", choices=("fused", "onecall", "onepass", "merge", "collision"), default="fused")
     ap.add_argument("--items", type=int, default=0,
                     help="outputs per merge partition (0: chosen from the mean key length)")
     ap.add_argument("--collision-mode", choices=("512", "2048", "512-tiled", "512-compact"),
@@ -81,8 +136,8 @@ def parse():
     ap.add_argument("--coarse-parts", type=int, default=0,
                     help="fused path: partitions per coarse partition (0: library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-scale", type=float, default=0.125,
-                    help="fraction of the workload the CPU oracle is timed on")
+    ap.add_argument("--scale", type=float, default=1.0,
+                    help="fraction of the workload's record counts (parity then comes from the oracle run here)")
     ap.add_argument("--navigation", action="store_true",
                     help="also time em_ef_navigation (the output navigation) on the step's outputs")
     ap.add_argument("--byte-profile", action="store_true",
@@ -123,48 +178,31 @@ def algorithmic_bytes(Ah, Bh, pl, path):
     survivor_key_bytes = int(np.sum(klen))
     value_bytes = int(np.sum(vlen))
     payload = 4 * ((T + 31) // 32)
-    per_rec_meta = 4 + 8 + 4 + 8 + 8 + 1  # final, off, lcp, key_off pair, val_off pair, tomb
     vmeta = 4 * (Ah.n + 1 + Bh.n + 1) + int(Ah.tomb.size + Bh.tomb.size)  # value offsets, tombstones
     out = {
         # merge: every key byte, both offset arrays; writes refs and both ordinal arrays
-        "em_merge_keep": keys + offs + 4 * S + 4 * N,
-        # lengths: survivor refs, their keys (own + predecessor's), offsets, tombs; writes len + lcp
-        "em_fc_lengths": 4 * S + survivor_key_bytes + S * (8 + 8 + 1) + 8 * S,
-        "em_scan": 4 * S + 8 * (S + 1),
-        "em_emit": S * per_rec_meta + suffix_bytes + value_bytes + payload,
+        "em_merge_keep": keys + offs,
+        # lengths: the survivors' keys, offsets and tombstones
+        "em_fc_lengths": survivor_key_bytes + S * (8 + 8 + 1),
+        "em_scan": 0,
+        "em_emit": S * (8 + 8 + 1) + suffix_bytes + value_bytes + payload,
         "em_partition": 0,
-        "em_collision_rank_mode": keys + offs + 4 * S + 4 * N,
+        "em_collision_rank_mode": keys + offs,
         # the whole path: every input byte once, the payload once
         "em_merge_fc": side_bytes(Ah) + side_bytes(Bh) + payload,
         # merge, keep, LCPs, lengths: every key byte, key and value offsets,
-        # tombstones; writes refs, LCPs and partition-form offsets
-        "em_merge_lengths": keys + offs + vmeta + 16 * S,
-        # emission: refs, LCPs, offsets (16 B), key_off and val_off pairs,
-        # tombstone, key suffixes, values; writes the payload
-        "em_emit_merged": S * (16 + 8 + 8 + 1) + suffix_bytes + value_bytes + payload,
+        # tombstones (the references, LCPs and offsets it hands to the
+        # emitter are not counted)
+        "em_merge_lengths": keys + offs + vmeta,
+        # emission: the survivors' key_off and val_off pairs and tombstone
+        # flags, key suffixes and values; writes the payload (the references,
+        # LCPs and offsets it reads from the first kernel are not counted)
+        "em_emit_merged": S * (8 + 8 + 1) + suffix_bytes + value_bytes + payload,
         # the single pass: every key byte, key and value offsets, tombstones,
         # the survivors' value bytes; writes the payload
         "em_merge_fc_onepass": keys + offs + vmeta + value_bytes + payload,
     }
     return out
-
-
-def cpu_baseline(w, scale):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import gen
-    import oracle
-    ws = w.scaled(scale)
-    A, B = gen.make(ws)
-    t0 = time.perf_counter()
-    refs = oracle.merge(A, B)
-    final, _, _, S = oracle.keep(A, B, refs)
-    _, _, _, T, payload = oracle.encode(A, B, final)
-    dt = time.perf_counter() - t0
-    n = A.n + B.n
-    return {"value": n / dt, "unit": "records/s", "cores": 1, "kind": "oracle",
-            "sample": f"{ws.name}: {A.n}+{B.n} records drawn by the same recipe "
-                      f"(scale {scale:g}), merge + keep + bitwise encode, {dt:.2f} s single-threaded",
-            "seconds": dt, "GBps": (side_bytes(A) + side_bytes(B) + len(payload)) / dt / 1e9}
 
 
 def main():
@@ -181,21 +219,39 @@ def main():
     import merge_front_coded_amd as em
 
     w = gen.WORKLOADS[args.workload]
+    if args.scale != 1.0:
+        w = w.scaled(args.scale)
     t_gen = time.perf_counter()
     Ah, Bh = gen.make(w)
     t_gen = time.perf_counter() - t_gen
     print(f"# generated {w.name}: {Ah.n}+{Bh.n} records in {t_gen:.1f}s", file=sys.stderr, flush=True)
     A = em.DeviceSide.from_host(Ah)
     B = em.DeviceSide.from_host(Bh)
-    fused = args.path in ("fused", "onepass")
+    fused = args.path in ("fused", "onecall", "onepass")
     extra = {"coarse_parts": args.coarse_parts} if (fused and args.coarse_parts) else {}
-    if args.path == "collision":
-        extra["collision_mode"] = args.collision_mode
-    if args.path == "onepass":
-        extra["one_pass"] = True
-    pl = em.Pipeline(A, B, items_per_part=args.items or None, path="fused" if fused else args.path,
-                     keep_all=not fused, **extra)
+    pl = make_pipeline(A, B, args.path, args.items, args.coarse_parts, args.collision_mode)
     torch.cuda.synchronize()
+
+    # ---- parity of the timed configuration, before any timing ----
+    pl.run()
+    torch.cuda.synchronize()
+    gpu_sha = payload_digest(pl)
+    ref = reference_digest(args.workload, args.scale)
+    oracle_result = None
+    if ref is not None:
+        parity_src = f"tests/golden/full_size_digests.json[{args.workload}] (S, T, payload SHA-256)"
+    else:
+        print("# running the CPU oracle on the same host buffers for parity", file=sys.stderr, flush=True)
+        oracle_result = oracle_run(Ah, Bh)
+        ref = oracle_result[:3]
+        parity_src = "CPU oracle run on the same host buffers (S, T, payload SHA-256)"
+    if (pl.S, pl.T, gpu_sha) != tuple(ref):
+        print(json.dumps({"error": "parity check failed before timing", "workload": w.name, "path": args.path,
+                          "got": {"S": pl.S, "T": pl.T, "payload_sha256": gpu_sha},
+                          "want": {"S": ref[0], "T": ref[1], "payload_sha256": ref[2]}, "reference": parity_src}),
+              flush=True)
+        sys.exit(3)
+    print(f"# parity ok against {parity_src}", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
         pl.run()
@@ -208,6 +264,7 @@ def main():
     calls = {"merge": ["em_partition", "em_merge_keep", "em_fc_lengths", "em_scan", "em_emit"],
              "collision": ["em_collision_rank_mode", "em_fc_lengths", "em_scan", "em_emit"],
              "fused": ["em_partition", "em_merge_lengths", "em_emit_merged"],
+             "onecall": ["em_partition", "em_merge_fc"],
              "onepass": ["em_partition", "em_merge_fc_onepass"]}[args.path]
     ev = {c: [] for c in calls}
     orig = {c: getattr(em.pipeline.em, c) for c in calls}
@@ -255,7 +312,8 @@ def main():
         torch.cuda.synchronize()
         complete_ms = s0.elapsed_time(e0) / args.steps
         # the per-record arrays, for the algorithmic-byte count only (not timed)
-        pl2 = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True, **extra)
+        pl2 = em.Pipeline(A, B, items_per_part=pl.items, path="fused", keep_all=True,
+                          one_pass=args.path == "onepass", **extra)
         pl2.run()
         torch.cuda.synchronize()
         assert (pl2.S, pl2.T) == (pl.S, pl.T)
@@ -309,9 +367,13 @@ def main():
         "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dominant], "call": dominant, "achieved": ach,
                      "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dominant, args.workload),
+                     "traffic": measured_traffic(dominant, w.name),
                      "algorithmic_bytes_per_launch": alg[dominant],
-                     "avg_launch_ms": per_call_ms[dominant]},
+                     "avg_launch_ms": per_call_ms[dominant],
+                     # the whole step: B_io over the step time
+                     "pipeline": {"achieved": gbps, "frac": gbps / HBM_PEAK_GBPS, "bytes": b_io,
+                                  "ms": ms_per_step}},
+        "parity": {"reference": parity_src, "S": pl.S, "T": pl.T, "payload_sha256": gpu_sha, "match": True},
     }
     if args.navigation:
         # the output navigation built from this step's outputs (the step after
@@ -440,8 +502,20 @@ def main():
         torch.cuda.synchronize()
         result["copy_GBps"] = 2 * n * 10 / (s.elapsed_time(e) * 1e-3) / 1e9
     if not args.no_cpu_baseline:
-        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_scale)
+        if oracle_result is None:
+            print("# timing the CPU oracle on the same host buffers", file=sys.stderr, flush=True)
+            oracle_result = oracle_run(Ah, Bh)
+        oS, oT, osha, dt = oracle_result
+        if (oS, oT, osha) != (pl.S, pl.T, gpu_sha):
+            print(json.dumps({"error": "the CPU oracle's payload differs from the timed GPU payload",
+                              "oracle": {"S": oS, "T": oT, "payload_sha256": osha}}), flush=True)
+            sys.exit(3)
+        result["parity"]["oracle_same_run"] = True
+        result["cpu_baseline"] = {"value": N / dt, "unit": "records/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"the whole timed workload ({w.name}: {Ah.n}+{Bh.n} records, the same "
+                                            f"host buffers as the GPU step): merge + keep-newer + bitwise encode, "
+                                            f"{dt:.1f} s on one thread; payload identical to the GPU's",
+                                  "seconds": dt, "GBps": b_io / dt / 1e9, **host_cpu()}
     print(json.dumps(result), flush=True)
 
 

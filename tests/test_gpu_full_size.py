@@ -1,8 +1,11 @@
 """Full-size parity: every output of the HIP path (and the output navigation
-sections built from it) on the five full-size
-workloads, in the benchmark's launch configuration (the partition size the
-pipeline chooses from the mean key length), against SHA-256 digests of the CPU oracle's outputs written by
+sections built from it) on the five full-size workloads, with the partition
+size the pipeline chooses from the mean key length and every per-record array
+kept (final references, ordinals, lengths, LCPs, offsets), against SHA-256
+digests of the CPU oracle's outputs written by
 tests/golden/make_full_size_digests.py (which calls only gen/ and oracle/).
+The benchmark's own configuration, which keeps none of the per-record arrays,
+is checked in test_gpu_bench_config.py.
 
 A digest covers every element, so this is an element-by-element comparison
 without rerunning the bit-at-a-time oracle on the GPU host.  The input digest

@@ -2,8 +2,8 @@
 accepts.  Three-byte big-endian keys (A: the even numbers below 2^24; B: the
 numbers that are 0 or 1 mod 4, less the last, so that a quarter of all keys is
 in both sides), values of 0..4 bytes, tombstones on B.  Every output of the
-fused path in the bench's launch configuration, of its single-pass variant,
-of the six-call path and of the collision path is compared element by element
+fused path (with its per-record arrays kept), of its single-pass variant, of
+the six-call path and of the collision path is compared element by element
 with the CPU oracle."""
 import numpy as np
 import pytest
