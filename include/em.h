@@ -30,8 +30,10 @@
  *    enqueued.
  *  - Inputs are trusted, not admitted (Everett, "Byte-profile GPU merge",
  *    "Pipeline"): each side must be strictly increasing in unsigned bytewise
- *    order with a proper prefix first.  Unsorted input gives unspecified
- *    output but never out-of-bounds access or a hang.
+ *    order with a proper prefix first.  On input that breaks this the output
+ *    is unspecified and memory safety is not guaranteed (some kernels clamp
+ *    references and partition splits, but not every call is guarded); a
+ *    caller with untrusted input must check its order first.
  *  - Caps (Everett, "GPU construction experiment", the host bound check, and
  *    "Byte-profile GPU merge", "Pipeline"): |A| + |B| < 2^24 records; each
  *    arena < 2^32 bytes (u32 offsets); key and value lengths < 2^27 bytes.

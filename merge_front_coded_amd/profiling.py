@@ -89,6 +89,22 @@ def _counter_rows(d: str):
     return rows
 
 
+def kernel_short_name(name: str) -> str:
+    """A rocprofv3 kernel name without its return type and argument list."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
 def _per_dispatch(rows, counter: str):
     """{kernel name: [value per dispatch]} for one counter (values summed over
     the rows of a dispatch)."""
@@ -96,7 +112,7 @@ def _per_dispatch(rows, counter: str):
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        key = (r["Kernel_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        key = (kernel_short_name(r["Kernel_Name"]), r.get("Dispatch_Id") or r.get("Correlation_Id"))
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
     for (name, _), v in acc.items():
@@ -154,7 +170,7 @@ def write_trace(out_md: str, title: str, stats_csv: str, command: str, top: int 
              "```", command, "```", "",
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in rows[:top]:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        lines.append(f"| `{kernel_short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
     with open(out_md, "w") as fh:
