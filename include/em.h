@@ -190,6 +190,19 @@ int em_scan(const uint32_t *len_bits, uint32_t S, uint64_t *off, void *ws, size_
             void *stream);
 
 /*
+ * em_scan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same scan and result, with the look-back state in a fixed device array of
+ * the library (33,024 bytes per device, held until the process ends) instead
+ * of a workspace.  Allocates nothing.  S must be below EM_MAX_RECORDS
+ * (EM_ERANGE otherwise).  Every call on one device shares that device's
+ * array: calls that overlap on one device (other streams, other host
+ * threads) race and must not be issued; calls in order on one stream are
+ * fine (each clears the state it needs).
+ */
+int em_scan_noalloc(const uint32_t *len_bits, uint32_t S, uint64_t *off, void *stream);
+
+/*
  * Word-owned payload emission (Everett, "GPU construction experiment": every
  * 32-bit output word has a single writer, which collects all of its bits and
  * stores it one time; bits run most significant first; records follow each

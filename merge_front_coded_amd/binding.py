@@ -60,6 +60,7 @@ def load_library(path: str = LIB_PATH):
         "em_rank2048_workspace_bytes": (sz, [u32]),
         "em_fc_lengths": (i32, [S, S, P, u32, P, P, P, sz, P]),
         "em_scan": (i32, [P, u32, P, P, sz, P]),
+        "em_scan_noalloc": (i32, [P, u32, P, P]),
         "em_emit": (i32, [S, S, P, P, u32, P, u64, P, u64, P, sz, P]),
         "em_rank512_probe": (i32, [P, u32, P, u32, P, P, sz, P]),
         "em_merge_fc_workspace_bytes": (sz, [u32, u32, u32]),
@@ -214,6 +215,10 @@ def em_fc_lengths(A, B, final_refs, S, len_bits, lcp_bits, ws, stream=None):
 
 def em_scan(len_bits, S, off, ws, stream=None):
     _check(lib().em_scan(_p(len_bits), S, _p(off), _p(ws), ws.numel(), _stream(stream)), "em_scan")
+
+
+def em_scan_noalloc(len_bits, S, off, stream=None):
+    _check(lib().em_scan_noalloc(_p(len_bits), S, _p(off), _stream(stream)), "em_scan_noalloc")
 
 
 def em_emit(A, B, final_refs, lcp_bits, S, off, T, payload, ws, stream=None):

@@ -6,6 +6,8 @@
 // offsets by one global scan, with no independently encoded chunk resetting
 // the prefix.  The offsets are 64-bit here because the payloads of the large
 // workloads exceed 2^32 bits.
+#include <mutex>
+
 #include "em_internal.h"
 
 namespace em {
@@ -133,4 +135,55 @@ extern "C" int em_scan(const uint32_t* len_bits, uint32_t S, uint64_t* off, void
   if (reinterpret_cast<uintptr_t>(ws) & 255) return EM_EINVAL;
   if (S > 0 && (reinterpret_cast<uintptr_t>(len_bits) & 15)) return EM_EINVAL;
   return scan_launch<uint64_t>(len_bits, S, off, ws, ws_bytes, as_stream(stream));
+}
+
+// ---------------------------------------------------------------------------
+// The same scan with its look-back state in a fixed device array instead of
+// a caller workspace, for callers that cannot allocate.  The array holds the
+// state for the largest S the ABI accepts (2^24 - 1 values: 4096 tiles).
+
+namespace em {
+constexpr size_t kScanScratchBytes = 256 + 4096 * sizeof(uint64_t);
+}  // namespace em
+
+// One copy per device, kept until the process ends.  Host code never uses
+// this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[em::kScanScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current).
+int scan_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return em::set_hip_error(e);
+  if (dev < 0 || dev >= kMaxDevices) return em::set_hip_error(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return em::set_hip_error(e);
+    if (!p) return em::set_hip_error(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EM_OK;
+}
+}  // namespace
+
+extern "C" int em_scan_noalloc(const uint32_t* len_bits, uint32_t S, uint64_t* off, void* stream) {
+  if (!off) return EM_EINVAL;
+  if (S > 0 && !len_bits) return EM_EINVAL;
+  if (S >= EM_MAX_RECORDS) return EM_ERANGE;
+  if (S > 0 && (reinterpret_cast<uintptr_t>(len_bits) & 15)) return EM_EINVAL;
+  if (scan_ws(S) > kScanScratchBytes) return EM_ERANGE;
+  void* ws = nullptr;
+  const int rc = scan_scratch(&ws);
+  if (rc) return rc;
+  return scan_launch<uint64_t>(len_bits, S, off, ws, kScanScratchBytes, as_stream(stream));
 }
