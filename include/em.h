@@ -271,15 +271,21 @@ int em_merge_fc(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_s
 
 /*
  * The whole path in one pass (Everett, "GPU construction experiment": the
- * same steps; each output word is written once): em_merge_fc's arguments
- * and results, but each partition's workgroup also takes its bit base from a
- * second decoupled look-back over the partitions' bit totals and writes its
- * records' payload words itself, in slices of an LDS window, reading the key
- * suffixes and values in place.  The word a partition shares with the next
- * one goes to the workspace and a small second kernel combines the two
- * parts.  final_refs, ord_A, ord_B, len_bits, lcp_bits and off are optional
- * (nullable); the workspace is em_merge_fc_workspace_bytes.
+ * same steps; each output word is written once; the prefix cache holds the
+ * eight key bytes after the common prefix the compared keys share).  One
+ * workgroup per partition of items_per_part (1..1024) merged outputs finds
+ * the partition's co-ranks inside the coarse partition of coarse_splits
+ * (em_partition's output for coarse_items, a multiple of items_per_part),
+ * merges with keep-newer, computes LCPs and exact lengths, takes its survivor
+ * base and its bit base from two decoupled look-backs over the partitions,
+ * and writes its records' payload words itself; a small second kernel writes
+ * the words that partition boundaries cut.  Results as em_merge_fc: the
+ * payload (16-byte aligned, payload_words covering em_payload_bound_bits),
+ * d_S, d_T and the optional (nullable) per-record arrays final_refs, ord_A,
+ * ord_B, len_bits, lcp_bits, off.  ws: em_onepass_workspace_bytes(|A|, |B|,
+ * items_per_part) bytes, 256-byte aligned (about 40 bytes per partition).
  */
+size_t em_onepass_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t items_per_part);
 int em_merge_fc_onepass(const em_side_t *A, const em_side_t *B, const uint32_t *coarse_splits,
                         uint32_t coarse_items, uint32_t items_per_part, uint32_t *payload,
                         uint64_t payload_words, uint32_t *d_S, uint64_t *d_T, uint32_t *final_refs,

@@ -66,6 +66,7 @@ def load_library(path: str = LIB_PATH):
         "em_merge_fc_workspace_bytes": (sz, [u32, u32, u32]),
         "em_merge_fc": (i32, [S, S, P, u32, u32, P, u64, P, P, P, P, P, P, P, P, P, sz, P]),
         "em_merge_fc_onepass": (i32, [S, S, P, u32, u32, P, u64, P, P, P, P, P, P, P, P, P, sz, P]),
+        "em_onepass_workspace_bytes": (sz, [u32, u32, u32]),
         "em_merge_lengths": (i32, [S, S, P, u32, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_emit_merged": (i32, [S, S, u32, P, u64, P, P, P, P, P, P, sz, P]),
         "em_rank512_workspace_bytes": (sz, [u32]),
@@ -255,6 +256,10 @@ def em_merge_fc(A, B, coarse_splits, coarse_items, items_per_part, payload, d_S,
                              _p(d_T), _p(final_refs), _p(ord_A), _p(ord_B), _p(len_bits),
                              _p(lcp_bits), _p(off), _p(ws), ws.numel(), _stream(stream)),
            "em_merge_fc")
+
+
+def em_onepass_workspace_bytes(nA: int, nB: int, items_per_part: int) -> int:
+    return int(lib().em_onepass_workspace_bytes(nA, nB, items_per_part))
 
 
 def em_merge_fc_onepass(A, B, coarse_splits, coarse_items, items_per_part, payload, d_S, d_T, ws,

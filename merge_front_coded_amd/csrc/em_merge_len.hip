@@ -2,10 +2,8 @@
 // merge with keep-newer, exact bit LCPs, record lengths and partition-local
 // bit offsets; (2) one workgroup scans the partitions' bit totals; (3) the
 // word-owned payload emitter, reading the survivor count and payload length
-// the first two left in device memory.  A single-pass variant of kernel 1
-// (kEmit) takes each partition's bit base from a second look-back and writes
-// the partition's payload words itself; a small kernel then writes the words
-// that partition boundaries cut.
+// the first two left in device memory.  (The single-pass form of the whole
+// path is em_onepass.hip.)
 //
 // Everett, "GPU construction experiment": merge by diagonal partitions with
 // ties to the older side; keep the last reference of each equal-key run; the
@@ -45,7 +43,7 @@ struct MlShared {
   static constexpr int kTile = kMlBlock * IPT;
   uint32_t a_off[kTile + 4];  // key offsets of A records aK0 .. i1 (aK0 = i0 - 2 when it exists)
   uint32_t b_off[kTile + 4];  // key offsets of B records bK0 .. j1 (+ the next B)
-  union alignas(16) {  // (single pass: then the output window)
+  union alignas(16) {
     struct {
       uint64_t a_pfx[kTile + 4];  // first 8 bytes of A keys aK0 .., big-endian, zero padded
       uint64_t b_pfx[kTile + 4];  // the same for B keys bK0 ..
@@ -59,57 +57,18 @@ struct MlShared {
   uint64_t scan64[IPT * kMlWaves + 1];
   uint32_t scan32[kMlWaves + 1];
   uint32_t tile, i0, i1, g0;
-  uint64_t b0;  // single pass: the partition's bit base
 };
 
 struct MlOut {
   uint32_t* d_S;
-  uint32_t* final_refs;  // required in two passes, optional in one
-  uint32_t* lcp_bits;    // required in two passes, optional in one
-  uint64_t* toff;        // two passes: partition << kTiledShift | partition-local bit offset
-  uint64_t* tile_bits;   // required: bit total of each partition
-  uint32_t* ord_A;       // optional
-  uint32_t* ord_B;       // optional
-  uint32_t* len_bits;    // optional
-  // single pass only: the payload, bit-base descriptors, each partition's
-  // contributions to the two words it shares with its neighbours, absolute
-  // offsets (optional) and T
-  uint32_t* payload;
-  uint64_t* desc_b;
-  uint32_t* edge_lo;
-  uint32_t* edge_hi;
-  uint64_t* off;
-  uint64_t* d_T;
+  uint32_t* final_refs;
+  uint32_t* lcp_bits;
+  uint64_t* toff;       // partition << kTiledShift | partition-local bit offset
+  uint64_t* tile_bits;  // bit total of each partition
+  uint32_t* ord_A;      // optional
+  uint32_t* ord_B;      // optional
+  uint32_t* len_bits;   // optional
 };
-
-// Record i's bits clipped to [from, to) (relative to its start) appended at
-// window bit `at`: EG0(c), EG0(k - l), key bits [l, k) of the source, the
-// value header, the value bytes (sources read in place as big-endian dword
-// streams).
-struct MlRec {
-  uint32_t c, kl, b1, b2, b3, b4, b5;
-  uint64_t vh, kbit, vbit;
-};
-
-__device__ __forceinline__ void ml_append(uint32_t* win, uint32_t at, const MlRec& r, uint32_t from, uint32_t to,
-                                          const uint32_t* kb, const uint32_t* vb) {
-  BitAppender ap;
-  ap.start(win, at);
-  auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
-    const uint32_t lo = max(a, from), hi = min(b, to);
-    if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
-  };
-  auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
-    const uint32_t lo = max(a, from), hi = min(b, to);
-    if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
-  };
-  imm(static_cast<uint64_t>(r.c) + 1u, 0, r.b1);
-  imm(static_cast<uint64_t>(r.kl) + 1u, r.b1, r.b2);
-  span(kb, r.kbit, r.b2, r.b3);
-  imm(r.vh, r.b3, r.b4);
-  span(vb, r.vbit, r.b4, r.b5);
-  ap.finish();
-}
 
 // Exact bit LCP of two keys from their 8-byte prefixes when these settle it,
 // else from the key bytes after the first 8.
@@ -135,8 +94,8 @@ __device__ __forceinline__ int cmp_from_prefix(uint64_t p, uint64_t q, const uin
 
 // (Six waves per SIMD: three 512-thread partitions per compute unit, which
 // their LDS allows.)
-template <int IPT, bool kEmit>
-__global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(kEmit ? 4 : 6))) void k_merge_len(em_side_t A, em_side_t B,
+template <int IPT>
+__global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_merge_len(em_side_t A, em_side_t B,
                                                         const uint32_t* __restrict__ csplits,
                                                         uint32_t coarse, uint32_t items, uint32_t P,
                                                         MlOut out, uint32_t* __restrict__ ticket,
@@ -373,136 +332,6 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(kEmit 
   for (int u = 0; u < IPT; ++u) rl[u] = rlen[u];
   block_exclusive_scan_rounds<uint64_t, kMlBlock, IPT>(rl, sh.scan64, sb, tile_bits);
 
-  if constexpr (kEmit) {
-    // ---- 8'. single pass: bit base by a second look-back, then the payload ----
-    if (tid == 0) lookback_publish(out.desc_b, tile, tile_bits);
-    // each survivor's control (the rest of its fields is rebuilt per slice,
-    // which costs less than holding it in registers)
-    uint32_t cc[IPT];
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const uint32_t x = tid + u * kMlBlock;
-      cc[u] = x < n_kept ? (((g0 + x) % 15u == 0) ? 1u + l[u] : kprev[u] - l[u]) : 0u;
-    }
-    // optional per-record outputs; the ordinals leave LDS before the window reuses it
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const uint32_t x = tid + u * kMlBlock;
-      if (x >= n_kept) continue;
-      if (out.final_refs) out.final_refs[g0 + x] = sref[u];
-      if (out.lcp_bits) out.lcp_bits[g0 + x] = l[u];
-      if (out.len_bits) out.len_bits[g0 + x] = rlen[u];
-    }
-    if (out.ord_A)
-      for (uint32_t x = tid; x < nA_t; x += kMlBlock) {
-        const uint32_t o = sh.u.c.ords[x];
-        out.ord_A[i0 + x] = o == EM_NONE ? EM_NONE : g0 + o;
-      }
-    if (out.ord_B)
-      for (uint32_t y = tid; y < nB_t; y += kMlBlock) out.ord_B[j0 + y] = g0 + sh.u.c.ords[nA_t + y];
-    if (tid < kWave) {
-      const uint64_t b = lookback_resolve(out.desc_b, tile, tile_bits);
-      if (tid == 0) sh.b0 = b;
-    }
-    __syncthreads();
-    // (workgroup-uniform: kept in scalar registers)
-    // (readfirstlane returns an int: each half goes through uint32_t, so
-    // that a low half of 2^31 or more does not sign-extend into the high one)
-    auto uni64 = [](uint64_t v) {
-      const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
-      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
-      return (static_cast<uint64_t>(hi) << 32) | lo;
-    };
-    const uint64_t Bp = uni64(sh.b0), end = Bp + uni64(tile_bits);
-    if (out.off)
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const uint32_t x = tid + u * kMlBlock;
-        if (x < n_kept) out.off[g0 + x] = Bp + sb[u];
-      }
-    if (tid == 0) {
-      out.tile_bits[tile] = tile_bits;
-      if (tile == P - 1) {
-        out.d_S[0] = g0 + n_kept;
-        out.d_T[0] = end;
-        if (out.off) out.off[g0 + n_kept] = end;
-      }
-    }
-    // The partition writes the words that start and end inside its bits;
-    // its bits in its first and last word go to edge_lo / edge_hi, and
-    // k_edge_fix writes every word that a partition boundary (or T) cuts.
-    const uint64_t wf = Bp >> 5, wl = tile_bits ? (end - 1) >> 5 : wf;
-    const uint64_t dlo = (Bp & 31u) ? wf + 1 : wf, dhi = tile_bits ? ((end & 31u) ? wl : wl + 1) : wf;
-    if (tid == 0) {
-      out.edge_lo[tile] = 0;
-      out.edge_hi[tile] = 0;
-    }
-    uint32_t* win = reinterpret_cast<uint32_t*>(&sh.u);
-    constexpr uint32_t kWin = 4 * Sh::kTile;  // window words (the prefix cache's LDS)
-    const uint32_t* kbA = reinterpret_cast<const uint32_t*>(A.keys);
-    const uint32_t* kbB = reinterpret_cast<const uint32_t*>(B.keys);
-    const uint32_t* vbA = reinterpret_cast<const uint32_t*>(A.vals);
-    const uint32_t* vbB = reinterpret_cast<const uint32_t*>(B.vals);
-    for (uint64_t s0 = (Bp >> 7) << 7; s0 < end; s0 += 32ull * kWin) {
-      const uint64_t s1 = min(s0 + 32ull * kWin, end);
-      const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
-      __syncthreads();  // (the previous slice's copy-out, or the LCP phase, is done with the LDS)
-      for (uint32_t i = tid; i < used4; i += kMlBlock) reinterpret_cast<uint4*>(win)[i] = uint4{0, 0, 0, 0};
-      __syncthreads();
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const uint32_t x = tid + u * kMlBlock;
-        if (x >= n_kept) continue;
-        const uint64_t ro = Bp + sb[u], re = ro + rlen[u];
-        if (ro >= s1 || re <= s0) continue;
-        const uint32_t from = ro >= s0 ? 0u : static_cast<uint32_t>(s0 - ro);
-        const uint32_t to = re <= s1 ? rlen[u] : static_cast<uint32_t>(s1 - ro);
-        // the record's fields again (key from LDS, value from the offsets
-        // read before, now in cache): holding them in registers through the
-        // look-back and the slices spilled
-        const uint32_t ref = sref[u];
-        const bool isB = ref >= A.n;
-        const uint32_t idx = isB ? ref - A.n : ref;
-        const uint32_t* vo = isB ? B.val_off : A.val_off;
-        const uint8_t* tb = isB ? B.tomb : A.tomb;
-        const uint32_t q0 = vo[idx], q1 = vo[idx + 1];
-        const bool t = tb != nullptr && tb[idx] != 0;
-        const uint32_t vl = t ? 0u : q1 - q0;
-        const KeyRef xk = key_at(ref);
-        MlRec r;
-        const uint32_t ev = eg0_len(vl);
-        r.c = cc[u];
-        r.kl = 8u * xk.len - l[u];
-        r.b1 = eg0_len(r.c);
-        r.b2 = r.b1 + eg0_len(r.kl);
-        r.b3 = r.b2 + r.kl;
-        r.b4 = r.b3 + (t ? 1u : 1u + ev);
-        r.b5 = rlen[u];
-        r.vh = t ? 0ull : ((1ull << ev) | (static_cast<uint64_t>(vl) + 1ull));
-        r.kbit = 8ull * xk.pos + l[u];
-        r.vbit = 8ull * q0;
-        ml_append(win, static_cast<uint32_t>(ro + from - s0), r, from, to, isB ? kbB : kbA, isB ? vbB : vbA);
-      }
-      __syncthreads();
-      const uint64_t wbase = s0 >> 5, wend = (s1 + 31) >> 5;
-      auto wv = [&](uint64_t w) { return __builtin_bswap32(win[static_cast<uint32_t>(w - wbase)]); };
-      if (tid == 0 && wf >= wbase && wf < wend) out.edge_lo[tile] = wv(wf);
-      if (tid == 0 && wl >= wbase && wl < wend) out.edge_hi[tile] = wv(wl);
-      const uint64_t o_lo = max(dlo, wbase), o_hi = min(dhi, wend);
-      if (o_lo < o_hi) {
-        const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
-        for (uint64_t w = o_lo + tid; w < a_lo; w += kMlBlock) out.payload[w] = wv(w);
-        for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kMlBlock) {
-          const uint4 v = reinterpret_cast<const uint4*>(win)[static_cast<uint32_t>(w - wbase) / 4];
-          *reinterpret_cast<uint4*>(out.payload + w) = uint4{__builtin_bswap32(v.x), __builtin_bswap32(v.y),
-                                                             __builtin_bswap32(v.z), __builtin_bswap32(v.w)};
-        }
-        for (uint64_t w = a_hi + tid; w < o_hi; w += kMlBlock) out.payload[w] = wv(w);
-      }
-    }
-    return;
-  }
-
   // ---- 8. outputs ----
   const uint64_t tag = static_cast<uint64_t>(tile) << kTiledShift;
 #pragma unroll
@@ -569,36 +398,6 @@ __global__ __launch_bounds__(kTsBlock) void k_tile_scan(const uint64_t* __restri
   if (tid == 0) d_T[0] = total;
 }
 
-// Single pass: the words that a partition boundary, or the end of the
-// payload, cuts.  Thread q (1 <= q <= P; boundary P is T) takes the word W
-// holding boundary q when it is the first boundary inside W: W is the last
-// word of the previous partition with bits, f, and the first word of the
-// partitions starting inside W; W = f's bits there | theirs (an empty
-// partition contributes none).
-__device__ __forceinline__ uint64_t ml_start(const uint64_t* desc_b, const uint64_t* tile_bits, uint32_t r) {
-  return (desc_b[r] & kDescValue) - tile_bits[r];
-}
-
-__global__ __launch_bounds__(256) void k_edge_fix(const uint64_t* __restrict__ desc_b,
-                                                  const uint64_t* __restrict__ tile_bits,
-                                                  const uint32_t* __restrict__ edge_lo,
-                                                  const uint32_t* __restrict__ edge_hi, uint32_t P,
-                                                  uint32_t* __restrict__ payload) {
-  const uint32_t q = blockIdx.x * 256 + threadIdx.x;
-  if (q == 0 || q > P) return;
-  if (q < P && tile_bits[q] == 0) return;  // (the next partition with bits, or T, has the same boundary)
-  const uint64_t Bq = q < P ? ml_start(desc_b, tile_bits, q) : (desc_b[P - 1] & kDescValue);
-  if ((Bq & 31u) == 0) return;
-  uint32_t f = q - 1;
-  while (f > 0 && tile_bits[f] == 0) --f;
-  if (tile_bits[f] == 0) return;  // (no bits before Bq; then Bq = 0)
-  const uint64_t W = Bq >> 5;
-  if (ml_start(desc_b, tile_bits, f) > 32 * W) return;  // f starts inside W: its own boundary takes W
-  uint32_t v = edge_hi[f];
-  for (uint32_t r = q; r < P && ml_start(desc_b, tile_bits, r) < 32 * (W + 1); ++r) v |= edge_lo[r];
-  payload[W] = v;
-}
-
 struct MlLayout {
   uint32_t* ticket;  // [0]: partition ticket of k_merge_len; from [kEmitCtrStride]: the emitter's counters
   uint64_t* desc_s;
@@ -607,9 +406,6 @@ struct MlLayout {
   uint32_t* refs;  // used when the caller passes no final_refs
   uint32_t* lcp;   // used when the caller passes no lcp_bits
   uint64_t* toff;
-  uint64_t* desc_b;  // single pass: bit-base look-back
-  uint32_t* edge_lo;
-  uint32_t* edge_hi;
 };
 
 MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
@@ -623,35 +419,31 @@ MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
   L.refs = cur.take<uint32_t>(N ? N : 1);
   L.lcp = cur.take<uint32_t>(N ? N : 1);
   L.toff = cur.take<uint64_t>(N ? N : 1);
-  L.desc_b = cur.take<uint64_t>(P ? P : 1);
-  L.edge_lo = cur.take<uint32_t>(P ? P : 1);
-  L.edge_hi = cur.take<uint32_t>(P ? P : 1);
   return L;
 }
 
 size_t ml_ws_bytes(uint32_t N, uint32_t items) {
   const size_t P = items ? (static_cast<size_t>(N) + items - 1) / items : 0;
   const size_t p = P ? P : 1, n = N ? N : 1;
-  return align_up((kEmitCtrStride + kEmitCtrWords) * 4, 256) + 4 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) +
-         align_up(n * 8, 256) + 2 * align_up(p * 4, 256);
+  return align_up((kEmitCtrStride + kEmitCtrWords) * 4, 256) + 3 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) +
+         align_up(n * 8, 256);
 }
 
-template <int IPT, bool kEmit>
+template <int IPT>
 static void launch_ml(const em_side_t& A, const em_side_t& B, const uint32_t* csplits, uint32_t coarse,
                       uint32_t items, uint32_t P, const MlOut& o, const MlLayout& L, hipStream_t st) {
-  hipLaunchKernelGGL((k_merge_len<IPT, kEmit>), dim3(P), dim3(kMlBlock), 0, st, A, B, csplits, coarse, items, P,
+  hipLaunchKernelGGL((k_merge_len<IPT>), dim3(P), dim3(kMlBlock), 0, st, A, B, csplits, coarse, items, P,
                      o, L.ticket, L.desc_s);
 }
 
-template <bool kEmit>
 static void launch_ml_items(const em_side_t& A, const em_side_t& B, const uint32_t* csplits, uint32_t coarse,
                             uint32_t items, uint32_t P, const MlOut& o, const MlLayout& L, hipStream_t st) {
   if (items <= static_cast<uint32_t>(kMlBlock))
-    launch_ml<1, kEmit>(A, B, csplits, coarse, items, P, o, L, st);
+    launch_ml<1>(A, B, csplits, coarse, items, P, o, L, st);
   else if (items <= 2u * kMlBlock)
-    launch_ml<2, kEmit>(A, B, csplits, coarse, items, P, o, L, st);
+    launch_ml<2>(A, B, csplits, coarse, items, P, o, L, st);
   else
-    launch_ml<4, kEmit>(A, B, csplits, coarse, items, P, o, L, st);
+    launch_ml<4>(A, B, csplits, coarse, items, P, o, L, st);
 }
 
 }  // namespace em
@@ -664,7 +456,7 @@ extern "C" size_t em_merge_fc_workspace_bytes(uint32_t nA, uint32_t nB, uint32_t
                      items_per_part ? items_per_part : 1);
 }
 
-// Checks shared by the three entry points below.
+// Checks shared by the entry points below.
 static int ml_check(const em_side_t* A, const em_side_t* B, uint32_t items_per_part, const void* ws,
                     size_t ws_bytes) {
   int rc = check_pair(A, B);
@@ -695,8 +487,8 @@ extern "C" int em_merge_lengths(const em_side_t* A, const em_side_t* B, const ui
   const MlLayout L = ml_layout(ws, N, items_per_part);
   clear_lookback(L.ticket, kEmitCtrStride + kEmitCtrWords, L.desc_s, nullptr, P, st);
   MlOut o{d_S, final_refs ? final_refs : L.refs, lcp_bits ? lcp_bits : L.lcp, L.toff, L.tile_bits,
-          ord_A, ord_B, len_bits, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
-  launch_ml_items<false>(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);
+          ord_A, ord_B, len_bits};
+  launch_ml_items(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);
   hipLaunchKernelGGL(k_tile_scan, dim3(1), dim3(kTsBlock), 0, st, L.tile_bits, P, L.tbase, d_T);
   return check_launch();
 }
@@ -743,38 +535,4 @@ extern "C" int em_merge_fc(const em_side_t* A, const em_side_t* B, const uint32_
   if (rc) return rc;
   return em_emit_merged(A, B, items_per_part, payload, payload_words, d_S, d_T, final_refs, lcp_bits, off, ws,
                         ws_bytes, stream);
-}
-
-extern "C" int em_merge_fc_onepass(const em_side_t* A, const em_side_t* B, const uint32_t* coarse_splits,
-                                   uint32_t coarse_items, uint32_t items_per_part, uint32_t* payload,
-                                   uint64_t payload_words, uint32_t* d_S, uint64_t* d_T, uint32_t* final_refs,
-                                   uint32_t* ord_A, uint32_t* ord_B, uint32_t* len_bits, uint32_t* lcp_bits,
-                                   uint64_t* off, void* ws, size_t ws_bytes, void* stream) {
-  int rc = ml_check(A, B, items_per_part, ws, ws_bytes);
-  if (rc) return rc;
-  if (!payload || !coarse_splits || !d_S || !d_T) return EM_EINVAL;
-  if (reinterpret_cast<uintptr_t>(payload) & 15) return EM_EINVAL;
-  if (coarse_items == 0 || coarse_items % items_per_part || coarse_items > EM_MAX_ITEMS_PER_PART * 256u)
-    return EM_EINVAL;
-  uint64_t bound = 0;
-  rc = em_payload_bound_bits(A, B, &bound);
-  if (rc) return rc;
-  if (payload_words < (bound + 31) / 32) return EM_ENOSPC;
-  hipStream_t st = as_stream(stream);
-  const uint32_t N = A->n + B->n;
-  if (N == 0) {
-    clear_u32(d_S, 1, st);
-    clear_u64(d_T, 1, st);
-    if (off) clear_u64(off, 1, st);
-    return check_launch();
-  }
-  const uint32_t P = (N + items_per_part - 1) / items_per_part;
-  const MlLayout L = ml_layout(ws, N, items_per_part);
-  clear_lookback(L.ticket, 1, L.desc_s, L.desc_b, P, st);
-  MlOut o{d_S, final_refs, lcp_bits, nullptr, L.tile_bits, ord_A, ord_B, len_bits,
-          payload, L.desc_b, L.edge_lo, L.edge_hi, off, d_T};
-  launch_ml_items<true>(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);
-  hipLaunchKernelGGL(k_edge_fix, dim3(P / 256 + 1), dim3(256), 0, st, L.desc_b, L.tile_bits, L.edge_lo,
-                     L.edge_hi, P, payload);
-  return check_launch();
 }

@@ -70,9 +70,10 @@ __device__ __forceinline__ uint32_t merge_slice_exact(const uint32_t* a_off, con
                                                 const uint8_t* bbase, uint32_t b_adj, uint32_t k,
                                                 uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                 bool has_next_b, uint32_t i0, uint32_t nA_all,
-                                                uint32_t j0, uint32_t (&refs)[IPT]) {
+                                                uint32_t j0, uint32_t (&refs)[IPT], uint32_t cp = 0) {
   // Prefix first; zero padding plus the lengths keep proper-prefix order exact
-  // (Everett, "GPU construction experiment", prefix-cache paragraph).
+  // (Everett, "GPU construction experiment", prefix-cache paragraph).  The
+  // cached 8 bytes start cp bytes into every key, all keys sharing those cp.
   // Returns false when the suffixes must decide.
   auto quick = [&](uint32_t a, uint32_t b, int& c) -> bool {
     const uint64_t pa = a_pfx[a], pb = b_pfx[b];
@@ -82,12 +83,12 @@ __device__ __forceinline__ uint32_t merge_slice_exact(const uint32_t* a_off, con
     }
     const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
     c = (la > lb) - (la < lb);
-    return la <= 8 || lb <= 8;
+    return la <= cp + 8 || lb <= cp + 8;
   };
   auto suffix = [&](uint32_t a, uint32_t b) -> int {
     const uint32_t pa = a_off[a], pb = b_off[b];
-    return cmp_keys(abase, KeyRef{pa - a_adj + 8, a_off[a + 1] - pa - 8}, bbase,
-                    KeyRef{pb - b_adj + 8, b_off[b + 1] - pb - 8});
+    return cmp_keys(abase, KeyRef{pa - a_adj + cp + 8, a_off[a + 1] - pa - cp - 8}, bbase,
+                    KeyRef{pb - b_adj + cp + 8, b_off[b + 1] - pb - cp - 8});
   };
 #pragma unroll
   for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
@@ -207,7 +208,8 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
                                                      const uint8_t* bbase, uint32_t b_adj, uint32_t k,
                                                      uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                      bool has_next_b, uint32_t i0, uint32_t nA_all,
-                                                     uint32_t j0, uint32_t (&refs)[IPT], bool& bad) {
+                                                     uint32_t j0, uint32_t (&refs)[IPT], bool& bad,
+                                                     uint32_t cp = 0) {
   constexpr int kNotes = 4;
   uint32_t note[kNotes];  // noted pairs, A index | B index << 16
 #pragma unroll
@@ -220,15 +222,15 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
     const uint64_t pa = a_pfx[a], pb = b_pfx[b];
     const uint32_t la = a_off[a + 1] - a_off[a], lb = b_off[b + 1] - b_off[b];
     const bool peq = pa == pb;
-    const int cp = pa < pb ? -1 : 1;
+    const int cpfx = pa < pb ? -1 : 1;
     const int cl = (la > lb) - (la < lb);
-    const bool open = use & peq & (la > 8u) & (lb > 8u);
+    const bool open = use & peq & (la > cp + 8u) & (lb > cp + 8u);
     open_pair |= open & (la != lb);
     const uint32_t v = a | (b << 16);
 #pragma unroll
     for (int q = 0; q < kNotes; ++q) note[q] = (open & (nnote == static_cast<uint32_t>(q))) ? v : note[q];
     nnote += open ? 1u : 0u;
-    return open ? 0 : (peq ? cl : cp);
+    return open ? 0 : (peq ? cl : cpfx);
   };
 #pragma unroll
   for (int s = 0; s < IPT; ++s) refs[s] = kDrop;
@@ -277,8 +279,8 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
       if (ok && static_cast<uint32_t>(q) < nnote) {
         const uint32_t x = note[q] & 0xFFFFu, y = note[q] >> 16;
         const uint32_t px = a_off[x], py = b_off[y];
-        ok = cmp_keys(abase, KeyRef{px - a_adj + 8, a_off[x + 1] - px - 8}, bbase,
-                      KeyRef{py - b_adj + 8, b_off[y + 1] - py - 8}) == 0;
+        ok = cmp_keys(abase, KeyRef{px - a_adj + cp + 8, a_off[x + 1] - px - cp - 8}, bbase,
+                      KeyRef{py - b_adj + cp + 8, b_off[y + 1] - py - cp - 8}) == 0;
       }
     }
   }
@@ -296,13 +298,13 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
                                                 const uint8_t* bbase, uint32_t b_adj, uint32_t k,
                                                 uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                 bool has_next_b, uint32_t i0, uint32_t nA_all,
-                                                uint32_t j0, uint32_t (&refs)[IPT]) {
+                                                uint32_t j0, uint32_t (&refs)[IPT], uint32_t cp = 0) {
   bool bad;
   uint32_t kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len,
-                                        nA_t, nB_t, has_next_b, i0, nA_all, j0, refs, bad);
+                                        nA_t, nB_t, has_next_b, i0, nA_all, j0, refs, bad, cp);
   if (__syncthreads_or(bad))
     kept = merge_slice_exact<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
-                                  nB_t, has_next_b, i0, nA_all, j0, refs);
+                                  nB_t, has_next_b, i0, nA_all, j0, refs, cp);
   return kept;
 }
 

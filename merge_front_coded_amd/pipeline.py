@@ -8,8 +8,9 @@ Paths:
   fused      partition -> merge_lengths (merge, keep, LCPs, lengths, bit
              offsets) -> emit_merged (the emitter); S and T stay on the
              device.  one_call=True runs the same work as em_merge_fc;
-             one_pass=True runs em_merge_fc_onepass (each partition emits
-             its own words).
+             one_pass=True runs partition -> em_merge_fc_onepass (each
+             partition emits its own words; 512 outputs per partition,
+             whose co-ranks em_partition finds).
 All buffers are allocated once up front (sized from em_workspace_bytes and
 em_payload_bound_bits) and reused by every run.
 """
@@ -34,6 +35,13 @@ def choose_items_per_part(A: em.DeviceSide, B: em.DeviceSide) -> int:
 _FUSE_COARSE_PARTS = 1
 
 
+def choose_onepass_items(A: em.DeviceSide, B: em.DeviceSide) -> int:
+    """Partition size of the single pass: 512 outputs (four 256-thread
+    workgroups, 40 KB of LDS each, share a compute unit), 256 for inputs too
+    small to give every compute unit partitions."""
+    return 512 if A.n + B.n >= 512 * 512 else 256
+
+
 def choose_fused_items(A: em.DeviceSide, B: em.DeviceSide) -> int:
     """Partition size of em_merge_fc's first kernel (at most 2048 outputs; the
     same choice as the merge path)."""
@@ -48,7 +56,10 @@ class Pipeline:
         if path not in ("merge", "collision", "fused"):
             raise ValueError("path is 'merge', 'collision' or 'fused'")
         self.A, self.B = A, B
-        if path == "fused":
+        if path == "fused" and one_pass:
+            self.items = int(items_per_part) if items_per_part else choose_onepass_items(A, B)
+            self.coarse = self.items * coarse_parts
+        elif path == "fused":
             self.items = int(items_per_part) if items_per_part else choose_fused_items(A, B)
             self.coarse = self.items * coarse_parts
         else:
@@ -79,6 +90,8 @@ class Pipeline:
         ws_bytes = em.em_workspace_bytes(A.n, B.n, min(self.items, 4096))
         if path == "fused":
             ws_bytes = max(ws_bytes, em.em_merge_fc_workspace_bytes(A.n, B.n, self.items))
+            if one_pass:
+                ws_bytes = max(ws_bytes, em.em_onepass_workspace_bytes(A.n, B.n, self.items))
         if path == "collision":
             ws_bytes = max(ws_bytes, em.em_collision_workspace_bytes(A.n, B.n, self.collision_mode))
         self.ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=device)

@@ -151,7 +151,7 @@ def test_onepass_argument_errors(lib):
     buf = ctypes.c_void_p(0x100000)
     ws = ctypes.c_void_p(0x100000)
     # partition sizes, coarse splits that are not a multiple, a misaligned payload, no splits
-    for items, coarse in ((0, 256), (2049, 4098), (64, 100)):
+    for items, coarse in ((0, 256), (1025, 2050), (64, 100)):
         assert lib.em_merge_fc_onepass(ctypes.byref(A), ctypes.byref(B), buf, coarse, items, buf, 1 << 20, buf,
                                        buf, None, None, None, None, None, None, ws, 1 << 20, None) == -1
     assert lib.em_merge_fc_onepass(ctypes.byref(A), ctypes.byref(B), buf, 64, 64, ctypes.c_void_p(0x100008),
