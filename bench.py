@@ -51,7 +51,7 @@ KERNEL_OF = {"em_partition": "k_partition", "em_merge_keep": "k_merge_keep", "em
              "em_scan": "k_scan", "em_emit": "k_emit",
              "em_collision_rank_mode": "k_mark, rank build, scatter or compact + merge",
              "em_merge_lengths": "k_merge_len + k_tile_scan", "em_emit_merged": "k_emit",
-             "em_merge_fc_onepass": "k_merge_len<4, true> + k_edge_fix",
+             "em_merge_fc_onepass": "k_onepass + k_op_edges",
              "em_merge_fc": "k_merge_len + k_tile_scan + k_emit"}
 
 
@@ -198,9 +198,8 @@ def algorithmic_bytes(Ah, Bh, pl, path):
         # flags, key suffixes and values; writes the payload (the references,
         # LCPs and offsets it reads from the first kernel are not counted)
         "em_emit_merged": S * (8 + 8 + 1) + suffix_bytes + value_bytes + payload,
-        # the single pass: every key byte, key and value offsets, tombstones,
-        # the survivors' value bytes; writes the payload
-        "em_merge_fc_onepass": keys + offs + vmeta + value_bytes + payload,
+        # the single pass: every input byte once, the payload once
+        "em_merge_fc_onepass": side_bytes(Ah) + side_bytes(Bh) + payload,
     }
     return out
 

@@ -16,17 +16,19 @@
 //  * co-ranks of the partition's two diagonals, searched inside the coarse
 //    partition that coarse_splits gives (read directly when the coarse
 //    partitions are the partitions);
-//  * the partition's key offsets and each key's first 8 bytes go to LDS,
+//  * the partition's key offsets and 8 bytes of each key go to LDS,
 //    including the two A keys and the B key before the partition (for its
 //    first survivor's predecessor) and the B key after it (for an equal pair
-//    split by the boundary); key bytes stay in HBM;
+//    split by the boundary): the first 8 bytes, or, when all those keys share
+//    a common prefix of 8 bytes or more, the 8 bytes after it (the pages'
+//    prefix cache); key bytes stay in HBM;
 //  * merge and keep as in em_merge_keep; the survivor count is published to
 //    a decoupled look-back right away and resolved after the LCPs (the global
 //    survivor index fixes the W15 phase of c_i);
 //  * each survivor's exact bit LCP with its predecessor comes from the two
-//    8-byte prefixes when they differ or a key is at most 8 bytes long, and
-//    from the key bytes in HBM otherwise; value lengths and tombstone flags
-//    are read while the LCPs run;
+//    cached words when they differ or a key ends inside them, and from the
+//    key bytes in HBM otherwise; value lengths and tombstone flags are read
+//    while the LCPs run;
 //  * lengths, a block scan into partition-local bit offsets, and the
 //    partition's bit total.  A survivor's offset is stored with its
 //    partition number; the emitter adds the partition's bit base.
@@ -56,7 +58,7 @@ struct MlShared {
   } u;
   uint64_t scan64[IPT * kMlWaves + 1];
   uint32_t scan32[kMlWaves + 1];
-  uint32_t tile, i0, i1, g0;
+  uint32_t tile, i0, i1, g0, cp;
 };
 
 struct MlOut {
@@ -69,28 +71,6 @@ struct MlOut {
   uint32_t* ord_B;      // optional
   uint32_t* len_bits;   // optional
 };
-
-// Exact bit LCP of two keys from their 8-byte prefixes when these settle it,
-// else from the key bytes after the first 8.
-__device__ __forceinline__ uint32_t lcp_from_prefix(uint64_t p, uint64_t q, const uint8_t* pb, KeyRef pk,
-                                                    const uint8_t* qb, KeyRef qk) {
-  const uint32_t m = pk.len < qk.len ? pk.len : qk.len;
-  if (p != q) {
-    const uint32_t d = static_cast<uint32_t>(__builtin_clzll(p ^ q));
-    return d < 8u * m ? d : 8u * m;
-  }
-  if (m <= 8) return 8u * m;
-  return 64u + lcp_bits(pb, KeyRef{pk.pos + 8, pk.len - 8}, qb, KeyRef{qk.pos + 8, qk.len - 8});
-}
-
-// Key order from prefixes and lengths, with the key bytes in HBM when the
-// prefixes tie and both keys are longer than 8 bytes.
-__device__ __forceinline__ int cmp_from_prefix(uint64_t p, uint64_t q, const uint8_t* pb, KeyRef pk,
-                                               const uint8_t* qb, KeyRef qk) {
-  if (p != q) return p < q ? -1 : 1;
-  if (pk.len <= 8 || qk.len <= 8) return (pk.len > qk.len) - (pk.len < qk.len);
-  return cmp_keys(pb, KeyRef{pk.pos + 8, pk.len - 8}, qb, KeyRef{qk.pos + 8, qk.len - 8});
-}
 
 // (Six waves per SIMD: three 512-thread partitions per compute unit, which
 // their LDS allows.)
@@ -155,9 +135,10 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   }
   __syncthreads();
 
-  // ---- 3. prefix cache of every key whose offsets are in LDS (all loads,
-  // then all stores) ----
-  {
+  // ---- 3. prefix cache of every key whose offsets are in LDS: 8 bytes at
+  // offset 0, or after the common prefix of all of them when that is at
+  // least 8 bytes long (all loads, then all stores) ----
+  auto load_cache = [&](uint32_t cp) {
     constexpr int kPer = IPT + 1;  // ceil((kTile + 3) / kMlBlock)
     uint64_t pa[kPer], pb[kPer];
 #pragma unroll
@@ -165,12 +146,12 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
       const uint32_t x = tid + u * kMlBlock;
       pa[u] = pb[u] = 0;
       if (x + 1 < na_off) {
-        const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
-        pa[u] = load_be8(A.keys, p0) & be_mask(ln < 8 ? ln : 8);
+        const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0 - cp;
+        pa[u] = load_be8(A.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
       }
       if (x + 1 < nb_off) {
-        const uint32_t p0 = sh.b_off[x], ln = sh.b_off[x + 1] - p0;
-        pb[u] = load_be8(B.keys, p0) & be_mask(ln < 8 ? ln : 8);
+        const uint32_t p0 = sh.b_off[x], ln = sh.b_off[x + 1] - p0 - cp;
+        pb[u] = load_be8(B.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
       }
     }
 #pragma unroll
@@ -179,8 +160,15 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
       if (x + 1 < na_off) sh.u.m.a_pfx[x] = pa[u];
       if (x + 1 < nb_off) sh.u.m.b_pfx[x] = pb[u];
     }
-  }
+  };
+  load_cache(0);
   __syncthreads();
+  const uint32_t cp = cache_offset(sh.a_off, na_off - 1, sh.b_off, nb_off - 1, sh.u.m.a_pfx, sh.u.m.b_pfx, A.keys,
+                                   B.keys, &sh.cp);
+  if (cp) {  // (uniform)
+    load_cache(cp);
+    __syncthreads();
+  }
 
   const uint32_t* ao = sh.a_off + a_first;  // A[i0 + x] is key [ao[x], ao[x+1])
   const uint32_t* bo = sh.b_off + b_first;  // B[j0 + y] is key [bo[y], bo[y+1])
@@ -191,7 +179,7 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
   const uint32_t kept = merge_slice<IPT>(ao, bo, apf, bpf, A.keys, 0u, B.keys, 0u, k, len, nA_t, nB_t,
-                                         has_next_b, i0, A.n, j0, refs);
+                                         has_next_b, i0, A.n, j0, refs, cp);
   // prefixes of this thread's outputs, and (thread 0) of the keys before the
   // partition, read before the compaction arrays overwrite the cache
   uint64_t opfx[IPT];
@@ -268,7 +256,7 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
     if (x > 0) {
       const uint32_t pref = sh.u.c.surv[x - 1];
       const KeyRef pk = key_at(pref);
-      l[u] = lcp_from_prefix(sh.u.c.spfx[x - 1], xp, pref >= A.n ? B.keys : A.keys, pk, xb, xk);
+      l[u] = lcp_cached(sh.u.c.spfx[x - 1], xp, cp, pref >= A.n ? B.keys : A.keys, pk, xb, xk);
       kprev[u] = 8u * pk.len;
     } else if (d0 > 0) {
       // The largest surviving key before the partition: A[i0-1] unless it is
@@ -281,7 +269,7 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
         ka = KeyRef{sh.a_off[a_first - 1], sh.a_off[a_first] - sh.a_off[a_first - 1]};
         pa = pa1;
         hA = true;
-        if (cmp_from_prefix(pa, xp, A.keys, ka, xb, xk) == 0) {
+        if (cmp_cached(pa, xp, cp, A.keys, ka, xb, xk) == 0) {
           hA = a_first >= 2;
           if (hA) {
             ka = KeyRef{sh.a_off[a_first - 2], sh.a_off[a_first - 1] - sh.a_off[a_first - 2]};
@@ -295,9 +283,9 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
         hB = true;
       }
       if (hA || hB) {
-        const bool use_a = hA && (!hB || cmp_from_prefix(pa, pbx, A.keys, ka, B.keys, kb) > 0);
+        const bool use_a = hA && (!hB || cmp_cached(pa, pbx, cp, A.keys, ka, B.keys, kb) > 0);
         const KeyRef pk = use_a ? ka : kb;
-        l[u] = lcp_from_prefix(use_a ? pa : pbx, xp, use_a ? A.keys : B.keys, pk, xb, xk);
+        l[u] = lcp_cached(use_a ? pa : pbx, xp, cp, use_a ? A.keys : B.keys, pk, xb, xk);
         kprev[u] = 8u * pk.len;
       }
     }

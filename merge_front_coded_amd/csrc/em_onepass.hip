@@ -104,28 +104,6 @@ struct OpOut {
   uint64_t* off;
 };
 
-// Exact bit LCP of two keys that share their first cp bytes, from the 8
-// cached bytes at cp when these settle it, else from the key bytes after them.
-__device__ __forceinline__ uint32_t lcp_cached(uint64_t p, uint64_t q, uint32_t cp, const uint8_t* pb, KeyRef pk,
-                                               const uint8_t* qb, KeyRef qk) {
-  const uint32_t m = pk.len < qk.len ? pk.len : qk.len;  // >= cp
-  if (p != q) {
-    const uint32_t d = 8u * cp + static_cast<uint32_t>(__builtin_clzll(p ^ q));
-    return d < 8u * m ? d : 8u * m;
-  }
-  if (m <= cp + 8) return 8u * m;
-  return 8u * (cp + 8) + lcp_bits(pb, KeyRef{pk.pos + cp + 8, pk.len - cp - 8}, qb,
-                                  KeyRef{qk.pos + cp + 8, qk.len - cp - 8});
-}
-
-// Key order of two keys that share their first cp bytes.
-__device__ __forceinline__ int cmp_cached(uint64_t p, uint64_t q, uint32_t cp, const uint8_t* pb, KeyRef pk,
-                                          const uint8_t* qb, KeyRef qk) {
-  if (p != q) return p < q ? -1 : 1;
-  if (pk.len <= cp + 8 || qk.len <= cp + 8) return (pk.len > qk.len) - (pk.len < qk.len);
-  return cmp_keys(pb, KeyRef{pk.pos + cp + 8, pk.len - cp - 8}, qb, KeyRef{qk.pos + cp + 8, qk.len - cp - 8});
-}
-
 // ---------------------------------------------------------------------------
 // Window writers.  The window holds output words in big-endian bit order and
 // starts zeroed; words that also hold bits of another field or record are
@@ -379,40 +357,9 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
   };
   load_cache(0);
   __syncthreads();
-  // Every cached key lies between the smallest and the largest of them, so
-  // all share the leading bytes that the first and last keys of each side
-  // and the two first keys share (the minimum of those three LCPs).
-  const uint32_t nka = na_off - 1, nkb = nb_off - 1;  // cached keys per side
-  if (tid == 0) {
-    bool all8 = nka + nkb > 0;
-    auto share8 = [&](uint64_t p, uint32_t lp, uint64_t q, uint32_t lq) { return p == q && lp >= 8 && lq >= 8; };
-    const uint32_t la0 = nka ? sh.a_off[1] - sh.a_off[0] : 0, laz = nka ? sh.a_off[nka] - sh.a_off[nka - 1] : 0;
-    const uint32_t lb0 = nkb ? sh.b_off[1] - sh.b_off[0] : 0, lbz = nkb ? sh.b_off[nkb] - sh.b_off[nkb - 1] : 0;
-    if (nka) all8 = all8 && share8(sh.u.m.a_pfx[0], la0, sh.u.m.a_pfx[nka - 1], laz);
-    if (nkb) all8 = all8 && share8(sh.u.m.b_pfx[0], lb0, sh.u.m.b_pfx[nkb - 1], lbz);
-    if (nka && nkb) all8 = all8 && share8(sh.u.m.a_pfx[0], la0, sh.u.m.b_pfx[0], lb0);
-    sh.cp = all8 ? 0xFFFFFFFFu : 0u;
-  }
-  __syncthreads();
-  uint32_t cp = __builtin_amdgcn_readfirstlane(sh.cp);
-  if (cp) {  // (uniform) the cached keys share at least 8 bytes: find how many
-    __syncthreads();
-    if (tid < 3) {
-      uint32_t l = 0xFFFFFFFFu;
-      if (tid == 0 && nka) {
-        l = lcp_bits(A.keys, KeyRef{sh.a_off[0], sh.a_off[1] - sh.a_off[0]}, A.keys,
-                     KeyRef{sh.a_off[nka - 1], sh.a_off[nka] - sh.a_off[nka - 1]});
-      } else if (tid == 1 && nkb) {
-        l = lcp_bits(B.keys, KeyRef{sh.b_off[0], sh.b_off[1] - sh.b_off[0]}, B.keys,
-                     KeyRef{sh.b_off[nkb - 1], sh.b_off[nkb] - sh.b_off[nkb - 1]});
-      } else if (tid == 2 && nka && nkb) {
-        l = lcp_bits(A.keys, KeyRef{sh.a_off[0], sh.a_off[1] - sh.a_off[0]}, B.keys,
-                     KeyRef{sh.b_off[0], sh.b_off[1] - sh.b_off[0]});
-      }
-      atomicMin(&sh.cp, l >> 3);
-    }
-    __syncthreads();
-    cp = __builtin_amdgcn_readfirstlane(sh.cp);
+  const uint32_t cp = cache_offset(sh.a_off, na_off - 1, sh.b_off, nb_off - 1, sh.u.m.a_pfx, sh.u.m.b_pfx, A.keys,
+                                   B.keys, &sh.cp);
+  if (cp) {  // (uniform) the cached keys share cp >= 8 bytes: cache the 8 after them
     load_cache(cp);
     __syncthreads();
   }

@@ -308,6 +308,69 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
   return kept;
 }
 
+// Exact bit LCP of two keys that share their first cp bytes, from the 8
+// cached bytes at cp when these settle it, else from the key bytes after them.
+__device__ __forceinline__ uint32_t lcp_cached(uint64_t p, uint64_t q, uint32_t cp, const uint8_t* pb, KeyRef pk,
+                                               const uint8_t* qb, KeyRef qk) {
+  const uint32_t m = pk.len < qk.len ? pk.len : qk.len;  // >= cp
+  if (p != q) {
+    const uint32_t d = 8u * cp + static_cast<uint32_t>(__builtin_clzll(p ^ q));
+    return d < 8u * m ? d : 8u * m;
+  }
+  if (m <= cp + 8) return 8u * m;
+  return 8u * (cp + 8) + lcp_bits(pb, KeyRef{pk.pos + cp + 8, pk.len - cp - 8}, qb,
+                                  KeyRef{qk.pos + cp + 8, qk.len - cp - 8});
+}
+
+// Key order of two keys that share their first cp bytes.
+__device__ __forceinline__ int cmp_cached(uint64_t p, uint64_t q, uint32_t cp, const uint8_t* pb, KeyRef pk,
+                                          const uint8_t* qb, KeyRef qk) {
+  if (p != q) return p < q ? -1 : 1;
+  if (pk.len <= cp + 8 || qk.len <= cp + 8) return (pk.len > qk.len) - (pk.len < qk.len);
+  return cmp_keys(pb, KeyRef{pk.pos + cp + 8, pk.len - cp - 8}, qb, KeyRef{qk.pos + cp + 8, qk.len - cp - 8});
+}
+
+// Where the prefix cache of a partition should start (Everett, "GPU
+// construction experiment", prefix-cache paragraph: the cached bytes follow
+// the common prefix the compared keys are known to share).  Every cached key
+// lies between the smallest and the largest of them, so all share the leading
+// bytes that the first and last cached keys of each side and the two first
+// keys share: the minimum of those three LCPs.  Returns 0 unless those keys
+// agree in their first 8 cached bytes (a_pfx / b_pfx, loaded at offset 0),
+// else that common prefix in whole bytes, measured from the key bytes.
+// a_off / b_off hold the na + 1 / nb + 1 offsets of the cached keys.  Every
+// thread calls it; `flag` is a word of LDS.
+__device__ __forceinline__ uint32_t cache_offset(const uint32_t* a_off, uint32_t na, const uint32_t* b_off,
+                                                 uint32_t nb, const uint64_t* a_pfx, const uint64_t* b_pfx,
+                                                 const uint8_t* akeys, const uint8_t* bkeys, uint32_t* flag) {
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) {
+    bool all8 = na + nb > 0;
+    auto share8 = [](uint64_t p, uint32_t lp, uint64_t q, uint32_t lq) { return p == q && lp >= 8 && lq >= 8; };
+    const uint32_t la0 = na ? a_off[1] - a_off[0] : 0, laz = na ? a_off[na] - a_off[na - 1] : 0;
+    const uint32_t lb0 = nb ? b_off[1] - b_off[0] : 0, lbz = nb ? b_off[nb] - b_off[nb - 1] : 0;
+    if (na) all8 = all8 && share8(a_pfx[0], la0, a_pfx[na - 1], laz);
+    if (nb) all8 = all8 && share8(b_pfx[0], lb0, b_pfx[nb - 1], lbz);
+    if (na && nb) all8 = all8 && share8(a_pfx[0], la0, b_pfx[0], lb0);
+    *flag = all8 ? 0xFFFFFFFFu : 0u;
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(*flag) == 0) return 0;  // (uniform)
+  __syncthreads();
+  if (tid < 3) {
+    uint32_t l = 0xFFFFFFFFu;
+    if (tid == 0 && na)
+      l = lcp_bits(akeys, KeyRef{a_off[0], a_off[1] - a_off[0]}, akeys, KeyRef{a_off[na - 1], a_off[na] - a_off[na - 1]});
+    else if (tid == 1 && nb)
+      l = lcp_bits(bkeys, KeyRef{b_off[0], b_off[1] - b_off[0]}, bkeys, KeyRef{b_off[nb - 1], b_off[nb] - b_off[nb - 1]});
+    else if (tid == 2 && na && nb)
+      l = lcp_bits(akeys, KeyRef{a_off[0], a_off[1] - a_off[0]}, bkeys, KeyRef{b_off[0], b_off[1] - b_off[0]});
+    atomicMin(flag, l >> 3);
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*flag);
+}
+
 // Appends bits MSB-first at consecutive output positions inside the current
 // slice window.  Positions are relative to the slice's first bit.
 struct BitAppender {

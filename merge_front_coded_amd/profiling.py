@@ -29,16 +29,14 @@ CSRC = os.path.join(PKG, "csrc")
 CALL_SOURCES = {
     "em_emit_merged": ("em_fc.hip", "em_tile.h", "em_internal.h"),
     "em_merge_lengths": ("em_merge_len.hip", "em_tile.h", "em_internal.h"),
-    "em_merge_fc_onepass": ("em_merge_len.hip", "em_tile.h", "em_internal.h"),
-    "em_merge_fc_stream": ("em_stream.hip", "em_tile.h", "em_internal.h"),
+    "em_merge_fc_onepass": ("em_onepass.hip", "em_tile.h", "em_internal.h"),
 }
 
 # The kernel (name prefix in the rocprofv3 output) behind each call's traffic.
 CALL_KERNEL = {
     "em_emit_merged": "em::k_emit<true, true, true>",
     "em_merge_lengths": "em::k_merge_len<",
-    "em_merge_fc_onepass": "em::k_merge_len<4, true>",
-    "em_merge_fc_stream": "em::k_stream<",
+    "em_merge_fc_onepass": "em::k_onepass<",
 }
 
 
