@@ -9,7 +9,8 @@ measuring it again.
 
 Usage (from the repository root, after rocprofv3 runs that wrote CSV files):
 
-  python -m merge_front_coded_amd.profiling traffic OUT.md WORKLOAD FETCH_DIR WRITE_DIR "COMMAND"
+  python -m merge_front_coded_amd.profiling traffic OUT.md WORKLOAD FETCH_DIRS WRITE_DIRS "COMMANDS"
+  (FETCH_DIRS / WRITE_DIRS: comma-separated rocprofv3 output directories)
   python -m merge_front_coded_amd.profiling trace OUT.md "TITLE" STATS_CSV "COMMAND"
 """
 from __future__ import annotations
@@ -78,12 +79,16 @@ def measured_traffic(call: str, workload_name: str) -> int | None:
     return None
 
 
-def _counter_rows(d: str):
-    """Rows of every rocprofv3 counter-collection CSV under directory d."""
+def _counter_rows(dirs: str):
+    """Rows of every rocprofv3 counter-collection CSV under the directories
+    (comma-separated)."""
     rows = []
-    for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
-        with open(p, newline="") as f:
-            rows.extend(csv.DictReader(f))
+    for d in dirs.split(","):
+        for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(p, newline="") as f:
+                for r in csv.DictReader(f):
+                    r["_file"] = p  # dispatch ids repeat across runs
+                    rows.append(r)
     return rows
 
 
@@ -110,10 +115,10 @@ def _per_dispatch(rows, counter: str):
     for r in rows:
         if r.get("Counter_Name") != counter:
             continue
-        key = (kernel_short_name(r["Kernel_Name"]), r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        key = (kernel_short_name(r["Kernel_Name"]), r.get("_file"), r.get("Dispatch_Id") or r.get("Correlation_Id"))
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     out = {}
-    for (name, _), v in acc.items():
+    for (name, _, _), v in acc.items():
         out.setdefault(name, []).append(v)
     return out
 
