@@ -49,6 +49,7 @@ struct MergeShared {
     } c;
   } u;
   uint32_t scan[kMergeBlock / kWave + 1];
+  uint32_t notes[kMergeBlock];  // the merge's list of pairs to check, kWave words per wave
   uint32_t tile, base;
 };
 
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
   const uint32_t kept = merge_slice<IPT>(sh.a_off, sh.b_off, sh.u.m.a_pfx, sh.u.m.b_pfx, A.keys, 0u, B.keys,
-                                         0u, k, len, nA_t, nB_t, has_next_b, i0, A.n, j0, refs);
+                                         0u, k, len, nA_t, nB_t, has_next_b, i0, A.n, j0, refs, sh.notes);
 
   // ---- keep scan inside the partition (its barriers end every read of the
   // prefix cache, which the compaction arrays then reuse) ----

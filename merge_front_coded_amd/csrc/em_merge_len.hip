@@ -58,6 +58,7 @@ struct MlShared {
   } u;
   uint64_t scan64[IPT * kMlWaves + 1];
   uint32_t scan32[kMlWaves + 1];
+  uint32_t notes[kMlBlock];  // the merge's list of pairs to check, kWave words per wave
   uint32_t tile, i0, i1, g0, cp;
 };
 
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
   const uint32_t kept = merge_slice<IPT>(ao, bo, apf, bpf, A.keys, 0u, B.keys, 0u, k, len, nA_t, nB_t,
-                                         has_next_b, i0, A.n, j0, refs, cp);
+                                         has_next_b, i0, A.n, j0, refs, sh.notes, cp);
   // prefixes of this thread's outputs, and (thread 0) of the keys before the
   // partition, read before the compaction arrays overwrite the cache
   uint64_t opfx[IPT];

@@ -82,6 +82,7 @@ struct OpShared {
   uint64_t scan64[IPT * kOpWaves + 1];
   uint64_t red[3 * kOpWaves];  // look-back reductions
   uint32_t scan32[kOpWaves + 1];
+  uint32_t notes[kOpBlock];  // the merge's list of pairs to check, kWave words per wave
   uint32_t tile, i0, i1, g0, cp, carry;
   uint32_t span_lo[4], span_hi[4], stage_at[5];  // A keys, B keys, A values, B values
   uint64_t base;          // the partition's bit base
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
   const uint32_t kept = merge_slice<IPT>(ao, bo, apf, bpf, A.keys, 0u, B.keys, 0u, k, len, nA_t, nB_t, has_next_b,
-                                         i0, A.n, j0, refs, cp);
+                                         i0, A.n, j0, refs, sh.notes, cp);
   // cached bytes of this thread's outputs and of the keys before the
   // partition, read before the compaction arrays overwrite the cache
   uint64_t opfx[IPT];

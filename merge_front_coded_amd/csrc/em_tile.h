@@ -209,7 +209,7 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
                                                      uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                      bool has_next_b, uint32_t i0, uint32_t nA_all,
                                                      uint32_t j0, uint32_t (&refs)[IPT], bool& bad,
-                                                     uint32_t cp = 0) {
+                                                     uint32_t* wave_list, uint32_t cp = 0) {
   constexpr int kNotes = 4;
   uint32_t note[kNotes];  // noted pairs, A index | B index << 16
 #pragma unroll
@@ -271,18 +271,47 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
     b += (live && c > 0) ? 1u : 0u;
   }
 
-  // check the pairs taken as equal, the whole wave together
+  // Check the pairs taken as equal.  The wave's noted pairs are listed in
+  // LDS (wave_list, kWave entries of this wave's own) and each lane takes
+  // one, so that the key loads of up to 64 pairs are in flight together: one
+  // memory round trip for the wave, instead of one per note of its busiest
+  // lane.  A lane whose own notes already fail lists none.
   bool ok = !open_pair && nnote <= static_cast<uint32_t>(kNotes);
   if (__ballot(nnote != 0) != 0) {
+    const uint32_t nn = ok ? nnote : 0u;  // < 8: three bits
+    const uint64_t lt = (1ull << __lane_id()) - 1ull;
+    uint32_t pre = 0, tot = 0;
 #pragma unroll
-    for (int q = 0; q < kNotes; ++q) {
-      if (ok && static_cast<uint32_t>(q) < nnote) {
-        const uint32_t x = note[q] & 0xFFFFu, y = note[q] >> 16;
-        const uint32_t px = a_off[x], py = b_off[y];
-        ok = cmp_keys(abase, KeyRef{px - a_adj + cp + 8, a_off[x + 1] - px - cp - 8}, bbase,
-                      KeyRef{py - b_adj + cp + 8, b_off[y + 1] - py - cp - 8}) == 0;
-      }
+    for (int bit = 0; bit < 3; ++bit) {
+      const uint64_t m = __ballot((nn >> bit) & 1u);
+      pre += static_cast<uint32_t>(__popcll(m & lt)) << bit;
+      tot += static_cast<uint32_t>(__popcll(m)) << bit;
     }
+    bool fail = false;
+    for (uint32_t base = 0; base < tot; base += kWave) {  // (wave-uniform)
+#pragma unroll
+      for (int q = 0; q < kNotes; ++q) {
+        const uint32_t at = pre + static_cast<uint32_t>(q);
+        if (static_cast<uint32_t>(q) < nn && at >= base && at < base + kWave) wave_list[at - base] = note[q];
+      }
+      // (LDS accesses of one wave are performed in program order; the
+      // fences keep the compiler from moving them across each other)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (base + __lane_id() < tot) {
+        const uint32_t v = wave_list[__lane_id()];
+        const uint32_t x = v & 0xFFFFu, y = v >> 16;
+        const uint32_t px = a_off[x], py = b_off[y];
+        // (a listed pair has equal lengths: a pair of different lengths set open_pair)
+        fail |= cmp_keys(abase, KeyRef{px - a_adj + cp + 8, a_off[x + 1] - px - cp - 8}, bbase,
+                         KeyRef{py - b_adj + cp + 8, b_off[y + 1] - py - cp - 8}) != 0;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    ok = ok && __ballot(fail) == 0;
   }
   bad = !ok;
   return kept;
@@ -290,7 +319,8 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
 
 // The merge of a workgroup's partition: every thread calls it (threads past
 // the partition's end get kDrop refs and a zero count).  Exact whichever
-// branch runs.
+// branch runs.  `notes` is LDS scratch of kWave words per wave of the
+// workgroup.
 template <int IPT>
 __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
                                                 const uint64_t* a_pfx, const uint64_t* b_pfx,
@@ -298,10 +328,12 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
                                                 const uint8_t* bbase, uint32_t b_adj, uint32_t k,
                                                 uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                 bool has_next_b, uint32_t i0, uint32_t nA_all,
-                                                uint32_t j0, uint32_t (&refs)[IPT], uint32_t cp = 0) {
+                                                uint32_t j0, uint32_t (&refs)[IPT], uint32_t* notes,
+                                                uint32_t cp = 0) {
   bool bad;
-  uint32_t kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len,
-                                        nA_t, nB_t, has_next_b, i0, nA_all, j0, refs, bad, cp);
+  uint32_t kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
+                                        nB_t, has_next_b, i0, nA_all, j0, refs, bad,
+                                        notes + (threadIdx.x / kWave) * kWave, cp);
   if (__syncthreads_or(bad))
     kept = merge_slice_exact<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
                                   nB_t, has_next_b, i0, nA_all, j0, refs, cp);
