@@ -274,18 +274,14 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
     } else {
       ok = true;
       vn = r.tomb ? 0u : r.vlen;
-      if (staged) {
-        const uint32_t q = r.isB ? 1u : 0u;
-        if (r.sfx) {
-          atomicMin(&sh.span_lo[q], r.kpos);
-          atomicMax(&sh.span_hi[q], r.kpos + r.sfx);
-        }
-        if (vn) {
-          atomicMin(&sh.span_lo[2 + q], r.vpos);
-          atomicMax(&sh.span_hi[2 + q], r.vpos + vn);
-        }
-      }
     }
+  }
+  if (staged) {  // (uniform) a side's records are in arena order: see span_widen
+    const bool ks = ok && r.sfx != 0, vs = ok && vn != 0;
+    span_widen(ks && !r.isB, r.kpos, r.kpos + r.sfx, &sh.span_lo[0], &sh.span_hi[0]);
+    span_widen(ks && r.isB, r.kpos, r.kpos + r.sfx, &sh.span_lo[1], &sh.span_hi[1]);
+    span_widen(vs && !r.isB, r.vpos, r.vpos + vn, &sh.span_lo[2], &sh.span_hi[2]);
+    span_widen(vs && r.isB, r.vpos, r.vpos + vn, &sh.span_lo[3], &sh.span_hi[3]);
   }
   if (!staged) {  // (uniform)
     if (ok)

@@ -275,18 +275,17 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
   }
   __syncthreads();
   // the source spans: the owned records', and those of the records after them
-  // that start inside the last owned word (usually one)
-  if (active && (j < nown || rec_off < 32ull * ((sh.bit_hi + 31) >> 5))) {
-    const uint32_t q = isB ? 1u : 0u;
-    const uint32_t klo = kpos + (l >> 3);
-    if (klo < kpos + klen) {
-      atomicMin(&sh.span_lo[q], klo);
-      atomicMax(&sh.span_hi[q], kpos + klen);
-    }
-    if (vlen) {
-      atomicMin(&sh.span_lo[2 + q], vpos);
-      atomicMax(&sh.span_hi[2 + q], vpos + vlen);
-    }
+  // that start inside the last owned word (usually one); a side's records
+  // are in arena order, so each span runs from its first record's bytes to
+  // its last record's
+  {
+    const bool src = active && (j < nown || rec_off < 32ull * ((sh.bit_hi + 31) >> 5));
+    const uint32_t klo = kpos + (l >> 3), khi = kpos + klen;
+    const bool ks = src && klo < khi, vs = src && vlen != 0;
+    span_widen(ks && !isB, klo, khi, &sh.span_lo[0], &sh.span_hi[0]);
+    span_widen(ks && isB, klo, khi, &sh.span_lo[1], &sh.span_hi[1]);
+    span_widen(vs && !isB, vpos, vpos + vlen, &sh.span_lo[2], &sh.span_hi[2]);
+    span_widen(vs && isB, vpos, vpos + vlen, &sh.span_lo[3], &sh.span_hi[3]);
   }
   __syncthreads();
   if (tid == 0) {

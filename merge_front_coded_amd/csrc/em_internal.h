@@ -115,6 +115,24 @@ __device__ __forceinline__ uint32_t eg0_len(uint64_t x) {
   return 2u * (63u - static_cast<uint32_t>(__builtin_clzll(x + 1))) + 1u;
 }
 
+// Widens a workgroup's byte span [*span_lo, *span_hi) (LDS) to cover the
+// ranges [lo, hi) of this wave's selected lanes, for ranges that increase
+// with the lane (a later selected lane's lo and hi are at least an earlier
+// one's, as for the records of one side in merged order): the first
+// selected lane holds the smallest lo and the last the largest hi, so one lane
+// each updates the bounds.  (An LDS atomic from every lane on the same word
+// is serialised by the LDS, one lane per cycle.)  Every lane of the wave
+// calls it.
+__device__ __forceinline__ void span_widen(bool sel, uint32_t lo, uint32_t hi, uint32_t* span_lo,
+                                           uint32_t* span_hi) {
+  const uint64_t m = __ballot(sel);
+  if (m) {
+    const uint32_t lane = __lane_id();
+    if (lane == static_cast<uint32_t>(__builtin_ctzll(m))) atomicMin(span_lo, lo);
+    if (lane == 63u - static_cast<uint32_t>(__builtin_clzll(m))) atomicMax(span_hi, hi);
+  }
+}
+
 // gfx950 global -> LDS load without registers: each active lane moves 16
 // bytes from `src` (per lane) to `lds_wave_base` + 16 * lane, where
 // `lds_wave_base` is the same for the whole wave.  The caller waits for the

@@ -555,13 +555,14 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
     const uint32_t x0 = ch * cs, x1 = min(x0 + cs, n_kept);
     // this thread's survivor in the chunk, if any (at most one of its slots)
     bool act = false;
-    uint32_t ref = 0, lc = 0, ctl = 0, rl = 0;
+    uint32_t ref = 0, lc = 0, ctl = 0, rl = 0, slot = 0;
     uint64_t lo = 0;
 #pragma unroll
     for (int v = 0; v < IPT; ++v) {
       const uint32_t xv = tid + v * kOpBlock;
       const bool in = xv >= x0 && xv < x1;
       act |= in;
+      slot = in ? static_cast<uint32_t>(v) : slot;
       ref = in ? sref[v] : ref;
       lc = in ? l[v] : lc;
       ctl = in ? cc[v] : ctl;
@@ -584,13 +585,19 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
     }
     __syncthreads();  // (also: every read of the compaction arrays is done)
     const uint32_t ksl = xk.pos + (lc >> 3);  // first key byte the record emits
-    if (act && ksl < xk.pos + xk.len) {
-      atomicMin(&sh.span_lo[isB ? 1 : 0], ksl);
-      atomicMax(&sh.span_hi[isB ? 1 : 0], xk.pos + xk.len);
-    }
-    if (act && vlen) {
-      atomicMin(&sh.span_lo[isB ? 3 : 2], vpos);
-      atomicMax(&sh.span_hi[isB ? 3 : 2], vpos + vlen);
+    {
+      // Lanes holding the same slot v have survivors in lane order, and a
+      // side's survivors are in arena order: per slot, the first and last
+      // such lane bound each span.
+      const bool ks = act && ksl < xk.pos + xk.len, vs = act && vlen != 0;
+#pragma unroll
+      for (int v = 0; v < IPT; ++v) {
+        const bool in = slot == static_cast<uint32_t>(v);
+        span_widen(in && ks && !isB, ksl, xk.pos + xk.len, &sh.span_lo[0], &sh.span_hi[0]);
+        span_widen(in && ks && isB, ksl, xk.pos + xk.len, &sh.span_lo[1], &sh.span_hi[1]);
+        span_widen(in && vs && !isB, vpos, vpos + vlen, &sh.span_lo[2], &sh.span_hi[2]);
+        span_widen(in && vs && isB, vpos, vpos + vlen, &sh.span_lo[3], &sh.span_hi[3]);
+      }
     }
     __syncthreads();
     if (tid == 0) {
