@@ -121,23 +121,30 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
       // this record's bits inside [s0, s1), relative to the record start
       const uint32_t from = r.off >= s0 ? 0u : static_cast<uint32_t>(s0 - r.off);
       const uint32_t to = r.end <= s1 ? r.b5 : static_cast<uint32_t>(s1 - r.off);
-      BitAppender ap;
-      ap.start(sh.out, static_cast<uint32_t>(r.off + from - s0));
-      // EG0(c), EG0(k-l), presence + EG0(value length): immediates
-      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field occupying [a, b)
+      // Each field, clipped to the slice, goes straight to its own position
+      // in the window: EG0(c) EG0(k-l) (one 64-bit field when they fit), the
+      // key suffix, presence + EG0(value length), the value bytes.
+      const uint32_t p0 = static_cast<uint32_t>(r.off + from - s0);  // window bit of record bit `from`
+      auto imm = [&](uint64_t v, uint32_t a, uint32_t b) {  // field of b - a <= 64 bits at [a, b)
         const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) ap.put64((v >> (b - hi)) & (hi - lo == 64 ? ~0ull : ((1ull << (hi - lo)) - 1)), hi - lo);
+        if (lo < hi) {
+          const uint64_t x = (v >> (b - hi)) & (hi - lo == 64u ? ~0ull : ((1ull << (hi - lo)) - 1ull));
+          if (x) or_bits64(sh.out, p0 + (lo - from), x, hi - lo);
+        }
       };
       auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
         const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) put_span(ap, base, bp + (lo - a), hi - lo);
+        if (lo < hi) or_span(sh.out, p0 + (lo - from), base, bp + (lo - a), hi - lo);
       };
-      imm(static_cast<uint64_t>(r.c) + 1u, 0, r.b1);
-      imm(static_cast<uint64_t>(r.k - r.l) + 1u, r.b1, r.b2);
+      if (r.b2 <= 64u) {
+        imm((static_cast<uint64_t>(r.c) + 1u) << (r.b2 - r.b1) | (static_cast<uint64_t>(r.k - r.l) + 1u), 0, r.b2);
+      } else {
+        imm(static_cast<uint64_t>(r.c) + 1u, 0, r.b1);
+        imm(static_cast<uint64_t>(r.k - r.l) + 1u, r.b1, r.b2);
+      }
       span(kbase, r.kbit, r.b2, r.b3);
       imm(r.vh, r.b3, r.b4);
       span(vbase, r.vbit, r.b4, r.b5);
-      ap.finish();
     }
     if (s0 == wb && tid == 0) sh.next = ticket;
     __syncthreads();

@@ -403,57 +403,6 @@ __device__ __forceinline__ uint32_t cache_offset(const uint32_t* a_off, uint32_t
   return __builtin_amdgcn_readfirstlane(*flag);
 }
 
-// Appends bits MSB-first at consecutive output positions inside the current
-// slice window.  Positions are relative to the slice's first bit.
-struct BitAppender {
-  uint32_t* out;
-  uint32_t w;      // word being filled
-  uint32_t fill;   // bits already in it
-  uint32_t acc;
-  bool shared;     // the word being filled also holds another record's bits
-
-  __device__ __forceinline__ void start(uint32_t* o, uint32_t pos) {
-    out = o;
-    w = pos >> 5;
-    fill = pos & 31u;
-    acc = 0;
-    shared = fill != 0;
-  }
-  __device__ __forceinline__ void store_full() {
-    if (shared)
-      atomicOr(out + w, acc);
-    else
-      out[w] = acc;
-    ++w;
-    acc = 0;
-    shared = false;
-  }
-  // n in 1..32, bits right-aligned
-  __device__ __forceinline__ void put(uint32_t bits, uint32_t n) {
-    const uint32_t space = 32u - fill;
-    if (n < space) {
-      acc |= bits << (space - n);
-      fill += n;
-      return;
-    }
-    const uint32_t rem = n - space;
-    acc |= rem ? bits >> rem : bits;
-    store_full();
-    acc = rem ? bits << (32u - rem) : 0u;
-    fill = rem;
-  }
-  __device__ __forceinline__ void put64(uint64_t v, uint32_t n) {  // n in 0..64
-    if (n > 32) {
-      put(static_cast<uint32_t>(v >> 32) & (0xFFFFFFFFu >> (64u - n)), n - 32);
-      n = 32;
-    }
-    if (n) put(static_cast<uint32_t>(v) & (0xFFFFFFFFu >> (32u - n)), n);
-  }
-  __device__ __forceinline__ void finish() {
-    if (fill) atomicOr(out + w, acc);  // the last word is shared with the next record
-  }
-};
-
 // 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
 __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
   const uint32_t* p = base + (bp >> 5);
@@ -463,30 +412,22 @@ __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp)
   return sh ? __builtin_amdgcn_alignbit(hi, lo, 32u - sh) : hi;
 }
 
-// Appends source bits [bp, bp + n) of a dword array.  The output word being
-// filled (fill f) is completed from the first source bits; every later
-// output word starts f bits before a 32-bit boundary of the remaining source,
-// so it is one funnel shift of two consecutive source dwords with a shift
-// that is the same for the whole span.  Reads reach at most one dword past
-// the one holding the span's last bit.
-__device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, uint64_t bp, uint32_t n) {
-  const uint32_t f = ap.fill;
-  if (f + n < 32u) {  // stays inside the word being filled
-    if (n) ap.put(bits32_at(base, bp) >> (32u - n), n);
-    return;
-  }
-  const uint32_t W = (f + n) >> 5, f2 = (f + n) & 31u;  // completed words, fill afterwards
-  const uint32_t v0 = ap.acc | (bits32_at(base, bp) >> f);
-  if (ap.shared)
-    atomicOr(ap.out + ap.w, v0);
-  else
-    ap.out[ap.w] = v0;
-  // output word i >= 1 holds source bits [P, P + 32) with P = bp + 32 i - f
-  // (P >= 1): bits of dwords (P - 1) / 32 and the next, shifted right by -P
-  // mod 32 (a shift of 0 gives the second dword).
+// Source bits [bp, bp + n) of a dword array placed at an output position
+// that is f bits into output word o[0] (the caller writes o[0] itself, from
+// the first 32 - f source bits):
+// output word i >= 1 holds source bits [P, P + 32) with P = bp + 32 i - f,
+// so every one of them is one funnel shift of two consecutive source dwords
+// with a shift that is the same for the whole span.  Words 1 .. W-1 are
+// stored; the bits of the partial word W (when f2 = (f + n) mod 32 > 0) are
+// returned.  Reads reach at most one dword past the one holding the span's
+// last bit.
+__device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base, uint64_t bp, uint32_t f,
+                                               uint32_t W, uint32_t f2) {
+  // P >= 1: bits of dwords (P - 1) / 32 and the next, shifted right by -P
+  // mod 32 (a shift of 0 gives the second dword)
   const uint32_t* p = base + ((bp + 31u - f) >> 5);
   const uint32_t sh = (f - static_cast<uint32_t>(bp)) & 31u;
-  uint32_t* o = ap.out + ap.w + 1;
+  o += 1;
   const uint32_t cnt = W - 1;  // words 1 .. W-1 go to o[0 .. cnt)
   uint32_t cur = __builtin_bswap32(p[0]);
   uint32_t t = 0;
@@ -499,9 +440,9 @@ __device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, 
     o[t + 3] = __builtin_amdgcn_alignbit(n3, n4, sh);
     cur = n4;
   }
-  // up to three more words, then the partial word left in the accumulator
-  // (source dwords t+1 .. t+rem, and one more when f2 > 0; indices past the
-  // last one needed re-read it)
+  // up to three more words, then the partial word (source dwords t+1 ..
+  // t+rem, and one more when f2 > 0; indices past the last one needed re-read
+  // it)
   const uint32_t rem = cnt - t;
   const uint32_t last = t + rem + (f2 ? 1u : 0u);
   const uint32_t m1 = __builtin_bswap32(p[min(t + 1, last)]), m2 = __builtin_bswap32(p[min(t + 2, last)]);
@@ -515,10 +456,41 @@ __device__ __forceinline__ void put_span(BitAppender& ap, const uint32_t* base, 
     const uint32_t y = rem == 0 ? m1 : rem == 1 ? m2 : rem == 2 ? m3 : m4;
     acc = __builtin_amdgcn_alignbit(x, y, sh) & ~(0xFFFFFFFFu >> f2);
   }
-  ap.w += W;
-  ap.fill = f2;
-  ap.acc = acc;
-  ap.shared = false;
+  return acc;
+}
+
+// Direct placement into a window that is zero wherever nothing has been
+// written yet: the n low bits of v (1 <= n <= 64), MSB first, at bit p.
+// Every word is ORed (other fields and records may share them).
+__device__ __forceinline__ void or_bits64(uint32_t* out, uint32_t p, uint64_t v, uint32_t n) {
+  const uint32_t f = p & 31u;
+  uint32_t* o = out + (p >> 5);
+  const uint64_t u = v << (64u - n);  // left-aligned
+  const uint32_t hi = static_cast<uint32_t>(u >> 32), lo = static_cast<uint32_t>(u);
+  atomicOr(o, hi >> f);
+  if (f + n > 32u) atomicOr(o + 1, __builtin_amdgcn_alignbit(hi, lo, f));  // (a shift of 0 gives lo)
+  if (f + n > 64u) atomicOr(o + 2, lo << (32u - f));                      // (f > 0 here)
+}
+
+// Direct placement of source bits [bp, bp + n) of a dword array at window bit
+// p: the first and the last word, which neighbouring fields may share, are
+// ORed, and every word between them is stored.
+__device__ __forceinline__ void or_span(uint32_t* out, uint32_t p, const uint32_t* base, uint64_t bp, uint32_t n) {
+  if (n == 0) return;
+  const uint32_t f = p & 31u;
+  uint32_t* o = out + (p >> 5);
+  const uint32_t x0 = bits32_at(base, bp);
+  if (f + n <= 32u) {
+    atomicOr(o, (n >= 32u ? x0 : x0 & ~(0xFFFFFFFFu >> n)) >> f);
+    return;
+  }
+  if (f)
+    atomicOr(o, x0 >> f);
+  else
+    o[0] = x0;  // the span covers the whole word
+  const uint32_t W = (f + n) >> 5, f2 = (f + n) & 31u;
+  const uint32_t acc = span_words(o, base, bp, f, W, f2);
+  if (f2) atomicOr(o + W, acc);
 }
 
 // Co-rank of diagonal d (A records among the first d outputs of the stable
