@@ -513,6 +513,72 @@ __device__ __forceinline__ bool fi_record_ok(const FiLayout& L, uint32_t i, uint
   return L.koff[i] + L.kbytes[i] <= key_cap && L.voff[i] + L.vbytes[i] <= val_cap;
 }
 
+// Payload bits [x, x + 8 n) to LDS bytes dst[0, n): single byte stores up
+// to dst's first 4-byte boundary and after its last, whole dwords between
+// them, each one funnel shift of two payload words with a shift that is the
+// same for the whole run (as in fi_copy_bytes).
+template <class Bits>
+__device__ __forceinline__ void fi_copy_to_lds(const Bits& bits, uint64_t x, uint8_t* dst, uint32_t n) {
+  if (n == 0) return;
+  const uint32_t head = min((4u - (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)) & 3u)) & 3u, n);
+  if (head) {
+    const uint32_t v = bits.at32(x);
+    for (uint32_t t = 0; t < head; ++t) dst[t] = static_cast<uint8_t>(v >> (24u - 8u * t));
+  }
+  const uint32_t nd = (n - head) >> 2;
+  if (nd) {
+    const uint64_t y = x + 8ull * head;
+    const uint64_t i0 = y >> 5;
+    const uint32_t sh = static_cast<uint32_t>(y & 31u);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + head);
+    uint32_t prev = bits.word(i0);
+    uint32_t k = 0;
+    for (; k + 4 <= nd; k += 4) {
+      uint32_t nx[4];
+      bits.word4(i0 + k + 1, nx);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t a = t ? nx[t - 1] : prev;
+        d[k + t] = __builtin_bswap32(sh ? __builtin_amdgcn_alignbit(a, nx[t], 32u - sh) : a);
+      }
+      prev = nx[3];
+    }
+    for (; k < nd; ++k) {
+      const uint32_t nx = bits.word(i0 + k + 1);
+      d[k] = __builtin_bswap32(sh ? __builtin_amdgcn_alignbit(prev, nx, 32u - sh) : prev);
+      prev = nx;
+    }
+  }
+  const uint32_t m = head + 4u * nd;
+  if (m < n) {
+    const uint32_t v = bits.at32(x + 8ull * m);
+    for (uint32_t t = 0; m + t < n; ++t) dst[m + t] = static_cast<uint8_t>(v >> (24u - 8u * t));
+  }
+}
+
+// LDS bytes src[0, n) to dst[0, n) (any alignments, no overlap): single bytes
+// up to dst's first 4-byte boundary and after its last, whole dwords between
+// them, each from the two aligned source dwords that hold its bytes (reads
+// reach at most 3 bytes past src + n).
+__device__ __forceinline__ void lds_copy_bytes(const uint8_t* src, uint8_t* dst, uint32_t n) {
+  const uint32_t head = min((4u - (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)) & 3u)) & 3u, n);
+  for (uint32_t t = 0; t < head; ++t) dst[t] = src[t];
+  const uint32_t nd = (n - head) >> 2;
+  if (nd) {
+    const uint8_t* s = src + head;
+    const uint32_t so = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) & 3u;
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(s - so);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst + head);
+    uint32_t lo = sw[0];
+    for (uint32_t k = 0; k < nd; ++k) {
+      const uint32_t hi = sw[k + 1];
+      d[k] = so ? __builtin_amdgcn_alignbyte(hi, lo, so) : lo;  // (little-endian bytes s[4k ..])
+      lo = hi;
+    }
+  }
+  for (uint32_t t = head + 4u * nd; t < n; ++t) dst[t] = src[t];
+}
+
 // block heads' inherited bytes, one thread each: key bytes [0, ceil(r_i / 8)),
 // the last of them complete (it also holds the literal's first bits).  The
 // literal bytes after them are the records kernel's.
@@ -628,12 +694,13 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
                                                          uint32_t* __restrict__ key_off, uint8_t* __restrict__ vals,
                                                          uint64_t val_cap, uint32_t* __restrict__ val_off,
                                                          uint8_t* __restrict__ tomb, uint64_t* __restrict__ err) {
-  __shared__ __align__(16) uint8_t win[kFiWin];
+  __shared__ __align__(16) uint8_t win[kFiWin + 16];  // (+16: reads past a copied key's end)
   if (L.S == 0) {  // (nothing was parsed or scanned)
     if (blockIdx.x == 0 && threadIdx.x == 0) key_off[0] = val_off[0] = 0;
     return;
   }
   const uint32_t r0 = blockIdx.x * rpb, r1 = min(r0 + rpb, L.S);
+
   const uint64_t kb0 = L.koff[r0], kb1 = L.koff[r1], vb0 = L.voff[r0], vb1 = L.voff[r1];
   const uint64_t kbase = kb0 & ~static_cast<uint64_t>(15), vbase = vb0 & ~static_cast<uint64_t>(15);
   const uint64_t kspan = (kb1 - kbase + 15) & ~static_cast<uint64_t>(15);
@@ -664,17 +731,17 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
         const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
         if (part && b < kb) {
           key[b] = static_cast<uint8_t>(bits.at32(L.lit[i]) >> (24u + part));
-          fi_copy_bytes(bits, L.lit[i] + (8u - part), key + b + 1, kb - b - 1);
+          fi_copy_to_lds(bits, L.lit[i] + (8u - part), key + b + 1, kb - b - 1);
         } else if (b < kb) {
-          fi_copy_bytes(bits, L.lit[i], key + b, kb - b);
+          fi_copy_to_lds(bits, L.lit[i], key + b, kb - b);
         }
         ok = true;
       } else {
         const uint32_t own = fi_head_bytes(L, i);
         for (uint32_t t = 0; t < own; ++t) key[t] = keys[ko + t];
-        if (own < kb) fi_copy_bytes(bits, L.lit[i] + (8ull * own - L.r[i]), key + own, kb - own);
+        if (own < kb) fi_copy_to_lds(bits, L.lit[i] + (8ull * own - L.r[i]), key + own, kb - own);
       }
-      fi_copy_bytes(bits, L.vbit[i], vwin + (vo - vbase), vb);
+      fi_copy_to_lds(bits, L.vbit[i], vwin + (vo - vbase), vb);
     } else {
       if (i == head) {
         const uint32_t own = fi_head_bytes(L, i);
@@ -703,7 +770,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
       uint8_t* key = kwin + (L.koff[i] - kbase);
       const uint8_t* pk = kwin + (L.koff[i - 1] - kbase);
       const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
-      for (uint32_t t = 0; t < b; ++t) key[t] = pk[t];
+      lds_copy_bytes(pk, key, b);
       if (part && b < L.kbytes[i]) key[b] = static_cast<uint8_t>((pk[b] & (0xFF00u >> part)) | key[b]);
     }
   }
