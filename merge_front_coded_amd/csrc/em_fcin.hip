@@ -653,6 +653,50 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
   fi_head_prefix(bits, L, i, keys + L.koff[i], fi_head_bytes(L, i), err);
 }
 
+// Key j's inherited bits [0, r_j) in the LDS window, from the keys of the
+// earlier records of its block: once every literal (and each head's whole
+// key) is in the window, walking t = j-1, j-2, ... down to the block head,
+// key j's bits [r_t, hi) are key t's own literal bits whenever r_t < hi (hi:
+// the bits still to fill, the smallest r met so far; every record between
+// them inherited at least hi bits), and the head's key gives the rest.  The
+// bytes are composed from the top down: whole bytes are copied, a byte split
+// between two sources is assembled in a register.  r[] and kp[] hold the
+// block's retained lengths and window offsets, indexed by thread; key j's
+// own literal bits of its byte r_j / 8 are already there.  Reads of another
+// key's partial byte keep only its literal bits, which its own thread does
+// not change.
+__device__ __forceinline__ void fi_prefix_lds(uint8_t* kwin, const uint32_t* r, const uint32_t* kp, uint32_t j,
+                                              uint32_t head) {
+  uint32_t hi = r[j];
+  if (hi == 0) return;
+  uint8_t* key = kwin + kp[j];
+  uint32_t acc = (hi & 7u) ? key[hi >> 3] : 0u;  // the byte being assembled, (hi - 1) / 8
+  for (uint32_t t = j - 1;; --t) {
+    const bool at_head = t == head;
+    const uint32_t lo = at_head ? 0u : r[t];
+    if (lo < hi) {
+      const uint8_t* src = kwin + kp[t];
+      while (hi > lo) {
+        if ((hi & 7u) == 0 && hi - lo >= 8) {  // whole bytes [ceil(lo / 8), hi / 8); acc is empty
+          const uint32_t b0 = (lo + 7u) >> 3, b1 = hi >> 3;
+          lds_copy_bytes(src + b0, key + b0, b1 - b0);
+          hi = 8u * b0;
+          continue;
+        }
+        const uint32_t b = (hi - 1u) >> 3, blo = max(lo, 8u * b);
+        acc |= src[b] & (0xFFu >> (blo - 8u * b)) & (0xFFu << (8u * b + 8u - hi));
+        hi = blo;
+        if (blo == 8u * b) {
+          key[b] = static_cast<uint8_t>(acc);
+          acc = 0;
+        }
+      }
+      if (hi == 0) return;
+    }
+    if (at_head) return;  // (only a chain that failed the prefix check ends here)
+  }
+}
+
 // every record: offsets, tombstone flag, value bytes, and the key bytes not
 // written before (all of a record's that is not a block head; a head's
 // literal).  A workgroup takes rpb consecutive records
@@ -660,12 +704,14 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_heads(FiBits bits, FiLayout L, 
 // value bytes are two contiguous ranges.  When both fit the LDS window (each
 // from the 16-byte boundary below its start), the records are written there
 // and the workgroup copies the two ranges out with 16-byte stores, single
-// bytes only in the groups it shares with its neighbours.  In the window a key
-// is built as the encoder defined it: a block head's inherited bytes are
-// copied from the arena (the kernel before wrote them) and its literal from
-// the payload; every other record writes its literal, then, in fourteen
-// rounds (round j: the records at block position j), takes its first r_i bits
-// from its predecessor's finished key.  A workgroup whose ranges do not fit
+// bytes only in the groups it shares with its neighbours.  In the window a
+// block head's inherited bytes are copied from the arena (the kernel before
+// wrote them) and its literal from the payload; every other record writes its
+// literal, and after one barrier takes its first r_i bits from the literals of
+// the earlier records of its block and the head's key (fi_prefix_lds), all
+// records at once.  (Copying each record's prefix from its predecessor's
+// finished key took fourteen barrier rounds, each with one fifteenth of the
+// threads busy.)  A workgroup whose ranges do not fit
 // writes each record to the arenas directly: the heads' literals first, then,
 // after a barrier, every other key by the owner chain, which may read a
 // head's literal bytes.
@@ -695,6 +741,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
                                                          uint64_t val_cap, uint32_t* __restrict__ val_off,
                                                          uint8_t* __restrict__ tomb, uint64_t* __restrict__ err) {
   __shared__ __align__(16) uint8_t win[kFiWin + 16];  // (+16: reads past a copied key's end)
+  __shared__ uint32_t rr[kFiBlock], kp[kFiBlock];     // retained bits and window offset of each record
   if (L.S == 0) {  // (nothing was parsed or scanned)
     if (blockIdx.x == 0 && threadIdx.x == 0) key_off[0] = val_off[0] = 0;
     return;
@@ -710,7 +757,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
   uint8_t* kwin = win;
   uint8_t* vwin = win + (staged ? kspan : 0);
   const uint32_t i = r0 + threadIdx.x;
-  bool ok = false;     // a staged record that takes its prefix in the rounds
+  bool ok = false;     // a staged record that takes its inherited prefix from the window
   bool chain = false;  // an unstaged record that takes its key by the owner chain
   if (threadIdx.x < rpb && i < r1) {
     const uint64_t ko = L.koff[i], vo = L.voff[i];
@@ -725,9 +772,11 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
                static_cast<unsigned long long>(prefix ? kFiErrPrefix : kFiErrCap));
     } else if (staged) {
       uint8_t* key = kwin + (ko - kbase);
+      rr[threadIdx.x] = L.r[i];
+      kp[threadIdx.x] = static_cast<uint32_t>(ko - kbase);
       if (i != head) {
         // the literal: key bits [r_i, 8 kb); a byte it shares with the
-        // inherited prefix gets its low bits here, its high bits in the round
+        // inherited prefix gets its low bits here, its high bits afterwards
         const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
         if (part && b < kb) {
           key[b] = static_cast<uint8_t>(bits.at32(L.lit[i]) >> (24u + part));
@@ -761,19 +810,8 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
     if (chain) fi_key(bits, L, i, i - i % kFiRecs, keys + L.koff[i - i % kFiRecs], keys + L.koff[i], L.kbytes[i], err);
     return;
   }
-  const uint32_t pos = threadIdx.x % kFiRecs;  // (r0 is a multiple of 15)
-  for (uint32_t j = 1; j < kFiRecs; ++j) {
-    __syncthreads();
-    if (ok && pos == j) {
-      // bits [0, r_i) from the predecessor's key (at least r_i bits long: the
-      // record passed the prefix check)
-      uint8_t* key = kwin + (L.koff[i] - kbase);
-      const uint8_t* pk = kwin + (L.koff[i - 1] - kbase);
-      const uint32_t l = L.r[i], b = l >> 3, part = l & 7u;
-      lds_copy_bytes(pk, key, b);
-      if (part && b < L.kbytes[i]) key[b] = static_cast<uint8_t>((pk[b] & (0xFF00u >> part)) | key[b]);
-    }
-  }
+  __syncthreads();  // every literal and every head's key is in the window
+  if (ok) fi_prefix_lds(kwin, rr, kp, threadIdx.x, threadIdx.x - threadIdx.x % kFiRecs);  // (r0: a multiple of 15)
   __syncthreads();
   fi_copy_out(keys, kwin, kbase, kb0, kb1);
   fi_copy_out(vals, vwin, vbase, vb0, vb1);
