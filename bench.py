@@ -460,24 +460,32 @@ def main():
         key_off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
         val_off = torch.empty(S + 1, dtype=torch.int32, device="cuda")
         tomb = torch.empty(max(S, 1), dtype=torch.uint8, device="cuda")
-        ev_p, ev_m = [], []
+        pfx = torch.empty(max(S, 1), dtype=torch.int64, device="cuda")
+        ev_p, ev_m, ev_c = [], [], []
         for it in range(args.steps + 1):
-            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a, b, c, d = (torch.cuda.Event(enable_timing=True) for _ in range(4))
             a.record(stream)
             em.em_fcin_parse(pn.payload, T, S, tot, ws, off=pn.off, stream=stream)
             b.record(stream)
             em.em_fcin_materialize(pn.payload, S, keys, key_off, vals, val_off, tomb, tot, ws, stream=stream)
             c.record(stream)
+            em.em_fcin_prefix8(pn.payload, S, pfx, ws, stream=stream)
+            d.record(stream)
             if it:  # the first pass warms up
                 ev_p.append((a, b))
                 ev_m.append((b, c))
+                ev_c.append((c, d))
         torch.cuda.synchronize()
         assert int(tot[2].item()) == 0
         parse_ms = sum(x.elapsed_time(y) for x, y in ev_p) / len(ev_p)
         mat_ms = sum(x.elapsed_time(y) for x, y in ev_m) / len(ev_m)
+        pfx_ms = sum(x.elapsed_time(y) for x, y in ev_c) / len(ev_c)
         fcin_bytes = (T + 7) // 8 + kb + vb + 8 * (S + 1) + S
         result["front_coded_input"] = {"calls": ["em_fcin_parse", "em_fcin_materialize"], "parse_ms": parse_ms,
                                        "materialize_ms": mat_ms, "key_bytes": kb, "value_bytes": vb,
+                                       # the prefix cache filled from the literal owners, no key
+                                       # arena (em_fcin_prefix8): its cost beside the materialization
+                                       "prefix_cache_from_owners_ms": pfx_ms,
                                        "algorithmic_bytes": fcin_bytes,
                                        "GBps": fcin_bytes / ((parse_ms + mat_ms) * 1e-3) / 1e9}
         if pn is not pl:

@@ -402,6 +402,23 @@ int em_fcin_materialize(const uint32_t *payload, uint64_t payload_words, uint32_
                         uint8_t *tomb, uint64_t *d_totals, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The prefix cache of a front-coded input filled from the literal owners,
+ * with no key arena (Everett, "GPU construction experiment", the
+ * prefix-cache paragraph -- eight key bytes cached per record -- and the
+ * literal-owner paragraph: bit p of key i is the literal bit of
+ * j = max{t <= i : r_t <= p}).  After em_fcin_parse on the same payload and
+ * workspace (no error bits), writes pfx[i] = the first 8 bytes of key i as a
+ * big-endian u64 (first key byte most significant), zero past the key's end,
+ * for i in [0, S).  pfx: u64[S] in device memory.  Every value depends only on
+ * the parse's outputs, so the call can run in place of, or besides,
+ * em_fcin_materialize.  Errors: EM_EINVAL (NULL or misaligned workspace, NULL
+ * payload or pfx with S > 0), EM_ERANGE (S >= EM_MAX_RECORDS), EM_ENOSPC
+ * (ws_bytes below em_fcin_workspace_bytes(S)).
+ */
+int em_fcin_prefix8(const uint32_t *payload, uint64_t payload_words, uint32_t S, uint64_t *pfx, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
  * Byte-profile front coding (Everett, "Byte-profile GPU merge", "Pipeline":
  * byte LEB128 counts, byte FC literals, optional-value tags, a common encoded
  * value width -- width seventeen is a presence tag and sixteen payload

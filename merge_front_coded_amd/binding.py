@@ -79,6 +79,7 @@ def load_library(path: str = LIB_PATH):
         "em_fcin_workspace_bytes": (sz, [u32]),
         "em_fcin_parse": (i32, [P, u64, u64, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_fcin_materialize": (i32, [P, u64, u32, P, u64, P, P, u64, P, P, P, P, sz, P]),
+        "em_fcin_prefix8": (i32, [P, u64, u32, P, P, sz, P]),
         "em_bp_workspace_bytes": (sz, [u32]),
         "em_bp_lengths": (i32, [S, S, P, P, u32, P, P, P, sz, P]),
         "em_bp_emit": (i32, [S, S, P, P, u32, P, u64, P, P, u64, P, P]),
@@ -367,6 +368,11 @@ def em_fcin_materialize(payload, S, keys, key_off, vals, val_off, tomb, d_totals
     _check(lib().em_fcin_materialize(_p(payload), payload.numel(), S, _p(keys), keys.numel(), _p(key_off),
                                      _p(vals), vals.numel(), _p(val_off), _p(tomb), _p(d_totals), _p(ws),
                                      ws.numel(), _stream(stream)), "em_fcin_materialize")
+
+
+def em_fcin_prefix8(payload, S, pfx, ws, stream=None):
+    _check(lib().em_fcin_prefix8(_p(payload), payload.numel(), S, _p(pfx), _p(ws), ws.numel(), _stream(stream)),
+           "em_fcin_prefix8")
 
 
 def fcin_decode(payload, T: int, S: int, off=None, nav: "EfSections | None" = None, device="cuda") -> DeviceSide:

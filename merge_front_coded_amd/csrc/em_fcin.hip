@@ -33,6 +33,11 @@ namespace em {
 constexpr int kFiBlock = 256;
 constexpr uint32_t kFiRecs = 15;  // records per block (the W15 period)
 constexpr uint32_t kFiInf = 0xFFFFFFFFu;
+constexpr int kFpBlock = 256;
+constexpr uint32_t kFpPer = 16;                  // rows of kFpBlock records per tile
+constexpr uint32_t kFpTile = kFpBlock * kFpPer;  // records per workgroup
+constexpr int kFpTilesBlock = 1024;
+constexpr uint32_t kFpTilesPer = 4;  // tiles per thread of the tile scan: EM_MAX_RECORDS / kFpTile / 1024
 
 enum : uint64_t {
   kFiErrRange = 1,    // a field reaches past T, or an EG0 code is malformed
@@ -56,6 +61,8 @@ struct FiLayout {
   uint64_t* voff;     // S + 2 value arena offsets
   uint32_t* tree;     // 2 P2 minimum tree over r (heap order, leaves at P2)
   uint32_t* pse;      // S: the last earlier record with a smaller r (kFiInf: none)
+  uint64_t* fp_agg;   // prefix cache: per tile of kFpTile records, its composed step (m, v)
+  uint64_t* fp_x;     // prefix cache: per tile, the first 64 key bits of the record before it
   uint8_t* scan_ws;
   size_t scan_bytes;
   size_t used;
@@ -80,6 +87,8 @@ static FiLayout fi_layout(void* ws, uint32_t S) {
   L.voff = cur.take<uint64_t>(n);
   L.tree = cur.take<uint32_t>(2 * static_cast<size_t>(L.P2));
   L.pse = cur.take<uint32_t>(n);
+  L.fp_agg = cur.take<uint64_t>(2 * (static_cast<size_t>(S) / kFpTile + 1));
+  L.fp_x = cur.take<uint64_t>(static_cast<size_t>(S) / kFpTile + 1);
   L.scan_bytes = scan_ws(S + 1);
   L.scan_ws = cur.take<uint8_t>(L.scan_bytes);
   L.used = cur.used;
@@ -817,6 +826,124 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
   fi_copy_out(vals, vwin, vbase, vb0, vb1);
 }
 
+// ---- the prefix cache filled from the literal owners ----
+//
+// Everett, "GPU construction experiment", the prefix-cache and literal-owner
+// paragraphs: the merge caches eight key bytes per record, and bit p of key
+// i is the literal bit of its owner j = max{t <= i : r_t <= p}.  For the
+// first 64 bits this owner rule is a running composition: record i keeps the
+// top min(r_i, 64) bits of record i-1's first 64 bits (every record from the
+// owner of such a bit up to i inherited it) and writes its own literal bits
+// [r_i, min(64, 8 k_i)) below them, zero past the key's end.  A step
+// "keep the top m bits of x, then OR v" composes associatively
+// ((m1, v1) then (m2, v2) = (min(m1, m2), (v1 & top(m2)) | v2)), so every
+// record's 64 bits come from one scan over the records instead of a walk down
+// each record's owner chain.
+
+struct FpStep {
+  uint32_t m;  // top bits kept
+  uint64_t v;  // bits ORed after
+};
+
+__device__ __forceinline__ uint64_t fp_top(uint32_t m) {
+  return m >= 64u ? ~0ull : (m == 0 ? 0ull : ~0ull << (64u - m));
+}
+
+// a, then b
+__device__ __forceinline__ FpStep fp_then(FpStep a, FpStep b) {
+  return FpStep{min(a.m, b.m), (a.v & fp_top(b.m)) | b.v};
+}
+
+__device__ __forceinline__ FpStep fp_record(const FiBits& bits, const FiLayout& L, uint32_t i) {
+  const uint32_t r = L.r[i];
+  const uint32_t e = min(64u, 8u * L.kbytes[i]);  // the key's bits inside the cache
+  if (r >= e) return FpStep{min(r, 64u), 0ull};
+  const uint64_t lit = L.lit[i];
+  const uint64_t w = (static_cast<uint64_t>(bits.at32(lit)) << 32) | bits.at32(lit + 32);
+  return FpStep{r, (w >> r) & fp_top(e) & ~fp_top(r)};  // literal bit k at key bit r + k
+}
+
+__device__ __forceinline__ FpStep fp_shfl_up(FpStep a, uint32_t d) {
+  return FpStep{__shfl_up(a.m, d), (static_cast<uint64_t>(__shfl_up(static_cast<uint32_t>(a.v >> 32), d)) << 32) |
+                                       __shfl_up(static_cast<uint32_t>(a.v), d)};
+}
+
+// Exclusive ordered scan of one step per thread over the workgroup (kThreads
+// a multiple of kWave); `tot` receives the composition of all of them.
+template <int kThreads>
+__device__ __forceinline__ FpStep fp_block_exclusive(FpStep x, FpStep* sh, FpStep& tot) {
+  constexpr int kW = kThreads / kWave;
+  const uint32_t lane = __lane_id(), wave = threadIdx.x / kWave;
+  FpStep inc = x;
+#pragma unroll
+  for (uint32_t d = 1; d < kWave; d <<= 1) {
+    const FpStep o = fp_shfl_up(inc, d);
+    if (lane >= d) inc = fp_then(o, inc);
+  }
+  FpStep exc = fp_shfl_up(inc, 1);
+  if (lane == 0) exc = FpStep{64u, 0ull};
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  FpStep before{64u, 0ull}, all{64u, 0ull};  // the waves before this one; all waves
+  for (int w = 0; w < kW; ++w) {
+    if (static_cast<uint32_t>(w) < wave) before = fp_then(before, sh[w]);
+    all = fp_then(all, sh[w]);
+  }
+  tot = all;
+  __syncthreads();
+  return fp_then(before, exc);
+}
+
+// A tile is kFpPer rows of kFpBlock consecutive records, one a thread, so
+// that the field loads, the literal reads and the stores of a row are
+// consecutive; the rows are composed in order.
+__device__ __forceinline__ FpStep fp_row_record(const FiBits& bits, const FiLayout& L, uint32_t tile, uint32_t u) {
+  const uint32_t i = tile * kFpTile + u * kFpBlock + threadIdx.x;
+  return i < L.S ? fp_record(bits, L, i) : FpStep{64u, 0ull};
+}
+
+__global__ __launch_bounds__(kFpBlock) void k_fp_reduce(FiBits bits, FiLayout L) {
+  __shared__ FpStep sh[kFpBlock / kWave];
+  FpStep agg{64u, 0ull};
+  for (uint32_t u = 0; u < kFpPer && blockIdx.x * kFpTile + u * kFpBlock < L.S; ++u) {
+    FpStep tot;
+    (void)fp_block_exclusive<kFpBlock>(fp_row_record(bits, L, blockIdx.x, u), sh, tot);
+    agg = fp_then(agg, tot);
+  }
+  if (threadIdx.x == 0) {
+    L.fp_agg[2 * blockIdx.x] = agg.m;
+    L.fp_agg[2 * blockIdx.x + 1] = agg.v;
+  }
+}
+
+// the first 64 key bits of the record before each tile (0 before the first)
+__global__ __launch_bounds__(kFpTilesBlock) void k_fp_tiles(FiLayout L, uint32_t ntiles) {
+  __shared__ FpStep sh[kFpTilesBlock / kWave];
+  const uint32_t t0 = threadIdx.x * kFpTilesPer;
+  FpStep a{64u, 0ull};
+  for (uint32_t q = 0; q < kFpTilesPer && t0 + q < ntiles; ++q)
+    a = fp_then(a, FpStep{static_cast<uint32_t>(L.fp_agg[2 * (t0 + q)]), L.fp_agg[2 * (t0 + q) + 1]});
+  FpStep tot;
+  FpStep before = fp_block_exclusive<kFpTilesBlock>(a, sh, tot);
+  for (uint32_t q = 0; q < kFpTilesPer && t0 + q < ntiles; ++q) {
+    L.fp_x[t0 + q] = before.v;  // (applied to the all-zero start)
+    before = fp_then(before, FpStep{static_cast<uint32_t>(L.fp_agg[2 * (t0 + q)]), L.fp_agg[2 * (t0 + q) + 1]});
+  }
+}
+
+__global__ __launch_bounds__(kFpBlock) void k_fp_apply(FiBits bits, FiLayout L, uint64_t* __restrict__ pfx) {
+  __shared__ FpStep sh[kFpBlock / kWave];
+  uint64_t x = L.fp_x[blockIdx.x];  // the first 64 bits of the record before the row
+  for (uint32_t u = 0; u < kFpPer && blockIdx.x * kFpTile + u * kFpBlock < L.S; ++u) {
+    const uint32_t i = blockIdx.x * kFpTile + u * kFpBlock + threadIdx.x;
+    const FpStep st = fp_row_record(bits, L, blockIdx.x, u);
+    FpStep tot;
+    const FpStep inc = fp_then(fp_block_exclusive<kFpBlock>(st, sh, tot), st);
+    if (i < L.S) pfx[i] = (x & fp_top(inc.m)) | inc.v;
+    x = (x & fp_top(tot.m)) | tot.v;
+  }
+}
+
 // totals and the size checks, after the scans
 __global__ void k_fi_totals(FiLayout L, uint64_t* __restrict__ totals) {
   const uint64_t kt = L.koff[L.S], vt = L.voff[L.S];
@@ -906,5 +1033,22 @@ extern "C" int em_fcin_materialize(const uint32_t* payload, uint64_t payload_wor
   rpb -= rpb % kFiRecs;  // whole blocks
   hipLaunchKernelGGL(k_fi_records, dim3(S ? (S + rpb - 1) / rpb : 1), dim3(kFiBlock), 0, st, bits, L, rpb, keys,
                      key_cap, key_off, vals, val_cap, val_off, tomb, d_totals + 2);
+  return check_launch();
+}
+
+extern "C" int em_fcin_prefix8(const uint32_t* payload, uint64_t payload_words, uint32_t S, uint64_t* pfx,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255)) return EM_EINVAL;
+  if (S >= EM_MAX_RECORDS) return EM_ERANGE;
+  if (S && (!payload || !pfx)) return EM_EINVAL;
+  if (ws_bytes < em_fcin_workspace_bytes(S)) return EM_ENOSPC;
+  if (S == 0) return EM_OK;
+  hipStream_t st = as_stream(stream);
+  const FiLayout L = fi_layout(ws, S);
+  const FiBits bits{payload, payload_words};
+  const uint32_t ntiles = (S + kFpTile - 1) / kFpTile;  // <= kFpTilesBlock * kFpTilesPer
+  hipLaunchKernelGGL(k_fp_reduce, dim3(ntiles), dim3(kFpBlock), 0, st, bits, L);
+  hipLaunchKernelGGL(k_fp_tiles, dim3(1), dim3(kFpTilesBlock), 0, st, L, ntiles);
+  hipLaunchKernelGGL(k_fp_apply, dim3(ntiles), dim3(kFpBlock), 0, st, bits, L, pfx);
   return check_launch();
 }

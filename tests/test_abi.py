@@ -164,6 +164,18 @@ def test_onepass_argument_errors(lib):
                                    None, None, None, None, None, ws, 0, None) == -3
 
 
+def test_fcin_prefix8_argument_errors(lib):
+    buf = ctypes.c_void_p(0x100000)
+    need = lib.em_fcin_workspace_bytes(5)
+    assert lib.em_fcin_prefix8(buf, 4, 5, buf, None, need, None) == -1  # no workspace
+    assert lib.em_fcin_prefix8(buf, 4, 5, buf, ctypes.c_void_p(0x100008), need, None) == -1  # misaligned
+    assert lib.em_fcin_prefix8(None, 4, 5, buf, buf, need, None) == -1  # no payload
+    assert lib.em_fcin_prefix8(buf, 4, 5, None, buf, need, None) == -1  # no output
+    assert lib.em_fcin_prefix8(buf, 4, 1 << 24, buf, buf, 1 << 40, None) == -2  # record cap
+    assert lib.em_fcin_prefix8(buf, 4, 5, buf, buf, need - 1, None) == -3  # workspace too small
+    assert lib.em_fcin_prefix8(None, 0, 0, None, buf, lib.em_fcin_workspace_bytes(0), None) == 0  # nothing to do
+
+
 def test_missing_library_fails_loudly(tmp_path):
     """Without the HIP library the binding raises; there is no CPU fallback."""
     from merge_front_coded_amd import binding

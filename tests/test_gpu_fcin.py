@@ -4,7 +4,9 @@ arenas and compared byte for byte with the CPU oracle's decoder, with block
 starts taken from the record offsets and from the navigation sections; a
 decoded side is merged again and compared with the oracle; block edges,
 sub-byte prefixes, long inherited chains, fixed-width values, the empty
-payload and malformed lengths are covered."""
+payload and malformed lengths are covered.  The prefix cache filled from the
+literal owners (em_fcin_prefix8) is compared with the first eight bytes of
+the oracle's decoded keys."""
 import numpy as np
 import pytest
 
@@ -152,3 +154,68 @@ def test_malformed_lengths_are_reported():
             em.fcin_decode(pl.payload, bad_T, S, off=pl.off)
     with pytest.raises(em.EmError):  # one record fewer: the last block ends early
         em.fcin_decode(pl.payload, T, S - 1, off=pl.off)
+
+
+def _first8(side):
+    """The first 8 bytes of every key as big-endian u64s, zero past the key's end."""
+    off = side.key_off.astype(np.int64)
+    lens = off[1:] - off[:-1]
+    keys = np.concatenate([side.keys, np.zeros(8, np.uint8)])
+    out = np.zeros(lens.size, np.uint64)
+    for b in range(8):
+        byte = np.where(lens > b, keys[np.minimum(off[:-1] + b, keys.size - 1)], 0).astype(np.uint64)
+        out |= byte << np.uint64(56 - 8 * b)
+    return out
+
+
+def _prefix_cache_case(Ah, Bh, label):
+    import merge_front_coded_amd as em
+    pl = run_gpu(Ah, Bh, items=256)
+    torch.cuda.synchronize()
+    S, T = pl.S, pl.T
+    payload_h = np.frombuffer(pl.payload_bytes(), np.uint8)
+    want = oracle.fc_decode(payload_h, T, S, int(Ah.keys.size + Bh.keys.size) + 16,
+                            int(Ah.vals.size + Bh.vals.size) + 16)
+    print(f"{label}: S={S} T={T}", flush=True)
+    ws = torch.empty(max(em.em_fcin_workspace_bytes(S), 256), dtype=torch.uint8, device="cuda")
+    tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+    em.em_fcin_parse(pl.payload, T, S, tot, ws, off=pl.off)
+    assert int(tot[2].item()) == 0
+    pfx = torch.full((max(S, 1),), -1, dtype=torch.int64, device="cuda")
+    em.em_fcin_prefix8(pl.payload, S, pfx, ws)
+    torch.cuda.synchronize()
+    got = pfx[:S].cpu().numpy().view(np.uint64)
+    exp = _first8(want)
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, f"{label}: prefix differs at {bad[:5]}: {[hex(int(got[i])) for i in bad[:3]]} " \
+                          f"vs {[hex(int(exp[i])) for i in bad[:3]]}"
+
+
+@pytest.mark.parametrize("wid,scale", [(1, 0.3), (2, 0.005), (3, 0.0025), (4, 0.001), (5, 0.002)])
+def test_prefix_cache_from_owners(wid, scale):
+    """Several 4096-record tiles and a ragged last one (workload 3 at this
+    scale: about 30k survivors); URL keys inherit far more than 8 bytes."""
+    A, B = workload(wid, scale)
+    _prefix_cache_case(A, B, f"workload {wid} at {scale}")
+
+
+def test_prefix_cache_edges():
+    """Keys shorter than 8 bytes and empty, prefixes that end inside a byte,
+    inherited runs longer than 8 bytes that end at and around byte 8, and one
+    record."""
+    rng = np.random.default_rng(23)
+    recs = [(b"", b"e")]
+    for i in range(3000):
+        k = bytes(rng.integers(0, 4, int(rng.integers(0, 7)), dtype=np.uint8))
+        recs.append((bytes([1 + i // 300]) + k, None if i % 5 == 0 else b"v"))
+    for i in range(1500):
+        recs.append((b"\x7f" * int(7 + i % 4) + bytes([i % 3, (i // 3) % 251]) + b"tail" * (i % 2), b"w"))
+    recs = sorted(set(recs), key=lambda kv: kv[0])
+    uniq = {}
+    for k, v in recs:
+        uniq[k] = v
+    items = sorted(uniq.items())
+    A = gen.side_from_records(items[::2])
+    B = gen.side_from_records(items[1::2])
+    _prefix_cache_case(A, B, "edges")
+    _prefix_cache_case(gen.side_from_records([(b"only", b"x")]), gen.side_from_records([]), "one record")
