@@ -12,6 +12,8 @@ Usage (from the repository root, after rocprofv3 runs that wrote CSV files):
   python -m merge_front_coded_amd.profiling traffic OUT.md WORKLOAD FETCH_DIRS WRITE_DIRS "COMMANDS"
   (FETCH_DIRS / WRITE_DIRS: comma-separated rocprofv3 output directories)
   python -m merge_front_coded_amd.profiling trace OUT.md "TITLE" STATS_CSV "COMMAND"
+  python -m merge_front_coded_amd.profiling counters OUT.md "TITLE" DIRS "COMMANDS"
+  (DIRS: comma-separated rocprofv3 output directories of --pmc runs)
 """
 from __future__ import annotations
 
@@ -180,11 +182,78 @@ def write_trace(out_md: str, title: str, stats_csv: str, command: str, top: int 
         fh.write("\n".join(lines) + "\n")
 
 
+def _per_dispatch_all(rows):
+    """{(kernel name, counter): [value per dispatch]} for every counter."""
+    acc = {}
+    for r in rows:
+        key = (kernel_short_name(r["Kernel_Name"]), r["Counter_Name"], r.get("_file"),
+               r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, counter, _, _), v in acc.items():
+        out.setdefault((name, counter), []).append(v)
+    return out
+
+
+def write_counters(out_md: str, title: str, dirs: str, command: str, cus: int = 256, simds: int = 1024,
+                   clock_ghz: float = 2.4) -> None:
+    """Summarise shader, LDS, address-unit and atomic counters per kernel
+    (mean per dispatch), with the derived shares: cycles = GRBM_GUI_ACTIVE / 8
+    (summed over the eight XCDs); VALU busy = 4 SQ_INSTS_VALU / (cycles x
+    SIMDs) (a wave64 VALU instruction occupies a SIMD for four clocks); LDS
+    conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; waiting share =
+    SQ_WAIT_ANY / SQ_WAVE_CYCLES; resident waves per CU = 4 SQ_WAVE_CYCLES /
+    (cycles x CUs) (SQ cycle counters tick once per four clocks); address unit
+    busy = TA_TA_BUSY_sum / (cycles x CUs)."""
+    vals = {k: sum(v) / len(v) for k, v in _per_dispatch_all(_counter_rows(dirs)).items()}
+    names = sorted({k for k, _ in vals})
+    g = lambda n, c: vals.get((n, c))
+    lines = [f"# Shader, LDS, address-unit and atomic counters: {title}", "",
+             "Commands (from the repository root, one MI355X; one counter group per run; values are means per "
+             "dispatch):", "", "```", command, "```", "",
+             "Derived: cycles = GRBM_GUI_ACTIVE / 8 (summed over the eight XCDs); VALU busy = 4 x SQ_INSTS_VALU / "
+             f"(cycles x {simds} SIMDs); LDS conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; waiting share "
+             "= SQ_WAIT_ANY / SQ_WAVE_CYCLES; resident waves per CU = 4 x SQ_WAVE_CYCLES / (cycles x "
+             f"{cus}); address unit busy = TA_TA_BUSY_sum / (cycles x {cus}); cycles as ms at {clock_ghz} GHz.", "",
+             "| kernel | waves | VALU instr | LDS instr | SALU instr | VALU busy | LDS conflict share | waiting share "
+             "| resident waves/CU | address unit busy | cycles as ms |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    fmt = lambda x, f: "-" if x is None else f(x)
+    atomic_rows = []
+    for n in names:
+        cyc = g(n, "GRBM_GUI_ACTIVE")
+        cyc = cyc / 8 if cyc else None
+        valu, lds, salu = g(n, "SQ_INSTS_VALU"), g(n, "SQ_INSTS_LDS"), g(n, "SQ_INSTS_SALU")
+        if valu is not None:
+            conf, idx = g(n, "SQ_LDS_BANK_CONFLICT"), g(n, "SQ_LDS_IDX_ACTIVE")
+            wait, wc, ta = g(n, "SQ_WAIT_ANY"), g(n, "SQ_WAVE_CYCLES"), g(n, "TA_TA_BUSY_sum")
+            pct = lambda a, b: None if a is None or not b else 100.0 * a / b
+            lines.append(
+                f"| `{n}` | {fmt(g(n, 'SQ_WAVES'), lambda x: f'{x:.0f}')} | {fmt(valu, lambda x: f'{x:.3g}')} | "
+                f"{fmt(lds, lambda x: f'{x:.3g}')} | {fmt(salu, lambda x: f'{x:.3g}')} | "
+                f"{fmt(pct(4 * valu, cyc * simds) if cyc else None, lambda x: f'{x:.0f}%')} | "
+                f"{fmt(pct(conf, idx), lambda x: f'{x:.0f}%')} | {fmt(pct(wait, wc), lambda x: f'{x:.0f}%')} | "
+                f"{fmt(4 * wc / (cyc * cus) if wc and cyc else None, lambda x: f'{x:.1f}')} | "
+                f"{fmt(pct(ta, cyc * cus) if cyc else None, lambda x: f'{x:.0f}%')} | "
+                f"{fmt(cyc / (clock_ghz * 1e6) if cyc else None, lambda x: f'{x:.3f}')} |")
+        wr, wor = g(n, "TCP_TCC_ATOMIC_WITH_RET_REQ_sum"), g(n, "TCP_TCC_ATOMIC_WITHOUT_RET_REQ_sum")
+        if wr is not None or wor is not None:
+            atomic_rows.append(f"| `{n}` | {fmt(g(n, 'SQ_WAVES'), lambda x: f'{x:.0f}')} | "
+                               f"{fmt(wor, lambda x: f'{x:.3g}')} | {fmt(wr, lambda x: f'{x:.3g}')} |")
+    if atomic_rows:
+        lines += ["", "| kernel | waves | atomics without return (TCP to TCC) | atomics with return |",
+                  "|---|---|---|---|"] + atomic_rows
+    with open(out_md, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     kind = sys.argv[1]
     if kind == "traffic":
         write_traffic(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
     elif kind == "trace":
         write_trace(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
+    elif kind == "counters":
+        write_counters(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     else:
         raise SystemExit(__doc__)
