@@ -375,7 +375,7 @@ int em_ef_encode(const uint64_t *entries, uint32_t n, uint64_t width, uint64_t *
  *     is not NULL, else by select on the navigation sections of
  *     em_ef_navigation (nav_info and the four arrays, device memory); one
  *     thread parses each block of at most 15 records (retained length r_i,
- *     key bytes, literal and value positions, tombstone flag); the key and
+ *     key bytes, literal position, value bytes, tombstone flag); the key and
  *     value arena offsets are scanned and a minimum tree over r_i is built.
  *     Writes d_totals[0] = key arena bytes, d_totals[1] = value arena bytes
  *     and d_totals[2] = error bits (0: none; 1: a field past T or a bad

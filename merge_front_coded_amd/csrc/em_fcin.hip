@@ -55,7 +55,6 @@ struct FiLayout {
   uint32_t* kbytes;   // S + 1 key bytes (scan input; entry S is 0)
   uint32_t* vbytes;   // S + 1 value bytes
   uint64_t* lit;      // S payload bit of each literal's first bit
-  uint64_t* vbit;     // S payload bit of each value's first byte
   uint8_t* tflag;     // S tombstone flags
   uint64_t* koff;     // S + 2 key arena offsets (scan output)
   uint64_t* voff;     // S + 2 value arena offsets
@@ -81,7 +80,6 @@ static FiLayout fi_layout(void* ws, uint32_t S) {
   L.kbytes = cur.take<uint32_t>(n);
   L.vbytes = cur.take<uint32_t>(n);
   L.lit = cur.take<uint64_t>(n);
-  L.vbit = cur.take<uint64_t>(n);
   L.tflag = cur.take<uint8_t>(n);
   L.koff = cur.take<uint64_t>(n);
   L.voff = cur.take<uint64_t>(n);
@@ -281,7 +279,7 @@ __global__ __launch_bounds__(kFiParseWave) void k_fi_parse(FiBits bits, uint64_t
                                                            uint32_t* __restrict__ r_out,
                                                            uint32_t* __restrict__ kbytes,
                                                            uint32_t* __restrict__ vbytes, uint64_t* __restrict__ lit,
-                                                           uint64_t* __restrict__ vbit, uint8_t* __restrict__ tflag,
+                                                           uint8_t* __restrict__ tflag,
                                                            uint64_t* __restrict__ err) {
   __shared__ __align__(16) uint32_t span[kFiParseWords];
   const uint32_t k0 = blockIdx.x * G;
@@ -342,7 +340,6 @@ __global__ __launch_bounds__(kFiParseWave) void k_fi_parse(FiBits bits, uint64_t
     }
     if (pos + nv > T) e |= kFiErrRange;
     pos += nv;
-    vbit[i] = pos;
     vbytes[i] = vlen;
     tflag[i] = present ? 0 : 1;
     pos += 8ull * vlen;
@@ -775,6 +772,9 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
     tomb[i] = L.tflag[i];
     const uint32_t kb = L.kbytes[i], vb = L.vbytes[i];
     const uint32_t head = i - i % kFiRecs;
+    // the value's first byte: after the literal (8 kb - r_i bits) and the
+    // value header (the presence bit and, for a present value, EG0(length))
+    const uint64_t vbit = L.lit[i] + (8ull * kb - L.r[i]) + (L.tflag[i] ? 1u : 1u + eg0_len(vb));
     if (!fi_record_ok(L, i, key_cap, val_cap)) {
       const bool prefix = i > 0 && L.r[i] > 8u * L.kbytes[i - 1];
       atomicOr(reinterpret_cast<unsigned long long*>(err),
@@ -799,7 +799,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
         for (uint32_t t = 0; t < own; ++t) key[t] = keys[ko + t];
         if (own < kb) fi_copy_to_lds(bits, L.lit[i] + (8ull * own - L.r[i]), key + own, kb - own);
       }
-      fi_copy_to_lds(bits, L.vbit[i], vwin + (vo - vbase), vb);
+      fi_copy_to_lds(bits, vbit, vwin + (vo - vbase), vb);
     } else {
       if (i == head) {
         const uint32_t own = fi_head_bytes(L, i);
@@ -807,7 +807,7 @@ __global__ __launch_bounds__(kFiBlock) void k_fi_records(FiBits bits, FiLayout L
       } else {
         chain = true;
       }
-      fi_copy_bytes(bits, L.vbit[i], vals + vo, vb);
+      fi_copy_bytes(bits, vbit, vals + vo, vb);
     }
   }
   if (r1 == L.S && threadIdx.x == 0) {
@@ -989,7 +989,7 @@ extern "C" int em_fcin_parse(const uint32_t* payload, uint64_t payload_words, ui
   const uint32_t G = static_cast<uint32_t>(
       std::max<uint64_t>(1, std::min<uint64_t>(kFiParseWave, (3 * 4 * kFiParseWords / 4) / mean_block)));
   hipLaunchKernelGGL(k_fi_parse, dim3((L.nb + G - 1) / G), dim3(kFiParseWave), 0, st, bits, T, S, L.nb, G, L.starts,
-                     L.r, L.kbytes, L.vbytes, L.lit, L.vbit, L.tflag, d_totals + 2);
+                     L.r, L.kbytes, L.vbytes, L.lit, L.tflag, d_totals + 2);
   int rc = check_launch();
   if (rc) return rc;
   rc = scan_launch<uint64_t>(L.kbytes, S + 1, L.koff, L.scan_ws, L.scan_bytes, st);
