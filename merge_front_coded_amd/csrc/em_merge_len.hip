@@ -237,8 +237,11 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
     const uint32_t idx = isB ? ref - A.n : ref;
     const uint32_t* vo = isB ? B.val_off : A.val_off;
     const uint8_t* tb = isB ? B.tomb : A.tomb;
-    v0[u] = vo[idx];
-    v1[u] = vo[idx + 1];
+    // (read once: streamed past the caches, which keeps the partition's key
+    // lines there longer for the checks and LCPs; measured 2% faster; the key
+    // offsets were slower so)
+    v0[u] = __builtin_nontemporal_load(vo + idx);
+    v1[u] = __builtin_nontemporal_load(vo + idx + 1);
     // (a side without tombstone flags reads a byte it then ignores)
     tv[u] = *(tb ? tb + idx : reinterpret_cast<const uint8_t*>(vo + idx));
   }
@@ -327,9 +330,9 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   for (int u = 0; u < IPT; ++u) {
     const uint32_t x = tid + u * kMlBlock;
     if (x >= n_kept) continue;
-    out.final_refs[g0 + x] = sref[u];
-    out.lcp_bits[g0 + x] = l[u];
-    out.toff[g0 + x] = tag | sb[u];
+    __builtin_nontemporal_store(sref[u], out.final_refs + g0 + x);
+    __builtin_nontemporal_store(l[u], out.lcp_bits + g0 + x);
+    __builtin_nontemporal_store(tag | sb[u], out.toff + g0 + x);
     if (out.len_bits) out.len_bits[g0 + x] = rlen[u];
   }
   if (out.ord_A)
