@@ -219,3 +219,39 @@ def test_prefix_cache_edges():
     B = gen.side_from_records(items[1::2])
     _prefix_cache_case(A, B, "edges")
     _prefix_cache_case(gen.side_from_records([(b"only", b"x")]), gen.side_from_records([]), "one record")
+
+
+@pytest.mark.parametrize("n", [4095, 4096, 4097, 8192, 12289])
+def test_prefix_cache_tile_boundaries(n):
+    """Record counts at and around whole tiles of the prefix scan (4096
+    records), one side empty: every record survives, so S = n."""
+    rng = np.random.default_rng(n)
+    keys = sorted({bytes(rng.integers(65, 70, int(rng.integers(1, 14)), dtype=np.uint8)) for _ in range(3 * n)})[:n]
+    assert len(keys) == n
+    A = gen.side_from_records([(k, b"v" * (i % 3)) for i, k in enumerate(keys)])
+    _prefix_cache_case(A, gen.side_from_records([]), f"{n} records")
+
+
+def test_prefix_cache_after_navigation_parse():
+    """Block starts from the navigation sections instead of the record
+    offsets: the same prefixes."""
+    import merge_front_coded_amd as em
+    A, B = workload(2, 0.004)
+    pl = run_gpu(A, B, items=256)
+    torch.cuda.synchronize()
+    S, T = pl.S, pl.T
+    sec = pl.ef_navigation()
+    out = []
+    for kw in ({"off": pl.off}, {"nav": sec}):
+        ws = torch.empty(max(em.em_fcin_workspace_bytes(S), 256), dtype=torch.uint8, device="cuda")
+        tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+        em.em_fcin_parse(pl.payload, T, S, tot, ws, **kw)
+        assert int(tot[2].item()) == 0
+        pfx = torch.empty(S, dtype=torch.int64, device="cuda")
+        em.em_fcin_prefix8(pl.payload, S, pfx, ws)
+        torch.cuda.synchronize()
+        out.append(pfx.cpu().numpy().view(np.uint64))
+    assert np.array_equal(out[0], out[1])
+    payload_h = np.frombuffer(pl.payload_bytes(), np.uint8)
+    want = oracle.fc_decode(payload_h, T, S, int(A.keys.size + B.keys.size) + 16, int(A.vals.size + B.vals.size) + 16)
+    assert np.array_equal(out[0], _first8(want))
