@@ -234,6 +234,7 @@ struct BpShared {
   uint4 stage[kBpStage / 16];
   uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
   uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
+  uint64_t src_at[4];               // global address of each staged span's first byte, less stage_at
 };
 
 __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
@@ -298,9 +299,12 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
         const uint32_t lo = sh.span_lo[q] & ~15u, hi = (sh.span_hi[q] + 4u + 15u) & ~15u;
         sh.span_lo[q] = lo;
         sh.span_hi[q] = hi;
+        const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
+        sh.src_at[q] = reinterpret_cast<uint64_t>(base) + lo - s_at;
         s_at += hi - lo;
       } else {
         sh.span_lo[q] = sh.span_hi[q] = 0;
+        sh.src_at[q] = 0;  // (no staged byte maps to an empty span)
       }
     }
     sh.stage_at[4] = s_at;
@@ -318,8 +322,7 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
       if (c < total16) {
         const uint32_t byte = c * 16;
         const uint32_t q = (byte >= at1) + (byte >= at2) + (byte >= at3);
-        const uint8_t* src = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
-        lds_dma16(src + sh.span_lo[q] + (byte - sh.stage_at[q]), sh.stage + c0);
+        lds_dma16(reinterpret_cast<const uint8_t*>(sh.src_at[q] + byte), sh.stage + c0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);

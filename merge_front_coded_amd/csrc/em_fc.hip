@@ -79,7 +79,9 @@ struct EmitShared {
   uint4 stage[kEmitStage / 16];
   uint32_t kbits[kEmitBlock];
   uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
+  uint4 wspan_lo[kEmitBlock / kWave], wspan_hi[kEmitBlock / kWave];  // each wave's bounds of the four
   uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
+  uint64_t src_at[4];               // global address of each staged span's first byte, less stage_at
   uint32_t kprev0;
   uint32_t next;  // the workgroup's next chunk ticket
   uint64_t bit_lo, bit_hi, bit_ext;
@@ -109,11 +111,11 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
   // groups of the payload are four-word groups of the window
   const uint64_t wb = (sh.bit_lo >> 7) << 7;
   const uint64_t w_lo = (sh.bit_lo + 31) >> 5;         // first owned word
-  const uint64_t w_hi = min((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
+  const uint64_t w_hi = min_u64((sh.bit_hi + 31) >> 5, (T + 31) >> 5);
   // bits past the last owned word are not needed
-  const uint64_t ext = min(sh.bit_ext, 32ull * w_hi);
+  const uint64_t ext = min_u64(sh.bit_ext, 32ull * w_hi);
   for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
-    const uint64_t s1 = min(s0 + 32ull * kEmitWindow, ext);
+    const uint64_t s1 = min_u64(s0 + 32ull * kEmitWindow, ext);
     const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
     for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
     __syncthreads();
@@ -149,10 +151,10 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
     if (s0 == wb && tid == 0) sh.next = ticket;
     __syncthreads();
     // owned words of this slice: 16-byte stores between a scalar head and tail
-    const uint64_t o_lo = max(w_lo, s0 >> 5), o_hi = min(w_hi, (s1 + 31) >> 5);
+    const uint64_t o_lo = max_u64(w_lo, s0 >> 5), o_hi = min_u64(w_hi, (s1 + 31) >> 5);
     const uint64_t wbase = s0 >> 5;  // global word number of window word 0
     auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
-    const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
+    const uint64_t a_lo = min_u64((o_lo + 3) & ~3ull, o_hi), a_hi = max_u64(o_hi & ~3ull, a_lo);
     for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
     // (non-temporal: the payload is written once and not read back here;
     // streaming it past the caches measured 2% faster than plain stores)
@@ -220,11 +222,6 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
   const uint32_t tid = threadIdx.x;
   const uint32_t nown = (S - R0) < rpb ? S - R0 : rpb;
   const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
-  if (tid < 4) {
-    sh.span_lo[tid] = 0xFFFFFFFFu;
-    sh.span_hi[tid] = 0;
-  }
-  __syncthreads();
 
   // ---- 1. this thread's record ----
   const uint32_t j = tid;
@@ -289,26 +286,44 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     const bool src = active && (j < nown || rec_off < 32ull * ((sh.bit_hi + 31) >> 5));
     const uint32_t klo = kpos + (l >> 3), khi = kpos + klen;
     const bool ks = src && klo < khi, vs = src && vlen != 0;
-    span_widen(ks && !isB, klo, khi, &sh.span_lo[0], &sh.span_hi[0]);
-    span_widen(ks && isB, klo, khi, &sh.span_lo[1], &sh.span_hi[1]);
-    span_widen(vs && !isB, vpos, vpos + vlen, &sh.span_lo[2], &sh.span_hi[2]);
-    span_widen(vs && isB, vpos, vpos + vlen, &sh.span_lo[3], &sh.span_hi[3]);
+    uint4 blo, bhi;  // (wave-uniform)
+    wave_bounds(ks && !isB, klo, khi, blo.x, bhi.x);
+    wave_bounds(ks && isB, klo, khi, blo.y, bhi.y);
+    wave_bounds(vs && !isB, vpos, vpos + vlen, blo.z, bhi.z);
+    wave_bounds(vs && isB, vpos, vpos + vlen, blo.w, bhi.w);
+    if ((tid & (kWave - 1)) == 0) {
+      sh.wspan_lo[tid / kWave] = blo;
+      sh.wspan_hi[tid / kWave] = bhi;
+    }
   }
   __syncthreads();
   if (tid == 0) {
+    uint32_t slo[4], shi[4];
+    for (int q = 0; q < 4; ++q) {
+      slo[q] = 0xFFFFFFFFu;
+      shi[q] = 0;
+    }
+    for (int w = 0; w < kEmitBlock / kWave; ++w) {
+      const uint4 a = sh.wspan_lo[w], b = sh.wspan_hi[w];
+      slo[0] = min(slo[0], a.x), slo[1] = min(slo[1], a.y), slo[2] = min(slo[2], a.z), slo[3] = min(slo[3], a.w);
+      shi[0] = max(shi[0], b.x), shi[1] = max(shi[1], b.y), shi[2] = max(shi[2], b.z), shi[3] = max(shi[3], b.w);
+    }
     uint32_t at = 0;
     for (int q = 0; q < 4; ++q) {
       sh.stage_at[q] = at;
-      if (sh.span_lo[q] < sh.span_hi[q]) {
-        const uint32_t lo = sh.span_lo[q] & ~15u;
+      if (slo[q] < shi[q]) {
+        const uint32_t lo = slo[q] & ~15u;
         // a 32-bit read at the last byte reaches at most 7 bytes past it
-        const uint32_t hi = (sh.span_hi[q] + 8u + 15u) & ~15u;
+        const uint32_t hi = (shi[q] + 8u + 15u) & ~15u;
         sh.span_lo[q] = lo;
         sh.span_hi[q] = hi;
+        const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
+        sh.src_at[q] = reinterpret_cast<uint64_t>(base) + lo - at;
         at += hi - lo;
       } else {
         sh.span_lo[q] = 0;
         sh.span_hi[q] = 0;
+        sh.src_at[q] = 0;  // (no staged byte maps to an empty span)
       }
     }
     sh.stage_at[4] = at;
@@ -335,8 +350,7 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
       if (c < total16) {
         const uint32_t byte = c * 16;
         const uint32_t q = (byte >= at1) + (byte >= at2) + (byte >= at3);
-        const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
-        lds_dma16(base + sh.span_lo[q] + (byte - sh.stage_at[q]), sh.stage + c0);
+        lds_dma16(reinterpret_cast<const uint8_t*>(sh.src_at[q] + byte), sh.stage + c0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);

@@ -167,8 +167,8 @@ __device__ __forceinline__ uint32_t fi_stage(uint32_t* __restrict__ lds, const F
   static_assert(kWords % (4 * kThreads) == 0, "whole rounds of 16-byte loads");
   constexpr int kIters = kWords / (4 * kThreads);
   w0 &= ~static_cast<uint64_t>(3);
-  w1 = min(w1, g.nwords);
-  const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min<uint64_t>(w1 - w0, kWords)) : 0u;
+  w1 = min_u64(w1, g.nwords);
+  const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min_u64(w1 - w0, kWords)) : 0u;
   const uint32_t n4 = n / 4;
   const uint4* src = reinterpret_cast<const uint4*>(g.w + w0);
   uint4 v[kIters];

@@ -110,26 +110,52 @@ __device__ __forceinline__ KeyRef key_of(const em_side_t& s, uint32_t r) {
   return KeyRef{p, s.key_off[r + 1] - p};
 }
 
+// Unsigned 64-bit min and max.  HIP's own min/max, given two different
+// 64-bit integer types (unsigned long and unsigned long long), resolve to
+// their double overload: a dozen VALU instructions through f64, exact only
+// below 2^53.
+__host__ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__host__ __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 // E(x) = 2 floor(log2(x+1)) + 1, the length of order-zero Exp-Golomb.
 __device__ __forceinline__ uint32_t eg0_len(uint64_t x) {
   return 2u * (63u - static_cast<uint32_t>(__builtin_clzll(x + 1))) + 1u;
+}
+
+// The bounds of this wave's selected lanes' ranges [lo, hi), for ranges that
+// increase with the lane (as in span_widen below): the first selected lane's
+// lo and the last one's hi, wave-uniform; (~0, 0) when no lane is selected.
+// Every active lane of the wave calls it.
+__device__ __forceinline__ void wave_bounds(bool sel, uint32_t lo, uint32_t hi, uint32_t& blo, uint32_t& bhi) {
+  const uint64_t m = __ballot(sel);
+  blo = 0xFFFFFFFFu;
+  bhi = 0;
+  if (m) {
+    blo = __builtin_amdgcn_readlane(lo, __builtin_ctzll(m));
+    bhi = __builtin_amdgcn_readlane(hi, 63 - __builtin_clzll(m));
+  }
 }
 
 // Widens a workgroup's byte span [*span_lo, *span_hi) (LDS) to cover the
 // ranges [lo, hi) of this wave's selected lanes, for ranges that increase
 // with the lane (a later selected lane's lo and hi are at least an earlier
 // one's, as for the records of one side in merged order): the first
-// selected lane holds the smallest lo and the last the largest hi, so one lane
-// each updates the bounds.  (An LDS atomic from every lane on the same word
-// is serialised by the LDS, one lane per cycle.)  Every lane of the wave
-// calls it.
+// selected lane holds the smallest lo and the last the largest hi, so the
+// first selected lane updates both bounds.  (An LDS atomic from every lane on
+// the same word is serialised by the LDS, one lane per cycle.)  Every active
+// lane of the wave calls it.
 __device__ __forceinline__ void span_widen(bool sel, uint32_t lo, uint32_t hi, uint32_t* span_lo,
                                            uint32_t* span_hi) {
   const uint64_t m = __ballot(sel);
   if (m) {
-    const uint32_t lane = __lane_id();
-    if (lane == static_cast<uint32_t>(__builtin_ctzll(m))) atomicMin(span_lo, lo);
-    if (lane == 63u - static_cast<uint32_t>(__builtin_clzll(m))) atomicMax(span_hi, hi);
+    const int first = __builtin_ctzll(m), last = 63 - __builtin_clzll(m);
+    // (wave-uniform operands: the atomics then compile to one lane's LDS
+    // atomic, not to a loop over the active lanes)
+    const uint32_t vlo = __builtin_amdgcn_readlane(lo, first), vhi = __builtin_amdgcn_readlane(hi, last);
+    if (__lane_id() == static_cast<uint32_t>(first)) {
+      atomicMin(span_lo, vlo);
+      atomicMax(span_hi, vhi);
+    }
   }
 }
 

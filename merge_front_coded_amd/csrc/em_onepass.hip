@@ -85,6 +85,7 @@ struct OpShared {
   uint32_t notes[kOpBlock];  // the merge's list of pairs to check, kWave words per wave
   uint32_t tile, i0, i1, g0, cp, carry;
   uint32_t span_lo[4], span_hi[4], stage_at[5];  // A keys, B keys, A values, B values
+  uint64_t src_at[4];     // global address of each staged span's first byte, less stage_at
   uint64_t base;          // the partition's bit base
   uint64_t clo, chi;      // the chunk's local bit range
 };
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
                          (sh.a_voff[nA_t] - sh.a_voff[0]) + (sh.b_voff[nB_t] - sh.b_voff[0]);
     const uint64_t by_bits = (static_cast<uint64_t>(kOpWin) * 32u * 9u / 10u) * n_kept / (tbits ? tbits : 1);
     const uint64_t by_src = (static_cast<uint64_t>(kOpStage) * 85u / 100u) * n_kept / (src + 16u * len + 1u);
-    const uint64_t c = min(by_bits, by_src);
+    const uint64_t c = min_u64(by_bits, by_src);
     cs = c < 1 ? 1u : (c > kOpMaxChunk ? kOpMaxChunk : static_cast<uint32_t>(c));
   }
   cs = __builtin_amdgcn_readfirstlane(cs);
@@ -610,10 +611,13 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
           const uint32_t shi = (sh.span_hi[q] + 8u + 15u) & ~15u;
           sh.span_lo[q] = slo;
           sh.span_hi[q] = shi;
+          const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
+          sh.src_at[q] = reinterpret_cast<uint64_t>(base) + slo - at;
           at += shi - slo;
         } else {
           sh.span_lo[q] = 0;
           sh.span_hi[q] = 0;
+          sh.src_at[q] = 0;  // (no staged byte maps to an empty span)
         }
       }
       sh.stage_at[4] = at;
@@ -632,8 +636,7 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
         if (c < total16) {
           const uint32_t byte = c * 16;
           const uint32_t q = (byte >= at1) + (byte >= at2) + (byte >= at3);
-          const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
-          lds_dma16(base + sh.span_lo[q] + (byte - sh.stage_at[q]), sh.u.e.stage + c0);
+          lds_dma16(reinterpret_cast<const uint8_t*>(sh.src_at[q] + byte), sh.u.e.stage + c0);
         }
       }
     }
@@ -682,11 +685,11 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
     // the words before its predecessor's end that the predecessor left partial
     const uint64_t alo = Bt + clo, ahi = Bt + chi;
     const uint64_t first_full = (Bt + 31) >> 5;  // the partition's first word of its own
-    uint64_t next_w = max(first_full, alo >> 5);  // next word to store
+    uint64_t next_w = max_u64(first_full, alo >> 5);  // next word to store
     const uint64_t ro = Bt + lo, re = ro + rl;
     const bool whole = ((ahi - ((alo >> 7) << 7) + 31) >> 5) <= kOpWin;  // (uniform) one slice
     for (uint64_t s0 = (alo >> 7) << 7;;) {
-      const uint64_t s1 = min(s0 + 32ull * kOpWin, ahi);
+      const uint64_t s1 = min_u64(s0 + 32ull * kOpWin, ahi);
       const uint64_t wbase = s0 >> 5;
       const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
       for (uint32_t i = tid; i < used4; i += kOpBlock) reinterpret_cast<uint4*>(win)[i] = uint4{0, 0, 0, 0};
@@ -712,9 +715,9 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
       __syncthreads();
       // complete words of this slice: 16-byte stores between a head and a tail
       auto wv = [&](uint64_t w) { return __builtin_bswap32(win[static_cast<uint32_t>(w - wbase)]); };
-      const uint64_t o_lo = max(next_w, wbase), o_hi = s1 >> 5;
+      const uint64_t o_lo = max_u64(next_w, wbase), o_hi = s1 >> 5;
       if (o_lo < o_hi) {
-        const uint64_t a_lo = min((o_lo + 3) & ~3ull, o_hi), a_hi = max(o_hi & ~3ull, a_lo);
+        const uint64_t a_lo = min_u64((o_lo + 3) & ~3ull, o_hi), a_hi = max_u64(o_hi & ~3ull, a_lo);
         for (uint64_t w = o_lo + tid; w < a_lo; w += kOpBlock) out.payload[w] = wv(w);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
         for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kOpBlock) {
