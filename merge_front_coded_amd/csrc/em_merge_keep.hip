@@ -83,14 +83,16 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   const uint32_t nb_off = nB_t + (has_next_b ? 2u : 1u);
 
   {
-    // all offset loads first, then the LDS stores, so the loads overlap in flight
+    // all offset loads first, then the LDS stores, so the loads overlap in
+    // flight (a thread past the end loads the first offset again, so that no
+    // load sits under a condition of its own)
     constexpr int kPer = IPT + 1;  // ceil((kTile + 2) / kMergeBlock)
     uint32_t va[kPer], vb[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint32_t x = tid + u * kMergeBlock;
-      va[u] = x <= nA_t ? A.key_off[i0 + x] : 0u;
-      vb[u] = x < nb_off ? B.key_off[j0 + x] : 0u;
+      va[u] = A.key_off[i0 + (x <= nA_t ? x : 0u)];
+      vb[u] = B.key_off[j0 + (x < nb_off ? x : 0u)];
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -104,17 +106,8 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_keep(
   // ---- prefix cache (the keys themselves stay in HBM: comparisons the
   // prefixes leave open read them in place, and the small LDS footprint
   // keeps more partitions resident) ----
-  {
-    const uint32_t nb_keys = nb_off - 1;
-    for (uint32_t x = tid; x < nA_t; x += kMergeBlock) {
-      const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0;
-      sh.u.m.a_pfx[x] = load_be8(A.keys, p0) & be_mask(ln < 8 ? ln : 8);
-    }
-    for (uint32_t y = tid; y < nb_keys; y += kMergeBlock) {
-      const uint32_t p0 = sh.b_off[y], ln = sh.b_off[y + 1] - p0;
-      sh.u.m.b_pfx[y] = load_be8(B.keys, p0) & be_mask(ln < 8 ? ln : 8);
-    }
-  }
+  fill_prefix_caches<kMergeBlock, IPT + 1>(PfxSide{sh.a_off, nA_t + 1, A.keys, sh.u.m.a_pfx},
+                                           PfxSide{sh.b_off, nb_off, B.keys, sh.u.m.b_pfx}, 0u);
   __syncthreads();
 
   // ---- merge this thread's slice ----

@@ -117,15 +117,17 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   const uint32_t na_off = i1 - aK0 + 1;
   const uint32_t nb_off = j1 + (has_next_b ? 1u : 0u) - bK0 + 1;
 
-  // ---- 2. key offsets (all loads, then all stores) ----
+  // ---- 2. key offsets (all loads, then all stores; a thread past the end
+  // loads the first offset again, so that no load sits under a condition
+  // of its own) ----
   {
     constexpr int kPer = IPT + 1;  // ceil((kTile + 4) / kMlBlock)
     uint32_t ka[kPer], kb[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint32_t x = tid + u * kMlBlock;
-      ka[u] = x < na_off ? A.key_off[aK0 + x] : 0u;
-      kb[u] = x < nb_off ? B.key_off[bK0 + x] : 0u;
+      ka[u] = A.key_off[aK0 + (x < na_off ? x : 0u)];
+      kb[u] = B.key_off[bK0 + (x < nb_off ? x : 0u)];
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -141,26 +143,8 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   // least 8 bytes long (all loads, then all stores) ----
   auto load_cache = [&](uint32_t cp) {
     constexpr int kPer = IPT + 1;  // ceil((kTile + 3) / kMlBlock)
-    uint64_t pa[kPer], pb[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t x = tid + u * kMlBlock;
-      pa[u] = pb[u] = 0;
-      if (x + 1 < na_off) {
-        const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0 - cp;
-        pa[u] = load_be8(A.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
-      }
-      if (x + 1 < nb_off) {
-        const uint32_t p0 = sh.b_off[x], ln = sh.b_off[x + 1] - p0 - cp;
-        pb[u] = load_be8(B.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t x = tid + u * kMlBlock;
-      if (x + 1 < na_off) sh.u.m.a_pfx[x] = pa[u];
-      if (x + 1 < nb_off) sh.u.m.b_pfx[x] = pb[u];
-    }
+    fill_prefix_caches<kMlBlock, kPer>(PfxSide{sh.a_off, na_off, A.keys, sh.u.m.a_pfx},
+                                       PfxSide{sh.b_off, nb_off, B.keys, sh.u.m.b_pfx}, cp);
   };
   load_cache(0);
   __syncthreads();

@@ -297,7 +297,9 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
   const uint32_t na_off = i1 - aK0 + 1;
   const uint32_t nb_off = j1 + (has_next_b ? 1u : 0u) - bK0 + 1;
 
-  // ---- 2. key offsets, value offsets, tombstone flags (all loads, then all stores) ----
+  // ---- 2. key offsets, value offsets, tombstone flags (all loads, then all
+  // stores; a thread past the end reads a valid entry and drops it, so that
+  // no load sits under a condition of its own) ----
   {
     constexpr int kPer = IPT + 1;  // ceil((kTile + 4) / kOpBlock)
     uint32_t ka[kPer], kb[kPer], va[kPer], vb[kPer];
@@ -305,16 +307,20 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const uint32_t x = tid + u * kOpBlock;
-      ka[u] = x < na_off ? A.key_off[aK0 + x] : 0u;
-      kb[u] = x < nb_off ? B.key_off[bK0 + x] : 0u;
-      va[u] = x <= nA_t ? A.val_off[i0 + x] : 0u;
-      vb[u] = x <= nB_t ? B.val_off[j0 + x] : 0u;
+      ka[u] = A.key_off[aK0 + (x < na_off ? x : 0u)];
+      kb[u] = B.key_off[bK0 + (x < nb_off ? x : 0u)];
+      va[u] = A.val_off[i0 + (x <= nA_t ? x : 0u)];
+      vb[u] = B.val_off[j0 + (x <= nB_t ? x : 0u)];
     }
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const uint32_t x = tid + u * kOpBlock;
-      ta[u] = (x < nA_t && A.tomb) ? A.tomb[i0 + x] : uint8_t(0);
-      tb[u] = (x < nB_t && B.tomb) ? B.tomb[j0 + x] : uint8_t(0);
+      const bool ha = x < nA_t && A.tomb, hb = x < nB_t && B.tomb;
+      // (without a flag to read, the side's first value offset is read instead)
+      ta[u] = *(ha ? A.tomb + i0 + x : reinterpret_cast<const uint8_t*>(A.val_off + i0));
+      tb[u] = *(hb ? B.tomb + j0 + x : reinterpret_cast<const uint8_t*>(B.val_off + j0));
+      if (!ha) ta[u] = 0;
+      if (!hb) tb[u] = 0;
     }
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
@@ -336,26 +342,8 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
   // ---- 3. prefix cache (offset 0, then at the common prefix when it is long) ----
   auto load_cache = [&](uint32_t cp) {
     constexpr int kPer = IPT + 1;
-    uint64_t pa[kPer], pb[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t x = tid + u * kOpBlock;
-      pa[u] = pb[u] = 0;
-      if (x + 1 < na_off) {
-        const uint32_t p0 = sh.a_off[x], ln = sh.a_off[x + 1] - p0 - cp;
-        pa[u] = load_be8(A.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
-      }
-      if (x + 1 < nb_off) {
-        const uint32_t p0 = sh.b_off[x], ln = sh.b_off[x + 1] - p0 - cp;
-        pb[u] = load_be8(B.keys, p0 + cp) & be_mask(ln < 8 ? ln : 8);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t x = tid + u * kOpBlock;
-      if (x + 1 < na_off) sh.u.m.a_pfx[x] = pa[u];
-      if (x + 1 < nb_off) sh.u.m.b_pfx[x] = pb[u];
-    }
+    fill_prefix_caches<kOpBlock, kPer>(PfxSide{sh.a_off, na_off, A.keys, sh.u.m.a_pfx},
+                                       PfxSide{sh.b_off, nb_off, B.keys, sh.u.m.b_pfx}, cp);
   };
   load_cache(0);
   __syncthreads();

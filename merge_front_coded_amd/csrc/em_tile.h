@@ -403,6 +403,54 @@ __device__ __forceinline__ uint32_t cache_offset(const uint32_t* a_off, uint32_t
   return __builtin_amdgcn_readfirstlane(*flag);
 }
 
+// The prefix caches of both sides' keys whose offsets are in LDS: for each
+// side, pfx[x] (x + 1 < n_off) is bytes [cp, cp + 8) of key x (bytes
+// offs[x] .. offs[x+1] of its arena) as a big-endian word, zero past the
+// key's end.  The thread takes x = threadIdx.x + u * kThreads for u < kPer.
+// Every load of both sides is issued before any is waited for, whatever x
+// is (a thread past the end reads its arena's first bytes and drops them):
+// a load under a condition of its own was compiled into a branch with the
+// wait for it inside, one memory round trip per load.
+struct PfxSide {
+  const uint32_t* offs;
+  uint32_t n_off;
+  const uint8_t* keys;
+  uint64_t* pfx;
+};
+
+template <int kThreads, int kPer>
+__device__ __forceinline__ void fill_prefix_caches(const PfxSide& a, const PfxSide& b, uint32_t cp) {
+  // (at most five rounds of both sides in flight: ten 12-byte loads)
+  constexpr int kBatch = 5;
+#pragma unroll
+  for (int u0 = 0; u0 < kPer; u0 += kBatch) {
+    uint64_t v[2][kBatch];
+    uint32_t nb[2][kBatch];
+#pragma unroll
+    for (int du = 0; du < kBatch && u0 + du < kPer; ++du) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const PfxSide& sd = q ? b : a;
+        const uint32_t x = threadIdx.x + (u0 + du) * kThreads;
+        const bool ok = x + 1 < sd.n_off;
+        const uint32_t xs = ok ? x : 0u;  // (an index inside the offsets either way)
+        const uint32_t p0 = sd.offs[xs], ln = sd.offs[xs + 1] - p0 - cp;
+        nb[q][du] = ok ? (ln < 8u ? ln : 8u) : 0u;
+        v[q][du] = load_be8(sd.keys, ok ? p0 + cp : 0u);
+      }
+    }
+#pragma unroll
+    for (int du = 0; du < kBatch && u0 + du < kPer; ++du) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const PfxSide& sd = q ? b : a;
+        const uint32_t x = threadIdx.x + (u0 + du) * kThreads;
+        if (x + 1 < sd.n_off) sd.pfx[x] = v[q][du] & be_mask(nb[q][du]);
+      }
+    }
+  }
+}
+
 // 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
 __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
   const uint32_t* p = base + (bp >> 5);
