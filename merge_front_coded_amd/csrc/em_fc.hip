@@ -116,9 +116,11 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
   const uint64_t ext = min_u64(sh.bit_ext, 32ull * w_hi);
   for (uint64_t s0 = wb; s0 < ext && (s0 >> 5) < w_hi; s0 += 32ull * kEmitWindow) {
     const uint64_t s1 = min_u64(s0 + 32ull * kEmitWindow, ext);
-    const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
-    for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
-    __syncthreads();
+    if (s0 != wb) {  // (the window arrives zeroed for the first slice)
+      const uint32_t used4 = static_cast<uint32_t>(((s1 - s0 + 31) / 32 + 3) / 4);
+      for (uint32_t i = tid; i < used4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
+      __syncthreads();
+    }
     if (r.live && r.off < s1 && r.end > s0) {
       // this record's bits inside [s0, s1), relative to the record start
       const uint32_t from = r.off >= s0 ? 0u : static_cast<uint32_t>(s0 - r.off);
@@ -150,21 +152,24 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
     }
     if (s0 == wb && tid == 0) sh.next = ticket;
     __syncthreads();
-    // owned words of this slice: 16-byte stores between a scalar head and tail
-    const uint64_t o_lo = max_u64(w_lo, s0 >> 5), o_hi = min_u64(w_hi, (s1 + 31) >> 5);
-    const uint64_t wbase = s0 >> 5;  // global word number of window word 0
-    auto win = [&](uint64_t w) { return __builtin_bswap32(sh.out[static_cast<uint32_t>(w - wbase)]); };
-    const uint64_t a_lo = min_u64((o_lo + 3) & ~3ull, o_hi), a_hi = max_u64(o_hi & ~3ull, a_lo);
-    for (uint64_t w = o_lo + tid; w < a_lo; w += kEmitBlock) payload[w] = win(w);
+    // owned words of this slice: 16-byte stores between a scalar head and
+    // tail; indices are relative to window word 0 (payload word s0 / 32, a
+    // multiple of four)
+    const uint64_t wbase = s0 >> 5;
+    uint32_t* const dst = payload + wbase;
+    const uint32_t o_lo = static_cast<uint32_t>(max_u64(w_lo, wbase) - wbase);
+    const uint32_t o_hi = static_cast<uint32_t>(min_u64(w_hi, (s1 + 31) >> 5) - wbase);
+    const uint32_t a_lo = min((o_lo + 3u) & ~3u, o_hi), a_hi = max(o_hi & ~3u, a_lo);
+    for (uint32_t i = o_lo + tid; i < a_lo; i += kEmitBlock) dst[i] = __builtin_bswap32(sh.out[i]);
     // (non-temporal: the payload is written once and not read back here;
     // streaming it past the caches measured 2% faster than plain stores)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kEmitBlock) {
-      const uint4 v = reinterpret_cast<const uint4*>(sh.out)[static_cast<uint32_t>(w - wbase) / 4];
+    for (uint32_t i = a_lo + 4 * tid; i < a_hi; i += 4 * kEmitBlock) {
+      const uint4 v = reinterpret_cast<const uint4*>(sh.out)[i / 4];
       const u32x4 q = {__builtin_bswap32(v.x), __builtin_bswap32(v.y), __builtin_bswap32(v.z), __builtin_bswap32(v.w)};
-      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(payload + w));
+      __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(dst + i));
     }
-    for (uint64_t w = a_hi + tid; w < o_hi; w += kEmitBlock) payload[w] = win(w);
+    for (uint32_t i = a_hi + tid; i < o_hi; i += kEmitBlock) dst[i] = __builtin_bswap32(sh.out[i]);
     __syncthreads();
   }
   if (!(wb < ext && (wb >> 5) < w_hi)) {  // no slice (offsets that leave the chunk no bits)
@@ -222,6 +227,10 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
   const uint32_t tid = threadIdx.x;
   const uint32_t nown = (S - R0) < rpb ? S - R0 : rpb;
   const uint32_t cnt = (S - R0) < rpb + kEmitExtra ? S - R0 : rpb + kEmitExtra;
+  // The window starts zeroed for the first slice (the previous chunk's last
+  // barrier ended its reads of the window; several barriers follow before
+  // the first bits are placed).
+  for (uint32_t i = tid; i < kEmitWindow / 4; i += kEmitBlock) reinterpret_cast<uint4*>(sh.out)[i] = uint4{0, 0, 0, 0};
 
   // ---- 1. this thread's record ----
   const uint32_t j = tid;

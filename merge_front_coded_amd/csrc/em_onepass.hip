@@ -705,16 +705,19 @@ __global__ __launch_bounds__(kOpBlock) __attribute__((amdgpu_waves_per_eu(4))) v
       auto wv = [&](uint64_t w) { return __builtin_bswap32(win[static_cast<uint32_t>(w - wbase)]); };
       const uint64_t o_lo = max_u64(next_w, wbase), o_hi = s1 >> 5;
       if (o_lo < o_hi) {
-        const uint64_t a_lo = min_u64((o_lo + 3) & ~3ull, o_hi), a_hi = max_u64(o_hi & ~3ull, a_lo);
-        for (uint64_t w = o_lo + tid; w < a_lo; w += kOpBlock) out.payload[w] = wv(w);
+        // (indices relative to window word 0, payload word wbase, a multiple of four)
+        uint32_t* const dst = out.payload + wbase;
+        const uint32_t r_lo = static_cast<uint32_t>(o_lo - wbase), r_hi = static_cast<uint32_t>(o_hi - wbase);
+        const uint32_t a_lo = min((r_lo + 3u) & ~3u, r_hi), a_hi = max(r_hi & ~3u, a_lo);
+        for (uint32_t i = r_lo + tid; i < a_lo; i += kOpBlock) dst[i] = __builtin_bswap32(win[i]);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        for (uint64_t w = a_lo + 4 * tid; w < a_hi; w += 4 * kOpBlock) {
-          const uint4 v = reinterpret_cast<const uint4*>(win)[static_cast<uint32_t>(w - wbase) / 4];
+        for (uint32_t i = a_lo + 4 * tid; i < a_hi; i += 4 * kOpBlock) {
+          const uint4 v = reinterpret_cast<const uint4*>(win)[i / 4];
           const u32x4 q = {__builtin_bswap32(v.x), __builtin_bswap32(v.y), __builtin_bswap32(v.z),
                            __builtin_bswap32(v.w)};
-          __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(out.payload + w));
+          __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(dst + i));
         }
-        for (uint64_t w = a_hi + tid; w < o_hi; w += kOpBlock) out.payload[w] = wv(w);
+        for (uint32_t i = a_hi + tid; i < r_hi; i += kOpBlock) dst[i] = __builtin_bswap32(win[i]);
         next_w = o_hi;
       }
       if (tid == 0) {
