@@ -103,6 +103,7 @@ struct EmitRecord {
 // slice by slice, and each slice's owned words are copied out.  Thread 0
 // publishes `ticket` in sh.next before the first copy-out (it waits for the
 // ticket's atomic there, after the window is built).
+template <typename Pos>  // source bit positions: uint32_t for staged sources (LDS), uint64_t otherwise
 __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r, const uint32_t* kbase,
                                             const uint32_t* vbase, uint64_t T, uint32_t* payload,
                                             uint32_t ticket) {
@@ -138,7 +139,7 @@ __device__ __forceinline__ void emit_slices(EmitShared& sh, const EmitRecord& r,
       };
       auto span = [&](const uint32_t* base, uint64_t bp, uint32_t a, uint32_t b) {
         const uint32_t lo = max(a, from), hi = min(b, to);
-        if (lo < hi) or_span(sh.out, p0 + (lo - from), base, bp + (lo - a), hi - lo);
+        if (lo < hi) or_span<Pos>(sh.out, p0 + (lo - from), base, static_cast<Pos>(bp) + (lo - a), hi - lo);
       };
       if (r.b2 <= 64u) {
         imm((static_cast<uint64_t>(r.c) + 1u) << (r.b2 - r.b1) | (static_cast<uint64_t>(r.k - r.l) + 1u), 0, r.b2);
@@ -390,11 +391,11 @@ __device__ __forceinline__ void emit_chunk(EmitShared& sh, const em_side_t& A, c
     rec.kbit = 8ull * (kpos + (l >> 3) - sh.span_lo[qk] + sh.stage_at[qk]) + (l & 7u);
     rec.vbit = 8ull * (vpos - sh.span_lo[qv] + sh.stage_at[qv]);
     const uint32_t* st = reinterpret_cast<const uint32_t*>(sh.stage);
-    emit_slices(sh, rec, st, st, T, payload, ticket);
+    emit_slices<uint32_t>(sh, rec, st, st, T, payload, ticket);
   } else {
     rec.kbit = 8ull * kpos + l;
     rec.vbit = 8ull * vpos;
-    emit_slices(sh, rec, reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys),
+    emit_slices<uint64_t>(sh, rec, reinterpret_cast<const uint32_t*>(isB ? B.keys : A.keys),
                 reinterpret_cast<const uint32_t*>(isB ? B.vals : A.vals), T, payload, ticket);
   }
 }

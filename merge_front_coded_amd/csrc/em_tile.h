@@ -451,8 +451,12 @@ __device__ __forceinline__ void fill_prefix_caches(const PfxSide& a, const PfxSi
   }
 }
 
+// Source bit positions are 32-bit for a source in LDS (a staged span) and
+// 64-bit for an arena in global memory.
+
 // 32 source bits starting at bit `bp` of a dword array (MSB-first stream order)
-__device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp) {
+template <typename Pos>
+__device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, Pos bp) {
   const uint32_t* p = base + (bp >> 5);
   const uint32_t hi = __builtin_bswap32(p[0]), lo = __builtin_bswap32(p[1]);
   const uint32_t sh = static_cast<uint32_t>(bp & 31u);
@@ -469,7 +473,8 @@ __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, uint64_t bp)
 // stored; the bits of the partial word W (when f2 = (f + n) mod 32 > 0) are
 // returned.  Reads reach at most one dword past the one holding the span's
 // last bit.
-__device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base, uint64_t bp, uint32_t f,
+template <typename Pos>
+__device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base, Pos bp, uint32_t f,
                                                uint32_t W, uint32_t f2) {
   // P >= 1: bits of dwords (P - 1) / 32 and the next, shifted right by -P
   // mod 32 (a shift of 0 gives the second dword)
@@ -478,20 +483,21 @@ __device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base
   o += 1;
   const uint32_t cnt = W - 1;  // words 1 .. W-1 go to o[0 .. cnt)
   uint32_t cur = __builtin_bswap32(p[0]);
-  uint32_t t = 0;
-  for (; t + 4 <= cnt; t += 4) {  // four source dwords in flight per iteration
-    const uint32_t n1 = __builtin_bswap32(p[t + 1]), n2 = __builtin_bswap32(p[t + 2]);
-    const uint32_t n3 = __builtin_bswap32(p[t + 3]), n4 = __builtin_bswap32(p[t + 4]);
-    o[t] = __builtin_amdgcn_alignbit(cur, n1, sh);
-    o[t + 1] = __builtin_amdgcn_alignbit(n1, n2, sh);
-    o[t + 2] = __builtin_amdgcn_alignbit(n2, n3, sh);
-    o[t + 3] = __builtin_amdgcn_alignbit(n3, n4, sh);
+  // (the loop's end is computed up front, so that its counter is not needed
+  // after it)
+  const uint32_t t = cnt & ~3u, rem = cnt & 3u;
+  for (uint32_t i = 0; i < t; i += 4) {  // four source dwords in flight per iteration
+    const uint32_t n1 = __builtin_bswap32(p[i + 1]), n2 = __builtin_bswap32(p[i + 2]);
+    const uint32_t n3 = __builtin_bswap32(p[i + 3]), n4 = __builtin_bswap32(p[i + 4]);
+    o[i] = __builtin_amdgcn_alignbit(cur, n1, sh);
+    o[i + 1] = __builtin_amdgcn_alignbit(n1, n2, sh);
+    o[i + 2] = __builtin_amdgcn_alignbit(n2, n3, sh);
+    o[i + 3] = __builtin_amdgcn_alignbit(n3, n4, sh);
     cur = n4;
   }
   // up to three more words, then the partial word (source dwords t+1 ..
   // t+rem, and one more when f2 > 0; indices past the last one needed re-read
   // it)
-  const uint32_t rem = cnt - t;
   const uint32_t last = t + rem + (f2 ? 1u : 0u);
   const uint32_t m1 = __builtin_bswap32(p[min(t + 1, last)]), m2 = __builtin_bswap32(p[min(t + 2, last)]);
   const uint32_t m3 = __builtin_bswap32(p[min(t + 3, last)]), m4 = __builtin_bswap32(p[min(t + 4, last)]);
@@ -523,7 +529,8 @@ __device__ __forceinline__ void or_bits64(uint32_t* out, uint32_t p, uint64_t v,
 // Direct placement of source bits [bp, bp + n) of a dword array at window bit
 // p: the first and the last word, which neighbouring fields may share, are
 // ORed, and every word between them is stored.
-__device__ __forceinline__ void or_span(uint32_t* out, uint32_t p, const uint32_t* base, uint64_t bp, uint32_t n) {
+template <typename Pos>
+__device__ __forceinline__ void or_span(uint32_t* out, uint32_t p, const uint32_t* base, Pos bp, uint32_t n) {
   if (n == 0) return;
   const uint32_t f = p & 31u;
   uint32_t* o = out + (p >> 5);
