@@ -233,6 +233,7 @@ struct BpShared {
   uint4 win[kBpWin / 16];
   uint4 stage[kBpStage / 16];
   uint32_t span_lo[4], span_hi[4];  // byte spans of the four sources
+  uint4 wspan_lo[kBpBlock / kWave], wspan_hi[kBpBlock / kWave];  // each wave's bounds of the four
   uint32_t stage_at[5];             // LDS byte offset of each staged span, [4] = total
   uint64_t src_at[4];               // global address of each staged span's first byte, less stage_at
 };
@@ -252,11 +253,6 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
   const uint64_t base = b0 & ~static_cast<uint64_t>(15);
   const bool staged = b0 <= b1 && b1 <= cap && b1 - base <= kBpWin;  // (uniform over the workgroup)
   const uint32_t W = d_width[0];
-  if (tid < 4) {
-    sh.span_lo[tid] = 0xFFFFFFFFu;
-    sh.span_hi[tid] = 0;
-  }
-  __syncthreads();
   const uint32_t i = r0 + tid;
   bool ok = false;
   BpRec r{};
@@ -277,12 +273,17 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
       vn = r.tomb ? 0u : r.vlen;
     }
   }
-  if (staged) {  // (uniform) a side's records are in arena order: see span_widen
+  if (staged) {  // (uniform) a side's records are in arena order: see wave_bounds
     const bool ks = ok && r.sfx != 0, vs = ok && vn != 0;
-    span_widen(ks && !r.isB, r.kpos, r.kpos + r.sfx, &sh.span_lo[0], &sh.span_hi[0]);
-    span_widen(ks && r.isB, r.kpos, r.kpos + r.sfx, &sh.span_lo[1], &sh.span_hi[1]);
-    span_widen(vs && !r.isB, r.vpos, r.vpos + vn, &sh.span_lo[2], &sh.span_hi[2]);
-    span_widen(vs && r.isB, r.vpos, r.vpos + vn, &sh.span_lo[3], &sh.span_hi[3]);
+    uint4 blo, bhi;  // (wave-uniform)
+    wave_bounds(ks && !r.isB, r.kpos, r.kpos + r.sfx, blo.x, bhi.x);
+    wave_bounds(ks && r.isB, r.kpos, r.kpos + r.sfx, blo.y, bhi.y);
+    wave_bounds(vs && !r.isB, r.vpos, r.vpos + vn, blo.z, bhi.z);
+    wave_bounds(vs && r.isB, r.vpos, r.vpos + vn, blo.w, bhi.w);
+    if ((tid & (kWave - 1)) == 0) {
+      sh.wspan_lo[tid / kWave] = blo;
+      sh.wspan_hi[tid / kWave] = bhi;
+    }
   }
   if (!staged) {  // (uniform)
     if (ok)
@@ -291,12 +292,22 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
   }
   __syncthreads();
   if (tid == 0) {
+    uint32_t slo[4], shi[4];
+    for (int q = 0; q < 4; ++q) {
+      slo[q] = 0xFFFFFFFFu;
+      shi[q] = 0;
+    }
+    for (int w = 0; w < kBpBlock / kWave; ++w) {
+      const uint4 a = sh.wspan_lo[w], b = sh.wspan_hi[w];
+      slo[0] = min(slo[0], a.x), slo[1] = min(slo[1], a.y), slo[2] = min(slo[2], a.z), slo[3] = min(slo[3], a.w);
+      shi[0] = max(shi[0], b.x), shi[1] = max(shi[1], b.y), shi[2] = max(shi[2], b.z), shi[3] = max(shi[3], b.w);
+    }
     uint32_t s_at = 0;
     for (int q = 0; q < 4; ++q) {
       sh.stage_at[q] = s_at;
-      if (sh.span_lo[q] < sh.span_hi[q]) {
+      if (slo[q] < shi[q]) {
         // the copy reads up to 4 bytes past a span's last byte
-        const uint32_t lo = sh.span_lo[q] & ~15u, hi = (sh.span_hi[q] + 4u + 15u) & ~15u;
+        const uint32_t lo = slo[q] & ~15u, hi = (shi[q] + 4u + 15u) & ~15u;
         sh.span_lo[q] = lo;
         sh.span_hi[q] = hi;
         const uint8_t* base = q == 0 ? A.keys : q == 1 ? B.keys : q == 2 ? A.vals : B.vals;
@@ -343,12 +354,18 @@ __global__ __launch_bounds__(kBpBlock) void k_bp_emit(em_side_t A, em_side_t B,
     }
   }
   __syncthreads();
+  // 16-byte groups of the window, counted from `base`: [g_lo, g_hi) lie
+  // whole inside [b0, b1) and are stored at once; the (at most two) groups
+  // outside that range, which the workgroup shares with its neighbours, go
+  // byte by byte
   const uint32_t groups = static_cast<uint32_t>((b1 - base + 15) >> 4);
-  for (uint32_t g = tid; g < groups; g += kBpBlock) {
-    const uint64_t a = base + 16ull * g;
-    if (a >= b0 && a + 16 <= b1) {
-      *reinterpret_cast<uint4*>(payload + a) = sh.win[g];
-    } else {
+  const uint32_t g_lo = static_cast<uint32_t>((b0 - base + 15) >> 4), g_hi = static_cast<uint32_t>((b1 - base) >> 4);
+  uint4* const dst = reinterpret_cast<uint4*>(payload + base);
+  for (uint32_t g = g_lo + tid; g < g_hi; g += kBpBlock) dst[g] = sh.win[g];
+  if (tid < 2) {
+    const uint32_t g = tid == 0 ? 0u : g_hi;
+    if (g < groups && (g < g_lo || g >= g_hi) && !(tid == 1 && g == 0)) {
+      const uint64_t a = base + 16ull * g;
       for (uint32_t t = 0; t < 16; ++t)
         if (a + t >= b0 && a + t < b1) payload[a + t] = win[16 * g + t];
     }
