@@ -171,16 +171,25 @@ __device__ __forceinline__ uint32_t fi_stage(uint32_t* __restrict__ lds, const F
   const uint32_t n = w1 > w0 ? static_cast<uint32_t>(min_u64(w1 - w0, kWords)) : 0u;
   const uint32_t n4 = n / 4;
   const uint4* src = reinterpret_cast<const uint4*>(g.w + w0);
-  uint4 v[kIters];
+  if (n4) {  // (uniform)
+    // Every load is issued whatever x is (a lane past the end loads group 0
+    // again), and every loaded value is used once outside the stores'
+    // conditions (an empty asm), so that the compiler keeps the loads
+    // together: a load left to its store's branch was compiled with the wait
+    // for it right behind it, one memory round trip per load.
+    uint4 v[kIters];
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const uint32_t x = threadIdx.x + it * kThreads;
-    if (x < n4) v[it] = src[x];
-  }
+    for (int it = 0; it < kIters; ++it) {
+      const uint32_t x = threadIdx.x + it * kThreads;
+      v[it] = src[x < n4 ? x : 0u];
+    }
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    const uint32_t x = threadIdx.x + it * kThreads;
-    if (x < n4) reinterpret_cast<uint4*>(lds)[x] = v[it];
+    for (int it = 0; it < kIters; ++it) asm volatile("" ::"v"(v[it].x));
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const uint32_t x = threadIdx.x + it * kThreads;
+      if (x < n4) reinterpret_cast<uint4*>(lds)[x] = v[it];
+    }
   }
   for (uint32_t t = 4 * n4 + threadIdx.x; t < n; t += kThreads) lds[t] = g.w[w0 + t];
   return n;
