@@ -112,7 +112,7 @@ __device__ __forceinline__ KeyRef key_of(const em_side_t& s, uint32_t r) {
 
 // Unsigned 64-bit min and max.  HIP's own min/max, given two different
 // 64-bit integer types (unsigned long and unsigned long long), resolve to
-// their double overload: a dozen VALU instructions through f64, exact only
+// their double overload: about twenty VALU instructions through f64, exact only
 // below 2^53.
 __host__ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __host__ __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
