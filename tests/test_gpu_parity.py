@@ -143,6 +143,21 @@ def test_long_records_span_many_words():
     check_path(A, B, items=64, keep_lcp=False, label="emit without lcp array")
 
 
+def test_staged_chunks_over_several_slices():
+    """Records of about 500 bytes (keys of 50-150 bytes, values of 0-800):
+    the emitter sizes its chunks to fill about 90% of its output window
+    (about 18 records here), so with this spread about one chunk in eight
+    overflows the window and is emitted in two slices while its source bytes
+    still fit the stage: the staged path across slices, after the first
+    slice's window was cleared at the chunk's start."""
+    rng = random.Random(11)
+    keys = sorted({_rand_bytes(rng, 50, 150) for _ in range(4000)})
+    recs = [(k, _rand_bytes(rng, 0, 800)) for k in keys]
+    A = _records_side(recs[::2])
+    B = _records_side([(k, None if i % 5 == 0 else v) for i, (k, v) in enumerate(recs[1::2])])
+    check_path(A, B, items=2048, path="fused", label="staged chunks over several slices")
+
+
 def test_equal_pairs_split_by_partition_boundaries():
     rng = random.Random(5)
     keys = sorted({_rand_bytes(rng, 2, 6) for _ in range(3000)})
