@@ -158,6 +158,21 @@ def test_staged_chunks_over_several_slices():
     check_path(A, B, items=2048, path="fused", label="staged chunks over several slices")
 
 
+def test_records_longer_than_the_window():
+    """One record in ten carries a value of 20-60 KB (up to half a megabit,
+    several of the emitter's 80-kilobit windows) between short records: such
+    a record is emitted over several slices, and its workgroup's sources do
+    not fit the stage and are read in place."""
+    rng = random.Random(21)
+    keys = sorted({_rand_bytes(rng, 1, 40) for _ in range(300)})
+    recs = [(k, _rand_bytes(rng, 20000, 60000) if i % 10 == 0 else _rand_bytes(rng, 0, 50))
+            for i, k in enumerate(keys)]
+    A = _records_side(recs[::2])
+    B = _records_side([(k, None if i % 7 == 0 else v) for i, (k, v) in enumerate(recs[1::2])])
+    for path in ("fused", "merge"):
+        check_path(A, B, items=64, path=path, label=f"{path}, records longer than the window")
+
+
 def test_equal_pairs_split_by_partition_boundaries():
     rng = random.Random(5)
     keys = sorted({_rand_bytes(rng, 2, 6) for _ in range(3000)})
