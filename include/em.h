@@ -419,6 +419,33 @@ int em_fcin_prefix8(const uint32_t *payload, uint64_t payload_words, uint32_t S,
                     size_t ws_bytes, void *stream);
 
 /*
+ * Owner-search comparison of keys of two front-coded inputs, with no key
+ * arena (Everett, "GPU construction experiment", the literal-owner paragraph:
+ * bit p of key i is the literal bit of j = max{t <= i : r_t <= p}; a merge of
+ * compressed inputs needs such comparisons past its prefix cache, and the
+ * page leaves their cost against materialization to measurement).  After
+ * em_fcin_parse on each payload (no error bits; input A: payload_a of S_a
+ * records with workspace ws_a, input B likewise), for q in [0, n) compares
+ * key ia[q] of A with key jb[q] of B from byte from_byte on -- the bytes
+ * before it are taken as shared, as when a merge's cached bytes tie -- and
+ * writes lcp_bits[q] = the exact bit LCP of the two keys (clamped to the
+ * shorter one, counting the skipped bytes) and cmp[q] = -1, 0 or 1, the
+ * sign of A's key against B's in unsigned bytewise order with a proper
+ * prefix first.  Every key bit is read from its owner's literal in the
+ * payload, down the pse chain the parse built.  ia, jb: u32[n]; lcp_bits:
+ * u32[n], cmp: i32[n] (either may be NULL, not both), device memory.  An
+ * index past its input gives lcp_bits = 0xFFFFFFFF and cmp = 0.  The
+ * workspaces are only read.  Errors: EM_EINVAL (NULL or misaligned
+ * workspace, NULL payload with records, NULL index arrays or both outputs
+ * NULL with n > 0), EM_ERANGE (S_a or S_b >= EM_MAX_RECORDS), EM_ENOSPC (a
+ * workspace below em_fcin_workspace_bytes of its S).
+ */
+int em_fcin_compare(const uint32_t *payload_a, uint64_t words_a, uint32_t S_a, const void *ws_a,
+                    size_t ws_a_bytes, const uint32_t *payload_b, uint64_t words_b, uint32_t S_b,
+                    const void *ws_b, size_t ws_b_bytes, uint32_t n, const uint32_t *ia, const uint32_t *jb,
+                    uint32_t from_byte, uint32_t *lcp_bits, int32_t *cmp, void *stream);
+
+/*
  * Byte-profile front coding (Everett, "Byte-profile GPU merge", "Pipeline":
  * byte LEB128 counts, byte FC literals, optional-value tags, a common encoded
  * value width -- width seventeen is a presence tag and sixteen payload

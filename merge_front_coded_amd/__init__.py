@@ -11,7 +11,8 @@ from .binding import (COLLISION_MODES, EM_COLLISION_512, EM_COLLISION_512_COMPAC
                       em_payload_bound_bits, em_rank512_probe, em_rank512_workspace_bytes, em_rank2048_probe,
                       em_rank2048_workspace_bytes, em_scan, em_scan_noalloc, em_workspace_bytes, lib, load_library,
                       EF_INFO_FIELDS, EfSections, em_ef_capacity, em_ef_encode, em_ef_entry_count,
-                      em_ef_navigation, em_ef_workspace_bytes, em_fcin_materialize, em_fcin_parse, em_fcin_prefix8,
+                      em_ef_navigation, em_ef_workspace_bytes, em_fcin_compare, em_fcin_materialize, em_fcin_parse,
+                      em_fcin_prefix8,
                       em_fcin_workspace_bytes, fcin_decode, em_bp_emit, em_bp_lengths, em_bp_navigation,
                       em_bp_workspace_bytes)
 from .pipeline import Pipeline
@@ -20,7 +21,8 @@ __all__ = ["COLLISION_MODES", "EM_COLLISION_512", "EM_COLLISION_512_COMPACT", "E
            "EM_COLLISION_2048", "EM_NONE", "DeviceSide", "EmError", "Pipeline", "em_collision_rank",
            "em_collision_rank_mode", "em_collision_workspace_bytes", "em_rank2048_probe",
            "em_rank2048_workspace_bytes", "EF_INFO_FIELDS", "EfSections", "em_ef_capacity", "em_ef_encode",
-           "em_ef_entry_count", "em_ef_navigation", "em_ef_workspace_bytes", "em_fcin_materialize", "em_fcin_prefix8",
+           "em_ef_entry_count", "em_ef_navigation", "em_ef_workspace_bytes", "em_fcin_compare", "em_fcin_materialize",
+           "em_fcin_prefix8",
            "em_fcin_parse", "em_fcin_workspace_bytes", "fcin_decode", "em_bp_emit", "em_bp_lengths",
            "em_bp_navigation", "em_bp_workspace_bytes", "em_emit",
            "em_emit_merged", "em_fc_lengths", "em_merge_fc", "em_merge_fc_onepass", "em_merge_fc_workspace_bytes",

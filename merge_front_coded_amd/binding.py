@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH):
         "em_fcin_parse": (i32, [P, u64, u64, u32, P, P, P, P, P, P, P, P, sz, P]),
         "em_fcin_materialize": (i32, [P, u64, u32, P, u64, P, P, u64, P, P, P, P, sz, P]),
         "em_fcin_prefix8": (i32, [P, u64, u32, P, P, sz, P]),
+        "em_fcin_compare": (i32, [P, u64, u32, P, sz, P, u64, u32, P, sz, u32, P, P, u32, P, P, P]),
         "em_bp_workspace_bytes": (sz, [u32]),
         "em_bp_lengths": (i32, [S, S, P, P, u32, P, P, P, sz, P]),
         "em_bp_emit": (i32, [S, S, P, P, u32, P, u64, P, P, u64, P, P]),
@@ -373,6 +374,13 @@ def em_fcin_materialize(payload, S, keys, key_off, vals, val_off, tomb, d_totals
 def em_fcin_prefix8(payload, S, pfx, ws, stream=None):
     _check(lib().em_fcin_prefix8(_p(payload), payload.numel(), S, _p(pfx), _p(ws), ws.numel(), _stream(stream)),
            "em_fcin_prefix8")
+
+
+def em_fcin_compare(payload_a, S_a, ws_a, payload_b, S_b, ws_b, n, ia, jb, from_byte, lcp_bits=None, cmp=None,
+                    stream=None):
+    _check(lib().em_fcin_compare(_p(payload_a), payload_a.numel(), S_a, _p(ws_a), ws_a.numel(), _p(payload_b),
+                                 payload_b.numel(), S_b, _p(ws_b), ws_b.numel(), n, _p(ia), _p(jb), from_byte,
+                                 _p(lcp_bits), _p(cmp), _stream(stream)), "em_fcin_compare")
 
 
 def fcin_decode(payload, T: int, S: int, off=None, nav: "EfSections | None" = None, device="cuda") -> DeviceSide:

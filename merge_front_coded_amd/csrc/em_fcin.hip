@@ -965,6 +965,103 @@ __global__ void k_fi_clear(uint64_t* totals) {
   totals[0] = totals[1] = totals[2] = 0;
 }
 
+// ---- owner-search comparison of two compressed inputs' keys ----
+//
+// Everett, "GPU construction experiment", the literal-owner paragraph: a merge
+// of compressed inputs may compare keys without expanding them, taking each
+// key bit from its owner's literal; the page leaves the cost of that against
+// materializing the keys to measurement.  Bit p of key i belongs to
+// j = max{t <= i : r_t <= p}: the record's own literal holds bits [r_i, k_i),
+// pse(i) (the last earlier record with a smaller r) holds [r_pse(i), r_i),
+// and so on down the pse chain to a record with r = 0 (record 0 has r = 0,
+// so the chain always ends).
+
+// Key bits [x0, x0 + 256) of record i as eight most-significant-first words,
+// zero at and past key bit kend, every bit taken from its owner's literal.
+// False when the chain breaks, which a parse without error bits excludes.
+template <class Bits>
+__device__ __forceinline__ bool fi_window(const Bits& bits, const FiLayout& L, uint32_t i, uint32_t kend,
+                                          uint32_t x0, uint32_t (&w)[8]) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t) w[t] = 0;
+  const uint32_t x1 = min(kend, x0 + 256u);
+  uint32_t j = i, lo = L.r[i], hi = kend;  // record j's literal holds key bits [lo, hi)
+  uint64_t base = L.lit[i] - lo;           // key bit q of that fragment: payload bit base + q
+  while (true) {
+    const uint32_t a = max(lo, x0), b = min(hi, x1);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t w0 = x0 + 32u * t;  // word t: key bits [w0, w0 + 32)
+      const uint32_t qa = max(a, w0), qb = min(b, w0 + 32u);
+      if (qa < qb) {
+        const uint32_t n = qb - qa;  // 1 .. 32 bits, placed qa - w0 bits into the word
+        const uint32_t v = bits.at32(base + qa);
+        w[t] |= (n == 32u ? v : (v >> (32u - n)) << (32u - n)) >> (qa - w0);
+      }
+    }
+    if (lo <= x0) return true;
+    const uint32_t nj = L.pse[j];
+    if (nj >= j) return false;  // (no earlier owner)
+    const uint32_t nlo = L.r[nj];
+    if (nlo >= lo) return false;
+    hi = lo;
+    j = nj;
+    lo = nlo;
+    base = L.lit[nj] - nlo;
+  }
+}
+
+// Pair q: key ia[q] of input A against key jb[q] of input B, from byte
+// `from` on (the bytes before it are taken as shared), in windows of 256
+// bits; lcp[q] = their bit LCP, cmp[q] = the sign of A's key minus B's in
+// unsigned bytewise order with a proper prefix first.  An index past its
+// input, or a broken owner chain, gives lcp = kFiInf and cmp = 0.
+constexpr int kFcBlock = 256;
+
+__global__ __launch_bounds__(kFcBlock) void k_fi_compare(FiBits ba, FiLayout La, FiBits bb, FiLayout Lb, uint32_t n,
+                                                         const uint32_t* __restrict__ ia,
+                                                         const uint32_t* __restrict__ jb, uint32_t from,
+                                                         uint32_t* __restrict__ lcp, int32_t* __restrict__ cmp) {
+  const uint32_t q = blockIdx.x * kFcBlock + threadIdx.x;
+  if (q >= n) return;
+  const uint32_t i = ia[q], j = jb[q];
+  uint32_t l = kFiInf;
+  int32_t c = 0;
+  if (i < La.S && j < Lb.S) {
+    const uint32_t ka = 8u * La.kbytes[i], kb = 8u * Lb.kbytes[j], m = min(ka, kb);
+    const uint32_t start = from < m / 8u ? 8u * from : m;
+    bool done = false, broken = false;  // done: the first differing bit is known
+    for (uint32_t x0 = start; x0 < m && !done; x0 += 256u) {
+      uint32_t wa[8], wb[8];
+      if (!fi_window(ba, La, i, ka, x0, wa) || !fi_window(bb, Lb, j, kb, x0, wb)) {
+        broken = true;
+        break;
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t d = wa[t] ^ wb[t];
+        if (!done && d) {
+          done = true;
+          const uint32_t p = x0 + 32u * t + static_cast<uint32_t>(__builtin_clz(d));
+          if (p < m) {  // (a difference at or past the shorter key's end is none)
+            l = p;
+            c = wa[t] > wb[t] ? 1 : -1;
+          }
+        }
+      }
+    }
+    if (broken) {
+      l = kFiInf;
+      c = 0;
+    } else if (l == kFiInf) {  // equal up to the shorter key's end
+      l = m;
+      c = ka < kb ? -1 : (ka > kb ? 1 : 0);
+    }
+  }
+  if (lcp) lcp[q] = l;
+  if (cmp) cmp[q] = c;
+}
+
 }  // namespace em
 
 using namespace em;
@@ -1042,6 +1139,25 @@ extern "C" int em_fcin_materialize(const uint32_t* payload, uint64_t payload_wor
   rpb -= rpb % kFiRecs;  // whole blocks
   hipLaunchKernelGGL(k_fi_records, dim3(S ? (S + rpb - 1) / rpb : 1), dim3(kFiBlock), 0, st, bits, L, rpb, keys,
                      key_cap, key_off, vals, val_cap, val_off, tomb, d_totals + 2);
+  return check_launch();
+}
+
+extern "C" int em_fcin_compare(const uint32_t* payload_a, uint64_t words_a, uint32_t S_a, const void* ws_a,
+                               size_t ws_a_bytes, const uint32_t* payload_b, uint64_t words_b, uint32_t S_b,
+                               const void* ws_b, size_t ws_b_bytes, uint32_t n, const uint32_t* ia,
+                               const uint32_t* jb, uint32_t from_byte, uint32_t* lcp_bits, int32_t* cmp,
+                               void* stream) {
+  if (!ws_a || !ws_b || (reinterpret_cast<uintptr_t>(ws_a) & 255) || (reinterpret_cast<uintptr_t>(ws_b) & 255))
+    return EM_EINVAL;
+  if (S_a >= EM_MAX_RECORDS || S_b >= EM_MAX_RECORDS) return EM_ERANGE;
+  if ((S_a && !payload_a) || (S_b && !payload_b)) return EM_EINVAL;
+  if (n && (!ia || !jb || (!lcp_bits && !cmp))) return EM_EINVAL;
+  if (ws_a_bytes < em_fcin_workspace_bytes(S_a) || ws_b_bytes < em_fcin_workspace_bytes(S_b)) return EM_ENOSPC;
+  if (n == 0) return EM_OK;
+  const FiLayout La = fi_layout(const_cast<void*>(ws_a), S_a), Lb = fi_layout(const_cast<void*>(ws_b), S_b);
+  const FiBits ba{payload_a, words_a}, bb{payload_b, words_b};
+  hipLaunchKernelGGL(k_fi_compare, dim3((n + kFcBlock - 1) / kFcBlock), dim3(kFcBlock), 0, as_stream(stream), ba,
+                     La, bb, Lb, n, ia, jb, from_byte, lcp_bits, cmp);
   return check_launch();
 }
 

@@ -62,6 +62,8 @@ def _load():
         u32 = ctypes.c_uint32
         lib.or_key_cmp.restype = ctypes.c_int
         lib.or_key_cmp.argtypes = [S, u32, S, u32]
+        lib.or_key_lcp_bits.restype = ctypes.c_uint64
+        lib.or_key_lcp_bits.argtypes = [S, u32, S, u32]
         lib.or_merge.argtypes = [S, S, P]
         lib.or_corank.restype = u32
         lib.or_corank.argtypes = [P, u32, u32]
@@ -103,6 +105,11 @@ def _side(h):
 def key_cmp(X, i: int, Y, j: int) -> int:
     """Unsigned bytewise order, proper prefix first (<0, 0, >0)."""
     return _load().or_key_cmp(ctypes.byref(_side(X)), i, ctypes.byref(_side(Y)), j)
+
+
+def key_lcp_bits(X, i: int, Y, j: int) -> int:
+    """Leading equal bits of key i of X and key j of Y, clamped to the shorter key."""
+    return int(_load().or_key_lcp_bits(ctypes.byref(_side(X)), i, ctypes.byref(_side(Y)), j))
 
 
 def merge(A, B) -> np.ndarray:

@@ -182,6 +182,11 @@ static uint64_t bit_lcp(const uint8_t *p, uint64_t kp, const uint8_t *x, uint64_
   return b;
 }
 
+/* Exact bit LCP of key i of X and key j of Y (both lengths in bits). */
+uint64_t or_key_lcp_bits(const or_side *X, uint32_t i, const or_side *Y, uint32_t j) {
+  return bit_lcp(key_ptr(X, i), 8ull * key_len(X, i), key_ptr(Y, j), 8ull * key_len(Y, j));
+}
+
 /*
  * [GC] control equation and record grammar.  For survivor i with key bits k_i,
  * exact bit LCP l_i with the preceding survivor (l_0 = 0):

@@ -176,6 +176,24 @@ def test_fcin_prefix8_argument_errors(lib):
     assert lib.em_fcin_prefix8(None, 0, 0, None, buf, lib.em_fcin_workspace_bytes(0), None) == 0  # nothing to do
 
 
+def test_fcin_compare_argument_errors(lib):
+    buf = ctypes.c_void_p(0x100000)
+    mis = ctypes.c_void_p(0x100008)
+    need = lib.em_fcin_workspace_bytes(5)
+
+    def call(pa=buf, Sa=5, wa=buf, na=need, pb=buf, Sb=5, wb=buf, nb=need, n=3, ia=buf, jb=buf, lcp=buf, cmp=buf):
+        return lib.em_fcin_compare(pa, 4, Sa, wa, na, pb, 4, Sb, wb, nb, n, ia, jb, 0, lcp, cmp, None)
+
+    assert call(wa=None) == -1 and call(wb=mis) == -1  # no or misaligned workspace
+    assert call(pa=None) == -1 and call(pb=None) == -1  # no payload with records
+    assert call(ia=None) == -1 and call(jb=None) == -1  # no indices
+    assert call(lcp=None, cmp=None) == -1  # no output
+    assert call(Sa=1 << 24, na=1 << 40) == -2 and call(Sb=1 << 24, nb=1 << 40) == -2  # record cap
+    assert call(na=need - 1) == -3 and call(nb=need - 1) == -3  # workspace too small
+    assert call(n=0, ia=None, jb=None, lcp=None, cmp=None) == 0  # nothing to do
+    assert call(pa=None, Sa=0, na=lib.em_fcin_workspace_bytes(0), n=0) == 0
+
+
 def test_missing_library_fails_loudly(tmp_path):
     """Without the HIP library the binding raises; there is no CPU fallback."""
     from merge_front_coded_amd import binding

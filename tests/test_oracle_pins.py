@@ -299,6 +299,32 @@ def test_key_order_proper_prefix_and_unsigned_bytes():
     assert oracle.key_cmp(A, 0, A, 0) == 0
 
 
+def test_key_lcp_bits_closed_forms_and_brute_force():
+    """Bit LCP of two keys: hand values, then every pair of a small random
+    set against a bit-string comparison written out here."""
+    A = gen.side_from_records([(b"ab", b""), (b"\x80", b""), (b"abc", b"")])
+    B = gen.side_from_records([(b"a", b""), (b"ab", b""), (b"\x00", b""), (b"abd", b""), (b"", b"")])
+    assert oracle.key_lcp_bits(A, 0, B, 1) == 16   # identical keys: all their bits
+    assert oracle.key_lcp_bits(A, 0, B, 0) == 8    # a proper prefix: the shorter key's bits
+    assert oracle.key_lcp_bits(A, 1, B, 2) == 0    # the first bit differs
+    assert oracle.key_lcp_bits(A, 2, B, 3) == 21   # 'c' = 0x63, 'd' = 0x64: six equal high bits
+    assert oracle.key_lcp_bits(A, 0, B, 4) == 0    # an empty key
+    rng = np.random.default_rng(5)
+    keys = sorted({bytes(rng.integers(0, 3, int(rng.integers(0, 5)), dtype=np.uint8)) for _ in range(60)})
+    X = gen.side_from_records([(k, b"") for k in keys])
+
+    def bits(k):
+        return "".join(format(c, "08b") for c in k)
+
+    for i, ki in enumerate(keys):
+        for j, kj in enumerate(keys):
+            bi, bj = bits(ki), bits(kj)
+            n = 0
+            while n < min(len(bi), len(bj)) and bi[n] == bj[n]:
+                n += 1
+            assert oracle.key_lcp_bits(X, i, X, j) == n, (ki, kj)
+
+
 # ---- output navigation: Elias-Fano sections of the sampled offsets ----
 
 def test_ef_hand_examples():
