@@ -204,6 +204,95 @@ def algorithmic_bytes(Ah, Bh, pl, path):
     return out
 
 
+def _key_hash(X, weights):
+    """A 64-bit hash of every key of a device side (a weighted sum of its
+    bytes, one random weight per byte position, wrapping, mixed with the
+    length): equal keys hash alike."""
+    import torch
+    off = X.key_off[:X.n + 1].long()
+    lens = off[1:] - off[:-1]
+    nbytes = int(off[-1].item())
+    pos = torch.arange(nbytes, device=off.device) - torch.repeat_interleave(off[:-1], lens)
+    c = torch.zeros(nbytes + 1, dtype=torch.int64, device=off.device)
+    c[1:] = torch.cumsum(X.keys[:nbytes].long() * weights[pos], 0)
+    return (c[off[1:]] - c[off[:-1]]) * 1000003 + lens
+
+
+def owner_search_leg(A, B, items, steps, stream, replaced):
+    """A merge of the two inputs given front-coded instead of as arenas:
+    each input front-coded alone by this path and parsed; the pairs of equal
+    keys, whose comparisons every merge of the two must finish past its eight
+    cached bytes, compared from byte 8 by owner search (em_fcin_compare),
+    beside materializing both inputs into arenas.  Timings only; the
+    comparisons' parity is covered by the tests."""
+    import torch
+    import gen
+    import merge_front_coded_amd as em
+    empty = em.DeviceSide.from_host(gen.side_from_records([]))
+    ins = []
+    for X in (A, B):
+        px = em.Pipeline(X, empty, items_per_part=items, path="fused", keep_all=True)
+        px.run()
+        torch.cuda.synchronize()
+        wsx = torch.empty(max(em.em_fcin_workspace_bytes(px.S), 256), dtype=torch.uint8, device="cuda")
+        tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+        em.em_fcin_parse(px.payload, px.T, px.S, tot, wsx, off=px.off)
+        kb, vb, err = (int(x) for x in tot.cpu())
+        assert err == 0 and px.S == X.n
+        ins.append((px, wsx, tot, kb, vb))
+    # the pairs of equal keys: every merge finishes these comparisons past its cache
+    maxlen = int(max((A.key_off[1:A.n + 1] - A.key_off[:A.n]).max().item() if A.n else 0,
+                     (B.key_off[1:B.n + 1] - B.key_off[:B.n]).max().item() if B.n else 0))
+    g = torch.Generator(device="cuda").manual_seed(12345)
+    weights = torch.randint(-(1 << 62), 1 << 62, (maxlen + 1,), generator=g, dtype=torch.int64, device="cuda")
+    ha, order = torch.sort(_key_hash(A, weights))
+    hb = _key_hash(B, weights)
+    pos = torch.searchsorted(ha, hb).clamp(max=max(A.n - 1, 0))
+    hit = ha[pos] == hb
+    ia = order[pos[hit]].to(torch.int32).contiguous()
+    jb = torch.nonzero(hit).flatten().to(torch.int32).contiguous()
+    del ha, hb, order, pos, hit
+    n = int(ia.numel())
+    lcp = torch.empty(max(n, 1), dtype=torch.int32, device="cuda")
+    cmp = torch.empty(max(n, 1), dtype=torch.int32, device="cuda")
+    (xa, wa, ta, kba, vba), (xb, wb, tb, kbb, vbb) = ins
+    ev_c, ev_m, ev_p = [], [], []
+    keys_a = torch.zeros(kba + 64, dtype=torch.uint8, device="cuda")
+    keys_b = torch.zeros(kbb + 64, dtype=torch.uint8, device="cuda")
+    vals_a = torch.zeros(vba + 64, dtype=torch.uint8, device="cuda")
+    vals_b = torch.zeros(vbb + 64, dtype=torch.uint8, device="cuda")
+    offs = [torch.empty(x.S + 1, dtype=torch.int32, device="cuda") for x in (xa, xa, xb, xb)]
+    tombs = [torch.empty(max(x.S, 1), dtype=torch.uint8, device="cuda") for x in (xa, xb)]
+    pfx = [torch.empty(max(x.S, 1), dtype=torch.int64, device="cuda") for x in (xa, xb)]
+    for it in range(steps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        em.em_fcin_compare(xa.payload, xa.S, wa, xb.payload, xb.S, wb, n, ia, jb, 8, lcp_bits=lcp, cmp=cmp,
+                           stream=stream)
+        e[1].record(stream)
+        em.em_fcin_materialize(xa.payload, xa.S, keys_a, offs[0], vals_a, offs[1], tombs[0], ta, wa, stream=stream)
+        em.em_fcin_materialize(xb.payload, xb.S, keys_b, offs[2], vals_b, offs[3], tombs[1], tb, wb, stream=stream)
+        e[2].record(stream)
+        em.em_fcin_prefix8(xa.payload, xa.S, pfx[0], wa, stream=stream)
+        em.em_fcin_prefix8(xb.payload, xb.S, pfx[1], wb, stream=stream)
+        e[3].record(stream)
+        if it:
+            ev_c.append((e[0], e[1]))
+            ev_m.append((e[1], e[2]))
+            ev_p.append((e[2], e[3]))
+    torch.cuda.synchronize()
+    assert int(ta[2].item()) == 0 and int(tb[2].item()) == 0
+    equal = int((cmp[:n] == 0).sum().item()) if n else 0
+
+    def avg(ev):
+        return sum(x.elapsed_time(y) for x, y in ev) / len(ev)
+
+    return {"calls": ["em_fcin_compare", "em_fcin_materialize", "em_fcin_prefix8"],
+            "pairs": n, "pairs_equal": equal, "replaced_records": replaced,
+            "compare_from_byte_8_ms": avg(ev_c), "materialize_both_inputs_ms": avg(ev_m),
+            "prefix_cache_from_owners_both_inputs_ms": avg(ev_p)}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -490,6 +579,9 @@ def main():
                                        "GBps": fcin_bytes / ((parse_ms + mat_ms) * 1e-3) / 1e9}
         if pn is not pl:
             del pn
+        del ws, keys, vals, key_off, val_off, tomb, pfx
+        result["front_coded_input"]["owner_search"] = owner_search_leg(A, B, pl.items, args.steps, stream,
+                                                                       A.n + B.n - pl.S)
     result["step_ms"] = {"median": float(np.median(steps_ms)), "min": min(steps_ms), "max": max(steps_ms)}
     result["ms_per_step_with_host_reads"] = complete_ms if fused else ms_per_step
     result["B_min_bytes"] = b_io - replaced_val_bytes
