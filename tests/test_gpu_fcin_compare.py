@@ -151,3 +151,51 @@ def test_compare_edges():
     cx, cy = _compressed(A), _compressed(B)
     got_l, got_c = _run(cx, cy, np.array([A.n, 0, 0], np.uint32), np.array([0, B.n, B.n + 5], np.uint32))
     assert np.array_equal(got_l, np.full(3, 0xFFFFFFFF, np.uint32)) and np.array_equal(got_c, np.zeros(3, np.int32))
+
+
+def _compressed_on_gpu(X):
+    """X front-coded alone by the GPU path at full size (its payload's parity
+    is covered by the full-size digests), parsed on the GPU."""
+    import merge_front_coded_amd as em
+    empty = em.DeviceSide.from_host(gen.side_from_records([]))
+    pl = em.Pipeline(em.DeviceSide.from_host(X), empty, path="fused", keep_all=True)
+    pl.run()
+    torch.cuda.synchronize()
+    assert pl.S == X.n
+    ws = torch.empty(max(em.em_fcin_workspace_bytes(pl.S), 256), dtype=torch.uint8, device="cuda")
+    tot = torch.zeros(3, dtype=torch.int64, device="cuda")
+    em.em_fcin_parse(pl.payload, pl.T, pl.S, tot, ws, off=pl.off)
+    assert int(tot[2].item()) == 0
+    return pl.payload, pl.S, ws
+
+
+def test_compare_full_size_sampled():
+    """8M+8M inputs (the benchmark's workload), each front-coded alone:
+    20,000 B keys against the A key at or after them (equal keys where B
+    replaces A) and 20,000 random pairs, from byte 0 and, for the pairs that
+    share their first eight bytes, from byte 8."""
+    A, B = workload(3)
+    print(f"full size: |A|={A.n} |B|={B.n}", flush=True)
+    cx, cy = _compressed_on_gpu(A), _compressed_on_gpu(B)
+    rng = np.random.default_rng(33)
+    jb = np.sort(rng.choice(B.n, 20000, replace=False)).astype(np.uint32)
+    ia = np.empty_like(jb)
+    for t, j in enumerate(jb):  # the first A key not below B's (binary search)
+        k, lo, hi = B.key(int(j)), 0, A.n
+        while lo < hi:
+            mid = (lo + hi) // 2
+            if A.key(mid) < k:
+                lo = mid + 1
+            else:
+                hi = mid
+        ia[t] = min(lo, A.n - 1)
+    ia = np.concatenate([ia, rng.integers(0, A.n, 20000).astype(np.uint32)])
+    jb = np.concatenate([jb, rng.integers(0, B.n, 20000).astype(np.uint32)])
+    want_l = np.array([oracle.key_lcp_bits(A, int(i), B, int(j)) for i, j in zip(ia, jb)], np.uint32)
+    want_c = np.array([np.sign(oracle.key_cmp(A, int(i), B, int(j))) for i, j in zip(ia, jb)], np.int32)
+    assert (want_c == 0).sum() > 5000  # equal keys are among the pairs
+    got_l, got_c = _run(cx, cy, ia, jb)
+    assert np.array_equal(got_l, want_l) and np.array_equal(got_c, want_c), "from byte 0"
+    keep = want_l >= 64
+    got_l, got_c = _run(cx, cy, ia[keep], jb[keep], from_byte=8)
+    assert np.array_equal(got_l, want_l[keep]) and np.array_equal(got_c, want_c[keep]), "from byte 8"
