@@ -145,6 +145,9 @@ def parse():
                          "survivors")
     ap.add_argument("--fcin", action="store_true",
                     help="also time decoding the step's payload back into arenas (em_fcin_parse + _materialize)")
+    ap.add_argument("--owner-search", action="store_true",
+                    help="also time comparing the equal keys of the two inputs, each front-coded alone, through "
+                         "their literal owners (em_fcin_compare) against materializing both inputs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run the plain 1 GiB device copy (the default; kept for the counter-scaling commands)")
     ap.add_argument("--no-copy", action="store_true",
@@ -579,9 +582,8 @@ def main():
                                        "GBps": fcin_bytes / ((parse_ms + mat_ms) * 1e-3) / 1e9}
         if pn is not pl:
             del pn
-        del ws, keys, vals, key_off, val_off, tomb, pfx
-        result["front_coded_input"]["owner_search"] = owner_search_leg(A, B, pl.items, args.steps, stream,
-                                                                       A.n + B.n - pl.S)
+    if args.owner_search:
+        result["owner_search"] = owner_search_leg(A, B, pl.items, args.steps, stream, A.n + B.n - pl.S)
     result["step_ms"] = {"median": float(np.median(steps_ms)), "min": min(steps_ms), "max": max(steps_ms)}
     result["ms_per_step_with_host_reads"] = complete_ms if fused else ms_per_step
     result["B_min_bytes"] = b_io - replaced_val_bytes
