@@ -471,8 +471,8 @@ __device__ __forceinline__ uint32_t bits32_at(const uint32_t* base, Pos bp) {
 // so every one of them is one funnel shift of two consecutive source dwords
 // with a shift that is the same for the whole span.  Words 1 .. W-1 are
 // stored; the bits of the partial word W (when f2 = (f + n) mod 32 > 0) are
-// returned.  Reads reach at most one dword past the one holding the span's
-// last bit.
+// returned.  Reads of global memory reach at most one dword past the one
+// holding the span's last bit; reads of LDS at most five.
 template <typename Pos>
 __device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base, Pos bp, uint32_t f,
                                                uint32_t W, uint32_t f2) {
@@ -486,21 +486,36 @@ __device__ __forceinline__ uint32_t span_words(uint32_t* o, const uint32_t* base
   // (the loop's end is computed up front, so that its counter is not needed
   // after it)
   const uint32_t t = cnt & ~3u, rem = cnt & 3u;
-  for (uint32_t i = 0; i < t; i += 4) {  // four source dwords in flight per iteration
-    const uint32_t n1 = __builtin_bswap32(p[i + 1]), n2 = __builtin_bswap32(p[i + 2]);
-    const uint32_t n3 = __builtin_bswap32(p[i + 3]), n4 = __builtin_bswap32(p[i + 4]);
-    o[i] = __builtin_amdgcn_alignbit(cur, n1, sh);
-    o[i + 1] = __builtin_amdgcn_alignbit(n1, n2, sh);
-    o[i + 2] = __builtin_amdgcn_alignbit(n2, n3, sh);
-    o[i + 3] = __builtin_amdgcn_alignbit(n3, n4, sh);
-    cur = n4;
+  // the last source dword needed; indices past it re-read it
+  const uint32_t last = t + rem + (f2 ? 1u : 0u);
+  // source dwords 1 .. 4 past the current one (raw), loaded one round ahead
+  // of their use, so that each round's loads overlap the previous round's
+  // shifts and stores.  A source in LDS (32-bit positions: a staged span) is
+  // read up to four dwords past `last`, which stays inside the workgroup's
+  // LDS (the stage is followed by other arrays) and is never used; a source
+  // in global memory re-reads `last` instead.
+  auto ld = [&](uint32_t k) -> uint32_t {
+    if constexpr (sizeof(Pos) == 4)
+      return p[k];
+    else
+      return p[min(k, last)];
+  };
+  uint32_t n1 = p[min(1u, last)], n2 = p[min(2u, last)], n3 = p[min(3u, last)], n4 = p[min(4u, last)];
+  for (uint32_t i = 0; i < t; i += 4) {
+    const uint32_t m1 = ld(i + 5), m2 = ld(i + 6), m3 = ld(i + 7), m4 = ld(i + 8);
+    const uint32_t b1 = __builtin_bswap32(n1), b2 = __builtin_bswap32(n2);
+    const uint32_t b3 = __builtin_bswap32(n3), b4 = __builtin_bswap32(n4);
+    o[i] = __builtin_amdgcn_alignbit(cur, b1, sh);
+    o[i + 1] = __builtin_amdgcn_alignbit(b1, b2, sh);
+    o[i + 2] = __builtin_amdgcn_alignbit(b2, b3, sh);
+    o[i + 3] = __builtin_amdgcn_alignbit(b3, b4, sh);
+    cur = b4;
+    n1 = m1, n2 = m2, n3 = m3, n4 = m4;
   }
   // up to three more words, then the partial word (source dwords t+1 ..
-  // t+rem, and one more when f2 > 0; indices past the last one needed re-read
-  // it)
-  const uint32_t last = t + rem + (f2 ? 1u : 0u);
-  const uint32_t m1 = __builtin_bswap32(p[min(t + 1, last)]), m2 = __builtin_bswap32(p[min(t + 2, last)]);
-  const uint32_t m3 = __builtin_bswap32(p[min(t + 3, last)]), m4 = __builtin_bswap32(p[min(t + 4, last)]);
+  // t+rem, and one more when f2 > 0, already loaded)
+  const uint32_t m1 = __builtin_bswap32(n1), m2 = __builtin_bswap32(n2);
+  const uint32_t m3 = __builtin_bswap32(n3), m4 = __builtin_bswap32(n4);
   if (rem > 0) o[t] = __builtin_amdgcn_alignbit(cur, m1, sh);
   if (rem > 1) o[t + 1] = __builtin_amdgcn_alignbit(m1, m2, sh);
   if (rem > 2) o[t + 2] = __builtin_amdgcn_alignbit(m2, m3, sh);
