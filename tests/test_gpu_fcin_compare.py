@@ -5,7 +5,8 @@ the oracle's on the original keys.  Pairs: equal keys (the comparisons a
 merge must finish past its cache), merge neighbours, random pairs; a start
 byte past bytes the pair shares; sub-byte differences, long inherited
 chains, keys longer than one 256-bit window, empty keys, and indices past
-an input."""
+an input; a start byte past differing bytes (checked against the oracle
+on keys whose first bytes are zeroed)."""
 import numpy as np
 import pytest
 
@@ -124,6 +125,30 @@ def test_compare_from_byte():
     # lcp only
     got_l2, _ = _run(cx, cy, si, sj, from_byte=1 << 20, with_cmp=False)
     assert np.array_equal(got_l2, got_l)
+
+
+def _zero_head(X, f):
+    """X with the first f bytes of every key set to zero (lengths kept)."""
+    keys = X.keys.copy()
+    off = X.key_off.astype(np.int64)
+    for i in range(X.n):
+        keys[off[i]:min(off[i] + f, off[i + 1])] = 0
+    return gen.HostSide(keys=keys, key_off=X.key_off, vals=X.vals, val_off=X.val_off, tomb=X.tomb)
+
+
+def test_compare_from_byte_skips_differences():
+    """Bytes before the start byte count as shared even where they differ:
+    the result is the oracle's on keys whose first bytes are zeroed."""
+    A, B = workload(3, 0.0005)
+    rng = np.random.default_rng(17)
+    ia, jb = _pairs(A, B, rng, n_random=4000)
+    cx, cy = _compressed(A), _compressed(B)
+    for f in (2, 5):
+        Az, Bz = _zero_head(A, f), _zero_head(B, f)
+        got_l, got_c = _run(cx, cy, ia, jb, from_byte=f)
+        want_l = np.array([oracle.key_lcp_bits(Az, int(i), Bz, int(j)) for i, j in zip(ia, jb)], np.uint32)
+        want_c = np.array([np.sign(oracle.key_cmp(Az, int(i), Bz, int(j))) for i, j in zip(ia, jb)], np.int32)
+        assert np.array_equal(got_l, want_l) and np.array_equal(got_c, want_c), f"from byte {f}"
 
 
 def test_compare_edges():
