@@ -37,6 +37,11 @@
 namespace em {
 
 constexpr int kMlBlock = 512;
+// The workspace's first words: the partition ticket, the emitter's ticket
+// counters from kEmitCtrStride, and the merge statistics on a line of their
+// own from kMlStatWord; all zero at the start of each launch.
+constexpr uint32_t kMlStatWord = kEmitCtrStride + kEmitCtrWords;
+constexpr uint32_t kMlTicketWords = kMlStatWord + kEmitCtrStride;
 constexpr int kMlWaves = kMlBlock / kWave;
 constexpr uint32_t kMlMaxItems = 4 * kMlBlock;  // outputs per partition, at most
 
@@ -60,6 +65,7 @@ struct MlShared {
   uint32_t scan32[kMlWaves + 1];
   uint32_t notes[kMlBlock];  // the merge's list of pairs to check, kWave words per wave
   uint32_t tile, i0, i1, g0, cp;
+  uint32_t try_fast;  // this partition tries the merge on cached prefixes first
 };
 
 struct MlOut {
@@ -85,7 +91,13 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   __shared__ Sh sh;
   const uint32_t tid = threadIdx.x;
   const uint32_t N = A.n + B.n;
-  if (tid == 0) sh.tile = atomicAdd(ticket, 1u);
+  // the launch's record of merges on cached prefixes tried and failed (a line of its own)
+  uint64_t* const fast_stat = reinterpret_cast<uint64_t*>(ticket + kMlStatWord);
+  if (tid == 0) {
+    const uint32_t t = atomicAdd(ticket, 1u);
+    sh.tile = t;
+    sh.try_fast = fast_merge_worth_trying(fast_stat, t) ? 1u : 0u;
+  }
   __syncthreads();
   const uint32_t tile = __builtin_amdgcn_readfirstlane(sh.tile);  // (uniform: scalar registers)
   const uint32_t d0 = tile * items;
@@ -164,7 +176,9 @@ __global__ __launch_bounds__(kMlBlock) __attribute__((amdgpu_waves_per_eu(6))) v
   uint32_t refs[IPT];
   const uint32_t k = tid * IPT;
   const uint32_t kept = merge_slice<IPT>(ao, bo, apf, bpf, A.keys, 0u, B.keys, 0u, k, len, nA_t, nB_t,
-                                         has_next_b, i0, A.n, j0, refs, sh.notes, cp);
+                                         has_next_b, i0, A.n, j0, refs, sh.notes, cp,
+                                         __builtin_amdgcn_readfirstlane(sh.try_fast) != 0,
+                                         fast_merge_records(tile) ? fast_stat : nullptr);
   // prefixes of this thread's outputs, and (thread 0) of the keys before the
   // partition, read before the compaction arrays overwrite the cache
   uint64_t opfx[IPT];
@@ -375,7 +389,8 @@ __global__ __launch_bounds__(kTsBlock) void k_tile_scan(const uint64_t* __restri
 }
 
 struct MlLayout {
-  uint32_t* ticket;  // [0]: partition ticket of k_merge_len; from [kEmitCtrStride]: the emitter's counters
+  uint32_t* ticket;  // [0]: partition ticket of k_merge_len; from [kEmitCtrStride]: the emitter's
+                     // counters; [kMlStatWord]: the merge statistics (u64)
   uint64_t* desc_s;
   uint64_t* tile_bits;
   uint64_t* tbase;
@@ -388,7 +403,7 @@ MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
   const size_t P = items ? (static_cast<size_t>(N) + items - 1) / items : 0;
   WsCursor cur{static_cast<uint8_t*>(ws), 0};
   MlLayout L;
-  L.ticket = cur.take<uint32_t>(kEmitCtrStride + kEmitCtrWords);
+  L.ticket = cur.take<uint32_t>(kMlTicketWords);
   L.desc_s = cur.take<uint64_t>(P ? P : 1);
   L.tile_bits = cur.take<uint64_t>(P ? P : 1);
   L.tbase = cur.take<uint64_t>(P ? P : 1);
@@ -401,7 +416,7 @@ MlLayout ml_layout(void* ws, uint32_t N, uint32_t items) {
 size_t ml_ws_bytes(uint32_t N, uint32_t items) {
   const size_t P = items ? (static_cast<size_t>(N) + items - 1) / items : 0;
   const size_t p = P ? P : 1, n = N ? N : 1;
-  return align_up((kEmitCtrStride + kEmitCtrWords) * 4, 256) + 3 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) +
+  return align_up(kMlTicketWords * 4, 256) + 3 * align_up(p * 8, 256) + 2 * align_up(n * 4, 256) +
          align_up(n * 8, 256);
 }
 
@@ -461,7 +476,7 @@ extern "C" int em_merge_lengths(const em_side_t* A, const em_side_t* B, const ui
   }
   const uint32_t P = (N + items_per_part - 1) / items_per_part;
   const MlLayout L = ml_layout(ws, N, items_per_part);
-  clear_lookback(L.ticket, kEmitCtrStride + kEmitCtrWords, L.desc_s, nullptr, P, st);
+  clear_lookback(L.ticket, kMlTicketWords, L.desc_s, nullptr, P, st);
   MlOut o{d_S, final_refs ? final_refs : L.refs, lcp_bits ? lcp_bits : L.lcp, L.toff, L.tile_bits,
           ord_A, ord_B, len_bits};
   launch_ml_items(*A, *B, coarse_splits, coarse_items, items_per_part, P, o, L, st);

@@ -320,7 +320,9 @@ __device__ __forceinline__ uint32_t merge_slice_fast(const uint32_t* a_off, cons
 // The merge of a workgroup's partition: every thread calls it (threads past
 // the partition's end get kDrop refs and a zero count).  Exact whichever
 // branch runs.  `notes` is LDS scratch of kWave words per wave of the
-// workgroup.
+// workgroup.  try_fast (uniform): try the merge on the cached prefixes
+// first; otherwise go straight to the exact one.  stat (nullable): when the
+// first is tried, thread 0 adds 1 + (2^32 if it failed) to *stat.
 template <int IPT>
 __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uint32_t* b_off,
                                                 const uint64_t* a_pfx, const uint64_t* b_pfx,
@@ -329,15 +331,46 @@ __device__ __forceinline__ uint32_t merge_slice(const uint32_t* a_off, const uin
                                                 uint32_t len, uint32_t nA_t, uint32_t nB_t,
                                                 bool has_next_b, uint32_t i0, uint32_t nA_all,
                                                 uint32_t j0, uint32_t (&refs)[IPT], uint32_t* notes,
-                                                uint32_t cp = 0) {
-  bool bad;
-  uint32_t kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
-                                        nB_t, has_next_b, i0, nA_all, j0, refs, bad,
-                                        notes + (threadIdx.x / kWave) * kWave, cp);
-  if (__syncthreads_or(bad))
+                                                uint32_t cp = 0, bool try_fast = true,
+                                                uint64_t* stat = nullptr) {
+  bool redo = true;
+  uint32_t kept = 0;
+  if (try_fast) {
+    bool bad;
+    kept = merge_slice_fast<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t, nB_t,
+                                 has_next_b, i0, nA_all, j0, refs, bad, notes + (threadIdx.x / kWave) * kWave, cp);
+    redo = __syncthreads_or(bad) != 0;
+    if (stat && threadIdx.x == 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(stat), 1ull + (redo ? (1ull << 32) : 0ull));
+  }
+  if (redo)
     kept = merge_slice_exact<IPT>(a_off, b_off, a_pfx, b_pfx, abase, a_adj, bbase, b_adj, k, len, nA_t,
                                   nB_t, has_next_b, i0, nA_all, j0, refs, cp);
   return kept;
+}
+
+// Whether a partition tries the merge on cached prefixes before the exact
+// one, and whether it records the outcome.  On inputs whose cached bytes tie
+// between keys of different lengths in nearly every partition (long shared
+// prefixes: paths, URLs), that merge almost always fails and its time is
+// lost.  stat holds the partitions that tried it (low 32 bits) and those that
+// failed (high 32 bits) so far in the launch.  The first kFastSample
+// partitions (by ticket) and every kFastResample-th after them try it and
+// record the outcome; the others read stat and skip it when at least 7/8 of
+// the tries failed.  (Few recorded outcomes keep the atomic traffic on that
+// one word small.)  Either way the merge is exact; only its time depends on
+// the choice.
+constexpr uint32_t kFastSample = 128, kFastResample = 32;
+
+__device__ __forceinline__ bool fast_merge_records(uint32_t tile) {
+  return tile < kFastSample || tile % kFastResample == 0;
+}
+
+__device__ __forceinline__ bool fast_merge_worth_trying(const uint64_t* stat, uint32_t tile) {
+  if (fast_merge_records(tile)) return true;
+  const uint64_t s = __hip_atomic_load(stat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t tried = static_cast<uint32_t>(s), failed = static_cast<uint32_t>(s >> 32);
+  return tried == 0 || static_cast<uint64_t>(failed) * 8u < static_cast<uint64_t>(tried) * 7u;
 }
 
 // Exact bit LCP of two keys that share their first cp bytes, from the 8
