@@ -68,6 +68,19 @@ def test_fused_every_partition_size(items, coarse_parts):
     check_path(A, B, items=items, path="fused", coarse_parts=coarse_parts)
 
 
+@pytest.mark.parametrize("wid,scale", [(5, 0.02), (2, 0.08), (3, 0.005)])
+def test_fused_after_the_sampled_partitions(wid, scale):
+    """Several hundred 256-output partitions, past the 128 that always try the
+    merge on cached prefixes: on the URL and path inputs most partitions then
+    go straight to the exact merge, on the base64 inputs they keep trying the
+    cached one; the outputs are exact either way."""
+    A, B = workload(wid, scale)
+    P = -(-(A.n + B.n) // 256)
+    print(f"workload {wid} at {scale}: {A.n}+{B.n}, {P} partitions", flush=True)
+    assert P > 300
+    check_path(A, B, items=256, path="fused")
+
+
 @pytest.mark.parametrize("scale,items", [(0.4096, 1), (0.4097, 1), (1.0, 2), (1.0, 1)])
 def test_fused_many_partitions(scale, items):
     """8192, 8194, 10000 and 20000 partitions: the scan of partition bit
