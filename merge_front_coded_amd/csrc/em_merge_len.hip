@@ -22,7 +22,9 @@
 //    split by the boundary): the first 8 bytes, or, when all those keys share
 //    a common prefix of 8 bytes or more, the 8 bytes after it (the pages'
 //    prefix cache); key bytes stay in HBM;
-//  * merge and keep as in em_merge_keep; the survivor count is published to
+//  * merge and keep as in em_merge_keep (a partition goes straight to the
+//    exact merge when most of the launch's sampled partitions failed the
+//    merge on cached prefixes); the survivor count is published to
 //    a decoupled look-back right away and resolved after the LCPs (the global
 //    survivor index fixes the W15 phase of c_i);
 //  * each survivor's exact bit LCP with its predecessor comes from the two
