@@ -86,6 +86,12 @@ struct EmitShared {
   uint32_t next;  // the workgroup's next chunk ticket
   uint64_t bit_lo, bit_hi, bit_ext;
 };
+// The span copy reads a staged source up to four dwords past the last dword
+// a span needs; the array after the stage keeps such reads inside the
+// workgroup's LDS.
+static_assert(offsetof(EmitShared, kbits) == offsetof(EmitShared, stage) + sizeof(EmitShared::stage) &&
+                  sizeof(EmitShared::kbits) >= 16,
+              "the stage is followed by at least 16 bytes of the same allocation");
 
 // One record's fields for the slice loop; segment ends are relative to the
 // record start, kbit/vbit are the source bit positions of the key suffix and
